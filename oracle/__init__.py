@@ -1,0 +1,152 @@
+"""CPU oracle for C = A x B in FP32 inputs with an FP64 result.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package.  The GPU library never
+imports, links or calls it, and it imports nothing from the GPU library.
+
+The arithmetic lives in ``oracle.c`` (plain C, built with gcc, OpenMP over
+rows).  This module only builds that file and marshals numpy arrays to it.
+What it computes and the passages it follows are stated in ``oracle.c``:
+the inner-product definition ("Tiling Hierarchy on GPUs", section "Inner
+Product"; "Tiling Strategies", section 2), with zero-initialised accumulators
+and no read of C ("CMU DLSys Lecture 12: GPU Acceleration", section 5).
+
+Every function returns FP64 arrays: the product ``C`` and the magnitude sum
+``Cabs[i, j] = sum_k |A[i, k]| |B[k, j]|`` that the acceptance bound uses.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (OpenMP, no fast-math)."""
+    if (not force and os.path.exists(_LIB)
+            and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC)):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-fopenmp",
+           "-ffp-contract=off", "-fno-fast-math", _SRC, "-o", tmp, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    build()
+    lib = ctypes.CDLL(_LIB)
+    i64, p = ctypes.c_int64, ctypes.c_void_p
+    lib.oracle_sgemm_f64.argtypes = [i64, i64, i64, p, i64, p, i64, p, p, i64, ctypes.c_int]
+    lib.oracle_sgemm_f64.restype = ctypes.c_int
+    lib.oracle_sgemm_strided_batched_f64.argtypes = [
+        i64, i64, i64, p, i64, i64, p, i64, i64, p, p, i64, i64, i64, ctypes.c_int]
+    lib.oracle_sgemm_strided_batched_f64.restype = ctypes.c_int
+    lib.oracle_sgemm_entries_f64.argtypes = [i64, p, i64, p, i64, i64, p, p, p, p]
+    lib.oracle_sgemm_entries_f64.restype = None
+    lib.oracle_max_threads.argtypes = []
+    lib.oracle_max_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _f32_flat(x) -> np.ndarray:
+    a = np.asarray(x)
+    if a.dtype != np.float32:
+        raise TypeError("oracle operands must be float32, got %s" % a.dtype)
+    return np.ascontiguousarray(a.reshape(-1))
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def max_threads() -> int:
+    return _load().oracle_max_threads()
+
+
+def sgemm_f64(M: int, N: int, K: int, A, lda: int, B, ldb: int, nthreads: int = 0):
+    """C = A x B from flat row-major buffers with leading dimensions.
+
+    ``A`` holds at least (M-1)*lda + K floats and ``B`` at least
+    (K-1)*ldb + N floats; padding past each row's end is never read.
+    Returns ``(C, Cabs, threads_used)`` with C and Cabs of shape (M, N), FP64.
+    """
+    lib = _load()
+    a, b = _f32_flat(A), _f32_flat(B)
+    if M > 0 and K > 0 and a.size < (M - 1) * lda + K:
+        raise ValueError("A buffer too small")
+    if K > 0 and N > 0 and b.size < (K - 1) * ldb + N:
+        raise ValueError("B buffer too small")
+    C = np.empty((M, N), dtype=np.float64)
+    Cabs = np.empty((M, N), dtype=np.float64)
+    used = 1
+    if M > 0 and N > 0:
+        used = lib.oracle_sgemm_f64(M, N, K, _ptr(a), lda, _ptr(b), ldb,
+                                    _ptr(C), _ptr(Cabs), N, nthreads)
+    return C, Cabs, used
+
+
+def matmul_f64(A, B, nthreads: int = 0):
+    """Convenience form on 2-D float32 arrays (rows may be strided views)."""
+    A = np.asarray(A)
+    B = np.asarray(B)
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    C, Cabs, _ = sgemm_f64(M, N, K, np.ascontiguousarray(A), K,
+                           np.ascontiguousarray(B), N, nthreads)
+    return C, Cabs
+
+
+def sgemm_strided_batched_f64(M, N, K, A, lda, strideA, B, ldb, strideB, batch,
+                              nthreads: int = 0):
+    """Batched product; returns C and Cabs of shape (batch, M, N)."""
+    lib = _load()
+    a, b = _f32_flat(A), _f32_flat(B)
+    C = np.empty((batch, M, N), dtype=np.float64)
+    Cabs = np.empty((batch, M, N), dtype=np.float64)
+    if batch > 0 and M > 0 and N > 0:
+        need_a = (batch - 1) * strideA + (M - 1) * lda + K if K > 0 else 0
+        need_b = (batch - 1) * strideB + (K - 1) * ldb + N if K > 0 else 0
+        if a.size < need_a or b.size < need_b:
+            raise ValueError("operand buffer too small")
+        lib.oracle_sgemm_strided_batched_f64(M, N, K, _ptr(a), lda, strideA, _ptr(b), ldb,
+                                             strideB, _ptr(C), _ptr(Cabs), N, M * N, batch,
+                                             nthreads)
+    return C, Cabs
+
+
+def entries_f64(K: int, A, lda: int, B, ldb: int, rows, cols):
+    """Selected entries C[rows[e], cols[e]] and their magnitude sums, FP64.
+
+    Bitwise equal to the same entries of :func:`sgemm_f64` (same k order).
+    """
+    lib = _load()
+    a, b = _f32_flat(A), _f32_flat(B)
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    c = np.ascontiguousarray(np.asarray(cols, dtype=np.int64))
+    if r.shape != c.shape:
+        raise ValueError("rows and cols differ in length")
+    out = np.empty(r.size, dtype=np.float64)
+    out_abs = np.empty(r.size, dtype=np.float64)
+    if r.size:
+        if K > 0:
+            if a.size < int(r.max()) * lda + K or b.size < (K - 1) * ldb + int(c.max()) + 1:
+                raise ValueError("entry index outside the operands")
+        lib.oracle_sgemm_entries_f64(K, _ptr(a), lda, _ptr(b), ldb, r.size, _ptr(r), _ptr(c),
+                                     _ptr(out), _ptr(out_abs))
+    return out, out_abs

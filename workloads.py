@@ -1,0 +1,141 @@
+"""Seeded synthetic inputs for the FP32 GEMM workloads.
+
+This module holds input recipes only (shapes, layouts, value distributions,
+seeds); none of the product's arithmetic.  Both sides of every parity check,
+the HIP library and the CPU oracle, receive the very same float32 bits built
+here on the CPU with ``torch.Generator`` (A is drawn first, then B).
+
+Layouts are row-major with leading dimensions; when a leading dimension
+exceeds the row length the padding is filled with ``pad`` (NaN by default, so
+a kernel that reads padding is caught by the NaN it picks up).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    lda: int
+    ldb: int
+    ldc: int
+    dist_a: str          # "uniform" | "normal" | "int4"
+    dist_b: str
+    scale_a: float = 1.0
+    scale_b: float = 1.0
+    seed: int = 0
+    batch: int = 1
+    strideA: int = 0
+    strideB: int = 0
+    strideC: int = 0
+    about: str = field(default="", compare=False)
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K * self.batch
+
+    def describe(self) -> str:
+        s = "sgemm M=%d N=%d K=%d lda=%d ldb=%d ldc=%d" % (
+            self.M, self.N, self.K, self.lda, self.ldb, self.ldc)
+        if self.batch != 1:
+            s += " batch=%d strides=%d/%d/%d" % (self.batch, self.strideA, self.strideB,
+                                                 self.strideC)
+        return s + " A~%s B~%s seed=%d" % (self.dist_a, self.dist_b, self.seed)
+
+
+def _square(n, dist, scale, seed, about):
+    return Workload("square%d" % n, n, n, n, n, n, n, dist, dist, scale, scale, seed,
+                    about=about)
+
+
+# The five workloads, smallest first.  The 4096^3 product is the headline one.
+WORKLOADS = {
+    "square1024": _square(1024, "uniform", 1.0, 0,
+                          "1024^3 contiguous, uniform[-1,1), seed 0"),
+    "square1024_int": Workload("square1024_int", 1024, 1024, 1024, 1024, 1024, 1024,
+                               "int4", "int4", seed=0,
+                               about="1024^3 contiguous, integers in {-4..4}, seed 0"),
+    "square4096": _square(4096, "normal", 1.0 / math.sqrt(4096), 1,
+                          "4096^3 contiguous, normal(0,1)/sqrt(K), seed 1"),
+    "ragged": Workload("ragged", 4000, 3000, 4100, 4103, 3005, 3007, "uniform", "uniform",
+                       seed=2, about="4000x3000x4100, lda=K+3, ldb=N+5, ldc=N+7, seed 2"),
+    "tall": Workload("tall", 16384, 4096, 4096, 4096, 4096, 4096, "normal", "normal",
+                     1.0, 0.02, 3, about="16384x4096x4096, A~normal(0,1), B~normal(0,0.02)"),
+    "batched128": Workload("batched128", 128, 128, 128, 128, 128, 128, "uniform", "uniform",
+                           seed=4, batch=1024, strideA=128 * 128, strideB=128 * 128,
+                           strideC=128 * 128,
+                           about="1024 x 128^3, contiguous strided batches, seed 4"),
+}
+
+
+def draw(gen: torch.Generator, n: int, dist: str, scale: float = 1.0) -> torch.Tensor:
+    """n float32 values from one of the recipes, using ``gen``."""
+    if dist == "uniform":
+        # uniform on [-1, 1)
+        v = torch.rand(n, generator=gen, dtype=torch.float32) * 2.0 - 1.0
+    elif dist == "normal":
+        v = torch.randn(n, generator=gen, dtype=torch.float32)
+    elif dist == "int4":
+        v = torch.randint(-4, 5, (n,), generator=gen).to(torch.float32)
+    elif dist == "ones":
+        v = torch.ones(n, dtype=torch.float32)
+    else:
+        raise ValueError("unknown distribution %r" % dist)
+    if scale != 1.0:
+        v = v * scale
+    return v
+
+
+def place(values: torch.Tensor, rows: int, cols: int, ld: int, pad: float) -> torch.Tensor:
+    """Lay ``rows x cols`` values row-major into a flat buffer with leading dim ``ld``."""
+    if ld < cols:
+        raise ValueError("leading dimension below row length")
+    size = (rows - 1) * ld + cols if rows > 0 and cols > 0 else 0
+    buf = torch.full((max(rows * ld, size),), pad, dtype=torch.float32)
+    if rows > 0 and cols > 0:
+        buf.view(-1)[: rows * ld].view(rows, ld)[:, :cols] = values.view(rows, cols)
+    return buf
+
+
+def operands(M: int, N: int, K: int, lda: int, ldb: int, seed: int,
+             dist_a: str = "uniform", dist_b: str | None = None,
+             scale_a: float = 1.0, scale_b: float = 1.0, pad: float = float("nan"),
+             batch: int = 1, strideA: int | None = None, strideB: int | None = None):
+    """Flat float32 CPU buffers (A, B) for one product or a strided batch.
+
+    Matrix b of A starts at b*strideA floats (default: the padded matrix size);
+    likewise B.  Values are drawn batch by batch, A before B within each.
+    """
+    dist_b = dist_a if dist_b is None else dist_b
+    gen = torch.Generator("cpu").manual_seed(seed)
+    one_a = M * lda
+    one_b = K * ldb
+    sa = one_a if strideA is None else strideA
+    sb = one_b if strideB is None else strideB
+    if batch > 1 and (sa < one_a or sb < one_b):
+        raise ValueError("batch stride below one padded matrix")
+    A = torch.full(((batch - 1) * sa + one_a,), pad, dtype=torch.float32)
+    B = torch.full(((batch - 1) * sb + one_b,), pad, dtype=torch.float32)
+    for b in range(batch):
+        a_vals = draw(gen, M * K, dist_a, scale_a)
+        b_vals = draw(gen, K * N, dist_b, scale_b)
+        A[b * sa: b * sa + one_a] = place(a_vals, M, K, lda, pad)[:one_a]
+        B[b * sb: b * sb + one_b] = place(b_vals, K, N, ldb, pad)[:one_b]
+    return A, B
+
+
+def workload_operands(w: Workload, pad: float = float("nan")):
+    """Flat float32 CPU buffers (A, B) for one of the named workloads."""
+    if w.batch == 1:
+        return operands(w.M, w.N, w.K, w.lda, w.ldb, w.seed, w.dist_a, w.dist_b,
+                        w.scale_a, w.scale_b, pad)
+    return operands(w.M, w.N, w.K, w.lda, w.ldb, w.seed, w.dist_a, w.dist_b,
+                    w.scale_a, w.scale_b, pad, batch=w.batch, strideA=w.strideA,
+                    strideB=w.strideB)
