@@ -1,0 +1,203 @@
+"""Throughput of the FP32 GEMM C = A x B on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--path mfma|valu]
+                    [--workload square4096] [--no-cpu-baseline]
+
+One step is one call of the library on the named workload (default: the
+4096^3 product, A and B ~ normal(0,1)/sqrt(K), seed 1), inputs resident in
+device memory before timing starts.  W untimed calls, then K calls timed with
+HIP events recorded on the stream the kernel is launched on, bracketed by
+device synchronisation.  Prints one JSON line:
+
+  value      whole-job TFLOP/s = 2MNK / (time per step)
+  roofline   achieved TFLOP/s of the GEMM kernel against the FP32 matrix peak
+             (157.3 TFLOP/s), and HBM traffic measured with rocprofv3 counters
+             when the committed counter summary matches the current kernel source
+  cpu_baseline  the CPU oracle on a bounded sample (leading rows of C) of the
+             same workload, on all host threads
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FP32 GEMM TFLOP/s at M=N=K=4096 on 1 MI355X; % of FP32 peak"
+PEAK_FP32_TFLOPS = 157.3      # MI355X dense FP32 (vector and matrix)
+PEAK_HBM_GBS = 8000.0
+CSRC = os.path.join(ROOT, "tiled_fp32_gemm_sgemm_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_mfma_square4096.txt")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            h.update(name.encode())
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(path: str, workload: str, kpath: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    it is missing or was taken on a different kernel source."""
+    if kpath != "mfma" or workload != "square4096" or not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, A, B, target_s: float = 12.0):
+    """The oracle, untouched, on the leading rows of C of the same workload."""
+    import oracle
+    a = A.numpy()
+    b = B.numpy()
+    rows0 = 16
+    t0 = time.perf_counter()
+    _, _, used = oracle.sgemm_f64(rows0, w.N, w.K, a, w.lda, b, w.ldb)
+    dt0 = time.perf_counter() - t0
+    rows = int(min(w.M, max(rows0, rows0 * target_s / max(dt0, 1e-6))))
+    t0 = time.perf_counter()
+    _, _, used = oracle.sgemm_f64(rows, w.N, w.K, a, w.lda, b, w.ldb)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(used), "kind": "oracle",
+            "sample": "rows 0..%d of C for %s (%dx%dx%d, %.3g GFLOP) in %.2f s, FP64 "
+                      "accumulation, OpenMP over rows" % (rows - 1, w.name, rows, w.N, w.K,
+                                                          flops / 1e9, dt),
+            "seconds": dt}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--path", choices=["mfma", "valu"], default="mfma")
+    ap.add_argument("--workload", default="square4096")
+    ap.add_argument("--config", type=int, default=None, help="force a matrix-core tile config")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-comparator", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build runs on a single MI355X and has no "
+              "multi-GPU path (asked for --gpus %d)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+    from workloads import WORKLOADS, workload_operands
+    import tiled_fp32_gemm_sgemm_amd as sg
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    A_cpu, B_cpu = workload_operands(w, pad=0.0)
+    A = A_cpu.to(dev)
+    B = B_cpu.to(dev)
+    c_len = (w.batch - 1) * w.strideC + w.M * w.ldc
+    C = torch.empty(c_len, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream
+
+    def step(path=args.path, config=args.config):
+        if w.batch == 1 and config is None:
+            st = sg.sgemm_raw(w.M, w.N, w.K, A.data_ptr(), w.lda, B.data_ptr(), w.ldb,
+                              C.data_ptr(), w.ldc, handle, path)
+        else:
+            st = sg.sgemm_strided_batched_raw(w.M, w.N, w.K, A.data_ptr(), w.lda, w.strideA,
+                                              B.data_ptr(), w.ldb, w.strideB, C.data_ptr(),
+                                              w.ldc, w.strideC, w.batch, handle, path, config)
+        if st != 0:
+            raise sg.SgemmError(st, "sgemm")
+
+    def timed(n_steps, n_warm, path=args.path, config=args.config):
+        for _ in range(n_warm):
+            step(path, config)
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(n_steps):
+            step(path, config)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n_steps  # ms per step
+
+    ms = timed(args.steps, args.warmup)
+    flops = float(w.flops)
+    tflops = flops / (ms * 1e-3) / 1e12
+
+    if args.config is not None:
+        tile = sg.config_info(args.config)["name"]
+    elif args.path == "mfma":
+        tile = sg.config_info(sg.select_config(w.M, w.N, w.K, w.batch))["name"]
+    else:
+        tile = "valu_128x128x8_t8x8"
+
+    traffic = read_traffic(TRAFFIC_FILE, args.workload, args.path)
+    roofline = {"bound": "mfma" if args.path == "mfma" else "alu",
+                "achieved": tflops,
+                "peak": PEAK_FP32_TFLOPS if args.path == "mfma" else PEAK_FP32_TFLOPS / 2,
+                "unit": "TFLOP/s",
+                "frac": None,
+                "traffic": traffic,
+                "kernel": tile,
+                "avg_kernel_ms": ms}
+    roofline["frac"] = roofline["achieved"] / roofline["peak"]
+
+    comparators = {}
+    if not args.no_comparator and w.batch == 1:
+        other = "valu" if args.path == "mfma" else "mfma"
+        oms = timed(max(5, args.steps // 5), 3, other, None)
+        comparators[other] = {"tflops": flops / (oms * 1e-3) / 1e12, "ms_per_step": oms}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, A_cpu, B_cpu)
+
+    out = {
+        "metric": METRIC,
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_fp32_peak": 100.0 * tflops / PEAK_FP32_TFLOPS,
+        "config": {"workload": w.describe(), "M": w.M, "N": w.N, "K": w.K, "batch": w.batch,
+                   "path": args.path, "tile": tile},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "comparators": comparators,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,136 @@
+/*
+ * sgemm.h -- C ABI of the MI355X (gfx950) FP32 matrix-multiply library.
+ *
+ * Operation (every entry point below computes it):
+ *   C[i*ldc + j] = sum_{k<K} A[i*lda + k] * B[k*ldb + j]     for i < M, j < N,
+ * i.e. C = A x B with A (M x K), B (K x N) and C (M x N) row-major, each row
+ * starting a leading dimension after the previous one.  This is the product
+ * defined in "Tiling Hierarchy on GPUs" (introduction and section "Inner
+ * Product": each output is a K-term sum of products) and in "Tiling
+ * Strategies" section 2 ("The Problem").  As in "CMU DLSys Lecture 12: GPU
+ * Acceleration" section 5, the accumulators start at zero and C is never read:
+ * C's M x N window is overwritten (beta = 0), and nothing outside that window
+ * (the ldc padding, other memory) is written.  Padding between a row's end and
+ * its leading dimension is never read.  The order in which the K products of
+ * one element are summed is unspecified; results are IEEE FP32 with
+ * round-to-nearest-even; integer-valued inputs whose partial sums stay below
+ * 2^24 give the exact integer result.
+ *
+ * Memory and ownership: A, B and C are device pointers owned by the caller.
+ * The library never allocates, frees or copies memory between host and
+ * device, and keeps no mutable global state, so calls from several host
+ * threads are safe.  C must not overlap A or B (not checked).
+ *
+ * Asynchrony: work is enqueued on `stream` (NULL is the default stream) and
+ * the call returns without waiting for it ("CMU DLSys Lecture 12" section 2:
+ * launches are asynchronous and completion follows the stream's rules).  The
+ * caller synchronises before reading C.
+ *
+ * Errors: every entry point returns an sgemm_status_t.  Argument errors are
+ * detected on the host before anything is enqueued; a launch error reported
+ * by HIP is returned as SGEMM_STATUS_LAUNCH_FAILED.
+ *
+ * Degenerate sizes: M == 0, N == 0 or batch == 0 is a successful no-op.
+ * K == 0 with M, N > 0 writes +0.0 to C's M x N window (the empty sum).
+ */
+#ifndef TILED_FP32_SGEMM_H
+#define TILED_FP32_SGEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sgemm_status {
+    SGEMM_STATUS_SUCCESS = 0,
+    /* M, N, K or batch is negative. */
+    SGEMM_STATUS_INVALID_SIZE = -1,
+    /* lda < max(1, K), ldb < max(1, N) or ldc < max(1, N). */
+    SGEMM_STATUS_INVALID_LD = -2,
+    /* A, B or C is NULL although the call would read or write it. */
+    SGEMM_STATUS_NULL_POINTER = -3,
+    /* M, N, K or batch is 2^31 or more, or an element offset overflows 64 bits. */
+    SGEMM_STATUS_SIZE_OVERFLOW = -4,
+    /* A batch stride is negative, or strideC lets two C matrices overlap. */
+    SGEMM_STATUS_INVALID_STRIDE = -5,
+    /* HIP reported an error when the kernel was enqueued. */
+    SGEMM_STATUS_LAUNCH_FAILED = -6,
+    /* The tile configuration index passed to sgemm_with_config is unknown. */
+    SGEMM_STATUS_INVALID_CONFIG = -7
+} sgemm_status_t;
+
+/*
+ * Single product on the matrix cores (v_mfma_f32_32x32x2_f32), block tile
+ * chosen from the shape.  Arguments: sizes M, N, K (>= 0); A with leading
+ * dimension lda; B with ldb; C with ldc; stream.
+ */
+int sgemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+          int64_t ldb, float *C, int64_t ldc, hipStream_t stream);
+
+/*
+ * `batch` independent products.  Product b reads A + b*strideA and
+ * B + b*strideB and writes C + b*strideC (strides in elements, >= 0).
+ * strideA or strideB may be 0 (a shared operand); for batch > 1, strideC must
+ * be at least (M-1)*ldc + N so that the C matrices do not overlap.
+ */
+int sgemm_strided_batched(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                          int64_t strideA, const float *B, int64_t ldb, int64_t strideB,
+                          float *C, int64_t ldc, int64_t strideC, int64_t batch,
+                          hipStream_t stream);
+
+/*
+ * The same two operations on the vector ALUs: each lane owns an 8x8 register
+ * tile of a 128x128 block tile and updates it with FP32 fused multiply-adds,
+ * the thread-tile design of "Tiling Hierarchy on GPUs" (sections "Register
+ * Tiling" and "Register prefetching") and "Tiling Strategies" section 4
+ * ("Register Tiling").  Same contract as sgemm / sgemm_strided_batched.
+ */
+int sgemm_valu(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,
+               int64_t ldb, float *C, int64_t ldc, hipStream_t stream);
+
+int sgemm_valu_strided_batched(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                               int64_t strideA, const float *B, int64_t ldb, int64_t strideB,
+                               float *C, int64_t ldc, int64_t strideC, int64_t batch,
+                               hipStream_t stream);
+
+/*
+ * Matrix-core product with an explicit block-tile configuration, for tests
+ * and tuning ("Tiling Strategies" section 4: tile size trades reuse against
+ * occupancy and tail effects; "Tiling Hierarchy on GPUs", "Reducing Overhead
+ * Slots": libraries tune the tile per shape).  `config` is an index below
+ * sgemm_num_configs(); otherwise SGEMM_STATUS_INVALID_CONFIG.  batch == 1 with
+ * zero strides is a single product.
+ */
+int sgemm_with_config(int config, int64_t M, int64_t N, int64_t K, const float *A,
+                      int64_t lda, int64_t strideA, const float *B, int64_t ldb,
+                      int64_t strideB, float *C, int64_t ldc, int64_t strideC, int64_t batch,
+                      hipStream_t stream);
+
+/* Number of matrix-core tile configurations. */
+int sgemm_num_configs(void);
+
+/*
+ * Description of configuration `config` written into `buf` (at most `len`
+ * bytes, NUL-terminated), e.g. "mfma_256x128x16_w2x2".  Returns 0, or
+ * SGEMM_STATUS_INVALID_CONFIG.  Also fills the block-tile sizes when the
+ * pointers are not NULL.  Host only; touches no device.
+ */
+int sgemm_config_info(int config, char *buf, int64_t len, int *bm, int *bn, int *bk,
+                      int *threads);
+
+/*
+ * The configuration sgemm / sgemm_strided_batched would use for this shape.
+ * Host only; touches no device.  Returns a negative status for bad sizes.
+ */
+int sgemm_select_config(int64_t M, int64_t N, int64_t K, int64_t batch);
+
+/* Static text for a status code (never NULL). */
+const char *sgemm_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILED_FP32_SGEMM_H */

@@ -1,0 +1,12 @@
+"""FP32 matrix multiply C = A x B for the AMD Instinct MI355X (gfx950).
+
+The product runs in libsgemm.so (hand-written HIP kernels behind the C ABI
+in include/sgemm.h); this package only passes tensors' device addresses,
+leading dimensions and the current stream to it.
+"""
+from .api import (config_info, num_configs, select_config, sgemm, sgemm_raw,
+                  sgemm_strided_batched, sgemm_strided_batched_raw)
+from ._native import SgemmError, status_string
+
+__all__ = ["sgemm", "sgemm_strided_batched", "sgemm_raw", "sgemm_strided_batched_raw",
+           "num_configs", "config_info", "select_config", "SgemmError", "status_string"]

@@ -1,0 +1,85 @@
+"""ctypes view of libsgemm.so (the C ABI in include/sgemm.h).
+
+Argument marshalling only: every operation runs in the HIP library.  If the
+library has not been built, loading fails with an error that says so; there is
+no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libsgemm.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "sgemm.h")
+
+STATUS = {
+    0: "SGEMM_STATUS_SUCCESS",
+    -1: "SGEMM_STATUS_INVALID_SIZE",
+    -2: "SGEMM_STATUS_INVALID_LD",
+    -3: "SGEMM_STATUS_NULL_POINTER",
+    -4: "SGEMM_STATUS_SIZE_OVERFLOW",
+    -5: "SGEMM_STATUS_INVALID_STRIDE",
+    -6: "SGEMM_STATUS_LAUNCH_FAILED",
+    -7: "SGEMM_STATUS_INVALID_CONFIG",
+}
+
+
+class SgemmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (what, status_string(status), status))
+
+
+_lib = None
+
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+_SIGS = {
+    "sgemm": ([_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p], ctypes.c_int),
+    "sgemm_valu": ([_i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _p], ctypes.c_int),
+    "sgemm_strided_batched": (
+        [_i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64, _p],
+        ctypes.c_int),
+    "sgemm_valu_strided_batched": (
+        [_i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64, _p],
+        ctypes.c_int),
+    "sgemm_with_config": (
+        [ctypes.c_int, _i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64,
+         _p], ctypes.c_int),
+    "sgemm_num_configs": ([], ctypes.c_int),
+    "sgemm_config_info": ([ctypes.c_int, ctypes.c_char_p, _i64, ctypes.POINTER(ctypes.c_int),
+                           ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                           ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
+    "sgemm_select_config": ([_i64, _i64, _i64, _i64], ctypes.c_int),
+    "sgemm_status_string": ([ctypes.c_int], ctypes.c_char_p),
+}
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libsgemm.so is not built (%s); run `python -m tiled_fp32_gemm_sgemm_amd.build`"
+                % LIB_PATH)
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().sgemm_status_string(int(status)).decode()
+
+
+def header_functions(path: str = HEADER):
+    """Names of the functions include/sgemm.h declares."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sgemm\w*)\s*\(", text)))

@@ -1,0 +1,136 @@
+"""Python entry points over the C ABI (include/sgemm.h).
+
+PyTorch supplies device memory and the stream; the product itself runs in
+libsgemm.so.  Operands are row-major: a 2-D tensor with unit column stride,
+whose row stride is its leading dimension.  Nothing is copied or converted:
+an operand that does not already have that layout, dtype float32 and a CUDA
+device is rejected.
+"""
+from __future__ import annotations
+
+import ctypes
+
+from . import _native
+
+PATHS = ("mfma", "valu")
+
+
+def _stream_handle(stream, device) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise _native.SgemmError(status, what)
+
+
+def sgemm_raw(M, N, K, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, stream=0, path="mfma",
+              config=None) -> int:
+    """Direct call on raw device addresses; returns the status code."""
+    lib = _native.lib()
+    if config is not None:
+        return lib.sgemm_with_config(int(config), M, N, K, A_ptr, lda, 0, B_ptr, ldb, 0,
+                                     C_ptr, ldc, 0, 1, stream)
+    fn = lib.sgemm if path == "mfma" else lib.sgemm_valu
+    if path not in PATHS:
+        raise ValueError("path must be one of %s" % (PATHS,))
+    return fn(M, N, K, A_ptr, lda, B_ptr, ldb, C_ptr, ldc, stream)
+
+
+def sgemm_strided_batched_raw(M, N, K, A_ptr, lda, strideA, B_ptr, ldb, strideB, C_ptr, ldc,
+                              strideC, batch, stream=0, path="mfma", config=None) -> int:
+    lib = _native.lib()
+    if config is not None:
+        return lib.sgemm_with_config(int(config), M, N, K, A_ptr, lda, strideA, B_ptr, ldb,
+                                     strideB, C_ptr, ldc, strideC, batch, stream)
+    if path not in PATHS:
+        raise ValueError("path must be one of %s" % (PATHS,))
+    fn = lib.sgemm_strided_batched if path == "mfma" else lib.sgemm_valu_strided_batched
+    return fn(M, N, K, A_ptr, lda, strideA, B_ptr, ldb, strideB, C_ptr, ldc, strideC, batch,
+              stream)
+
+
+def _operand(t, name, ndim):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != torch.float32:
+        raise TypeError("%s must be float32, got %s" % (name, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU" % name)
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dimensions" % (name, ndim))
+    if t.size(-1) > 1 and t.stride(-1) != 1:
+        raise ValueError("%s must be row-major (unit stride along its last dimension)" % name)
+
+
+def _ld(t) -> int:
+    return max(int(t.stride(-2)), int(t.size(-1)), 1)
+
+
+def sgemm(A, B, out=None, *, path: str = "mfma", config=None, stream=None):
+    """C = A @ B for float32 CUDA tensors A (M, K) and B (K, N); returns C (M, N)."""
+    import torch
+    _operand(A, "A", 2)
+    _operand(B, "B", 2)
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ: %d vs %d" % (K, K2))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    _operand(out, "out", 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must have shape (%d, %d)" % (M, N))
+    with torch.cuda.device(A.device):
+        st = sgemm_raw(M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B), out.data_ptr(),
+                       _ld(out), _stream_handle(stream, A.device), path, config)
+    _check(st, "sgemm")
+    return out
+
+
+def sgemm_strided_batched(A, B, out=None, *, path: str = "mfma", config=None, stream=None):
+    """Batched C[b] = A[b] @ B[b] for 3-D float32 CUDA tensors; returns C (batch, M, N)."""
+    import torch
+    _operand(A, "A", 3)
+    _operand(B, "B", 3)
+    batch, M, K = A.shape
+    batch2, K2, N = B.shape
+    if K != K2 or batch != batch2:
+        raise ValueError("shapes differ: %s vs %s" % (tuple(A.shape), tuple(B.shape)))
+    if out is None:
+        out = torch.empty((batch, M, N), dtype=torch.float32, device=A.device)
+    _operand(out, "out", 3)
+    if tuple(out.shape) != (batch, M, N):
+        raise ValueError("out must have shape (%d, %d, %d)" % (batch, M, N))
+    with torch.cuda.device(A.device):
+        st = sgemm_strided_batched_raw(
+            M, N, K, A.data_ptr(), _ld(A), int(A.stride(0)), B.data_ptr(), _ld(B),
+            int(B.stride(0)), out.data_ptr(), _ld(out), int(out.stride(0)), batch,
+            _stream_handle(stream, A.device), path, config)
+    _check(st, "sgemm_strided_batched")
+    return out
+
+
+def num_configs() -> int:
+    return _native.lib().sgemm_num_configs()
+
+
+def config_info(config: int) -> dict:
+    buf = ctypes.create_string_buffer(64)
+    bm, bn, bk, nt = (ctypes.c_int() for _ in range(4))
+    st = _native.lib().sgemm_config_info(int(config), buf, 64, ctypes.byref(bm), ctypes.byref(bn),
+                                         ctypes.byref(bk), ctypes.byref(nt))
+    _check(st, "sgemm_config_info")
+    return {"name": buf.value.decode(), "bm": bm.value, "bn": bn.value, "bk": bk.value,
+            "threads": nt.value}
+
+
+def select_config(M: int, N: int, K: int, batch: int = 1) -> int:
+    st = _native.lib().sgemm_select_config(M, N, K, batch)
+    if st < 0:
+        raise _native.SgemmError(st, "sgemm_select_config")
+    return st

@@ -1,0 +1,127 @@
+// Shared device pieces of the FP32 GEMM kernels (gfx950, wave64):
+//  * the kernel argument block,
+//  * the workgroup -> output-tile map (XCD-aware, grouped),
+//  * coalesced 16-byte global loads with zero-filled masks for tails.
+//
+// "CMU DLSys Lecture 12: GPU Acceleration" section 5 splits the work into
+// block-owned output tiles and stages operand slabs cooperatively, with
+// zero-filled masked loads where the tile runs past the matrix; section 1
+// gives the ceil-div launch with a bounds check.  "Tiling Strategies"
+// section 2 ("The Tiled Solution") gives the same loop over K in slices.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgemm_dev {
+
+// Kernel arguments.  Sizes are validated on the host: M, N, K < 2^31, all
+// element offsets fit in int64.
+struct GemmArgs {
+    const float* A;
+    const float* B;
+    float* C;
+    int64_t lda, ldb, ldc;
+    int64_t strideA, strideB, strideC;  // batch strides (elements)
+    int M, N, K;
+    int tiles_m, tiles_n;               // output tiles per matrix
+    int batch_base;                     // first batch index of this launch
+    int batch_count;                    // batch members in this launch
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+// 16-byte vector that only claims 4-byte alignment: rows with an odd leading
+// dimension start on any 4-byte boundary and are still read with one
+// global_load_dwordx4 (the hardware accepts dword-aligned vector loads).
+typedef float f32x4_u __attribute__((ext_vector_type(4), aligned(4)));
+
+constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, one L2 each
+
+// Workgroups are handed to the XCDs round-robin (id % 8), and each XCD has its
+// own L2.  Renumber so that each XCD receives a contiguous run of tile ids;
+// with the grouped order below, neighbouring tiles that share A rows and B
+// columns then run on the same XCD and hit the same L2.
+__device__ __forceinline__ uint32_t xcd_contiguous_id(uint32_t bid, uint32_t nblocks) {
+    const uint32_t xcd = bid % kNumXcd;
+    const uint32_t slot = bid / kNumXcd;
+    const uint32_t q = nblocks / kNumXcd;
+    const uint32_t r = nblocks % kNumXcd;
+    return xcd < r ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+// Tile coordinates from a linear tile id: groups of `group_m` tile rows, and
+// inside a group the tile row varies fastest, so consecutive ids sweep a
+// group_m-tall column of tiles that reuses the same B panel.
+__device__ __forceinline__ void grouped_tile(uint32_t pid, int tiles_m, int tiles_n, int group_m,
+                                             int& tm, int& tn) {
+    const uint32_t per_group = (uint32_t)group_m * (uint32_t)tiles_n;
+    const uint32_t group = pid / per_group;
+    const int first_m = (int)group * group_m;
+    const int gsize = min(tiles_m - first_m, group_m);
+    const uint32_t in_group = pid - group * per_group;
+    tm = first_m + (int)(in_group % (uint32_t)gsize);
+    tn = (int)(in_group / (uint32_t)gsize);
+}
+
+// Block -> (batch member, tile row, tile column) for a 1-D grid that covers
+// tiles_m * tiles_n * batch_count workgroups.
+struct TileCoord {
+    int b, tm, tn;
+};
+
+__device__ __forceinline__ TileCoord map_block(const GemmArgs& p, int group_m) {
+    const uint32_t nblocks = gridDim.x;
+    const uint32_t pid = xcd_contiguous_id(blockIdx.x, nblocks);
+    const uint32_t per_matrix = (uint32_t)p.tiles_m * (uint32_t)p.tiles_n;
+    TileCoord t;
+    t.b = (int)(pid / per_matrix);
+    grouped_tile(pid - (uint32_t)t.b * per_matrix, p.tiles_m, p.tiles_n, group_m, t.tm, t.tn);
+    t.b += p.batch_base;
+    return t;
+}
+
+__device__ __forceinline__ f32x4 ldg4(const float* p) {
+    return (f32x4)(*(const f32x4_u*)p);
+}
+
+// Four consecutive elements p[0..3] of one row, of which only the first
+// `valid` (clamped to 0..4) exist; the rest read as zero and are not
+// accessed, so padding and memory past the matrix are never touched.
+__device__ __forceinline__ f32x4 ldg4_masked(const float* p, int valid) {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (valid >= 4) {
+        v = ldg4(p);
+    } else if (valid > 0) {
+        v.x = p[0];
+        if (valid > 1) v.y = p[1];
+        if (valid > 2) v.z = p[2];
+    }
+    return v;
+}
+
+__device__ __forceinline__ void stg4_masked(float* p, f32x4 v, int valid) {
+    if (valid >= 4) {
+        *(f32x4_u*)p = (f32x4_u)v;
+    } else if (valid > 0) {
+        p[0] = v.x;
+        if (valid > 1) p[1] = v.y;
+        if (valid > 2) p[2] = v.z;
+    }
+}
+
+// C's window set to +0 (K == 0: every output is the empty sum).
+__global__ void zero_fill_kernel(float* C, int64_t ldc, int64_t strideC, int M, int N,
+                                 int batch) {
+    const int64_t total = (int64_t)M * N * batch;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t b = e / ((int64_t)M * N);
+        const int64_t rem = e - b * (int64_t)M * N;
+        const int64_t i = rem / N;
+        const int64_t j = rem - i * N;
+        C[b * strideC + i * ldc + j] = 0.0f;
+    }
+}
+
+}  // namespace sgemm_dev
