@@ -34,6 +34,7 @@ PEAK_FP32_TFLOPS = 157.3      # MI355X dense FP32 (vector and matrix)
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "tiled_fp32_gemm_sgemm_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_mfma_square4096.txt")
+COPY_BYTES = 512 * 1024 * 1024   # larger than the 256 MB last-level cache
 
 
 def kernel_source_hash() -> str:
@@ -96,6 +97,8 @@ def main(argv=None) -> int:
     ap.add_argument("--config", type=int, default=None, help="force a matrix-core tile config")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparator", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain copy kernel of known size (counter scaling)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -141,6 +144,15 @@ def main(argv=None) -> int:
         ev1.record(stream)
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / n_steps  # ms per step
+
+    if args.calibrate_copy:
+        # Elementwise copy kernel: reads and writes exactly COPY_BYTES each.
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     ms = timed(args.steps, args.warmup)
     flops = float(w.flops)

@@ -81,17 +81,16 @@ RAGGED = [(M, N, K, K + _rng.randint(0, 3), N + _rng.randint(0, 5), N + _rng.ran
           for (M, N, K) in RAGGED]
 
 
-def _paths():
-    return ["valu"] + ["cfg%d" % i for i in range(sg.num_configs())]
-
-
 def _call(path, *args, **kw):
     if path.startswith("cfg"):
         return run_gpu(*args, config=int(path[3:]), **kw)
     return run_gpu(*args, path=path, **kw)
 
 
-@pytest.mark.parametrize("path", ["valu", "cfg0", "cfg1", "cfg2", "cfg3"])
+ALL_PATHS = ["valu"] + ["cfg%d" % i for i in range(10)]
+
+
+@pytest.mark.parametrize("path", ALL_PATHS)
 @pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
 def test_ragged_integer_bitwise(shape, path):
     M, N, K, lda, ldb, ldc = shape
@@ -101,7 +100,11 @@ def test_ragged_integer_bitwise(shape, path):
     parity.assert_bitwise(C, ref, "%s %s" % (path, shape))
 
 
-@pytest.mark.parametrize("path", ["valu", "cfg0", "cfg1", "cfg2", "cfg3"])
+def test_every_config_is_covered():
+    assert sg.num_configs() == len(ALL_PATHS) - 1
+
+
+@pytest.mark.parametrize("path", ALL_PATHS)
 @pytest.mark.parametrize("shape", RAGGED, ids=lambda s: "x".join(map(str, s)))
 def test_ragged_uniform_tolerance(shape, path):
     M, N, K, lda, ldb, ldc = shape
@@ -176,7 +179,7 @@ def test_invalid_arguments_enqueue_nothing():
 
 # ------------------------------------------------------------------ batched
 
-@pytest.mark.parametrize("path", ["mfma", "valu", "cfg1", "cfg2"])
+@pytest.mark.parametrize("path", ["mfma", "valu", "cfg1", "cfg2", "cfg5", "cfg6", "cfg7"])
 def test_batched_ragged_members_differ(path):
     M, N, K, lda, ldb, ldc, batch = 45, 77, 33, 36, 80, 79, 6
     sA, sB, sC = M * lda + 5, K * ldb + 3, M * ldc + 11

@@ -19,10 +19,19 @@ namespace {
 using namespace sgemm_dev;
 
 // Matrix-core tile configurations.  Index = config id in the ABI.
-using Cfg256x128 = MfmaTile<256, 128, 16, 2, 2, 8>;   // 4 waves of 128x64
-using Cfg128x128 = MfmaTile<128, 128, 16, 2, 2, 8>;   // 4 waves of 64x64
-using Cfg64x64 = MfmaTile<64, 64, 16, 2, 2, 8>;       // 4 waves of 32x32
-using Cfg256x256 = MfmaTile<256, 256, 16, 2, 4, 8>;   // 8 waves of 128x64
+// MfmaTile<BM, BN, BK, waves along M, waves along N, MFMA edge, waves per SIMD,
+//          tile-row group>
+using Cfg256x128 = MfmaTile<256, 128, 16, 2, 2, 32, 2, 8>;       // 4 waves of 128x64
+using Cfg128x128 = MfmaTile<128, 128, 16, 2, 2, 32, 3, 8>;       // 4 waves of 64x64
+using Cfg64x64 = MfmaTile<64, 64, 16, 2, 2, 32, 4, 8>;           // 4 waves of 32x32
+using Cfg256x256 = MfmaTile<256, 256, 16, 2, 4, 32, 2, 8>;       // 8 waves of 128x64
+using Cfg256x256k32 = MfmaTile<256, 256, 32, 2, 4, 32, 2, 8>;    // 8 waves of 128x64
+using Cfg128x128k32 = MfmaTile<128, 128, 32, 2, 2, 32, 2, 8>;    // 4 waves of 64x64
+using Cfg128x128k32m16 = MfmaTile<128, 128, 32, 2, 2, 16, 2, 8>; // 4 waves of 64x64
+using Cfg64x64k32m16 = MfmaTile<64, 64, 32, 2, 2, 16, 4, 8>;     // 4 waves of 32x32
+// One wave per SIMD, 128x128 wave tiles, accumulators in the AGPR file.
+using Cfg256x256m32w1 = MfmaTile<256, 256, 16, 2, 2, 32, 1, 8>;
+using Cfg256x256k32m32w1 = MfmaTile<256, 256, 32, 2, 2, 32, 1, 8>;
 
 struct ConfigEntry {
     const char* name;
@@ -32,16 +41,22 @@ struct ConfigEntry {
     int blocks_per_cu;       // workgroups that fit on one CU at once
 };
 
+#define SGEMM_CFG(T, name, eff, per_cu) \
+    { name, T::BM, T::BN, T::BK, T::NT, (const void*)&sgemm_mfma_kernel<T>, eff, per_cu }
+
 const ConfigEntry kConfigs[] = {
-    {"mfma_256x128x16_w2x2", 256, 128, 16, Cfg256x128::NT,
-     (const void*)&sgemm_mfma_kernel<Cfg256x128>, 1.00, 2},
-    {"mfma_128x128x16_w2x2", 128, 128, 16, Cfg128x128::NT,
-     (const void*)&sgemm_mfma_kernel<Cfg128x128>, 0.90, 2},
-    {"mfma_64x64x16_w2x2", 64, 64, 16, Cfg64x64::NT,
-     (const void*)&sgemm_mfma_kernel<Cfg64x64>, 0.60, 4},
-    {"mfma_256x256x16_w2x4", 256, 256, 16, Cfg256x256::NT,
-     (const void*)&sgemm_mfma_kernel<Cfg256x256>, 1.00, 1},
+    SGEMM_CFG(Cfg256x128, "mfma32_256x128x16_w2x2", 0.94, 2),
+    SGEMM_CFG(Cfg128x128, "mfma32_128x128x16_w2x2", 0.90, 3),
+    SGEMM_CFG(Cfg64x64, "mfma32_64x64x16_w2x2", 0.60, 8),
+    SGEMM_CFG(Cfg256x256, "mfma32_256x256x16_w2x4", 0.96, 1),
+    SGEMM_CFG(Cfg256x256k32, "mfma32_256x256x32_w2x4", 1.00, 1),
+    SGEMM_CFG(Cfg128x128k32, "mfma32_128x128x32_w2x2", 0.90, 2),
+    SGEMM_CFG(Cfg128x128k32m16, "mfma16_128x128x32_w2x2", 0.90, 2),
+    SGEMM_CFG(Cfg64x64k32m16, "mfma16_64x64x32_w2x2", 0.60, 4),
+    SGEMM_CFG(Cfg256x256m32w1, "mfma32_256x256x16_w2x2", 0.98, 1),
+    SGEMM_CFG(Cfg256x256k32m32w1, "mfma32_256x256x32_w2x2", 0.98, 1),
 };
+#undef SGEMM_CFG
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 constexpr int kNumCu = 256;  // MI355X compute units
 
@@ -96,8 +111,7 @@ int choose_config(int64_t M, int64_t N, int64_t K, int64_t batch) {
     (void)K;
     int best = 0;
     double best_score = -1.0;
-    const int order[] = {0, 3, 1, 2};
-    for (int idx : order) {
+    for (int idx = 0; idx < kNumConfigs; ++idx) {
         const ConfigEntry& c = kConfigs[idx];
         const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn) * batch;
         const double useful = (double)M * N * batch / ((double)tiles * c.bm * c.bn);
