@@ -33,7 +33,7 @@ METRIC = "FP32 GEMM TFLOP/s at M=N=K=4096 on 1 MI355X; % of FP32 peak"
 PEAK_FP32_TFLOPS = 157.3      # MI355X dense FP32 (vector and matrix)
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "tiled_fp32_gemm_sgemm_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sgemm_mfma_square4096.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sgemm_mfma_square4096_counters.txt")
 COPY_BYTES = 512 * 1024 * 1024   # larger than the 256 MB last-level cache
 
 
@@ -64,6 +64,120 @@ def read_traffic(path: str, workload: str, kpath: str):
         return float(vals["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _per_dispatch(rows, name_part):
+    """{dispatch id: {counter: value, 'dur_s': seconds}} for kernels whose name
+    contains name_part."""
+    out = {}
+    for r in rows:
+        if name_part not in r["Kernel_Name"]:
+            continue
+        d = out.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["dur_s"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    return out
+
+
+def _mean(vals):
+    vals = list(vals)
+    return sum(vals) / len(vals) if vals else float("nan")
+
+
+def summarize_trace(stats_csv: str, out: str, command: str) -> None:
+    """Text summary of a rocprofv3 --kernel-trace --stats kernel_stats.csv."""
+    rows = _read_csv(stats_csv)
+    lines = ["# rocprofv3 kernel statistics (durations in microseconds)",
+             "# command: " + command, ""]
+    for r in rows:
+        name = r.get("Name") or r.get("KernelName") or r.get("Kernel_Name")
+        calls = int(float(r.get("Calls", 0)))
+        avg_us = float(r.get("AverageNs", 0)) / 1e3
+        lines.append("kernel: %s" % name)
+        lines.append("  calls: %d  average_us: %.2f  min_us: %.2f  max_us: %.2f  percent: %s"
+                     % (calls, avg_us, float(r.get("MinNs", 0)) / 1e3,
+                        float(r.get("MaxNs", 0)) / 1e3, r.get("Percentage", "")))
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fetch_csv: str,
+                       write_csv: str, sq_csvs, commands) -> None:
+    """Counter summary: utilisation, instruction counts against the closed
+    forms, LDS bank conflicts and HBM traffic scaled by a copy kernel of known
+    size (FETCH_SIZE / WRITE_SIZE in KiB per dispatch)."""
+    from workloads import WORKLOADS
+    from tiled_fp32_gemm_sgemm_amd import model
+    import tiled_fp32_gemm_sgemm_amd as sg
+    w = WORKLOADS[workload]
+    L = ["# rocprofv3 hardware counters, %s path, workload %s" % (path, w.describe()),
+         "# commands (one counter pass each, run from the repository root):"]
+    L += ["#   " + c for c in commands]
+    L.append("kernel_source_sha256_16: %s" % kernel_source_hash())
+    copy_part = "MulFunctor"
+    fetch = _per_dispatch(_read_csv(fetch_csv), kernel_part) if fetch_csv else {}
+    write = _per_dispatch(_read_csv(write_csv), kernel_part) if write_csv else {}
+    hbm = None
+    if fetch and write:
+        cf = _per_dispatch(_read_csv(fetch_csv), copy_part)
+        cw = _per_dispatch(_read_csv(write_csv), copy_part)
+        f_copy = _mean(d["FETCH_SIZE"] for d in cf.values())
+        w_copy = _mean(d["WRITE_SIZE"] for d in cw.values())
+        f_scale = COPY_BYTES / (f_copy * 1024.0)
+        w_scale = COPY_BYTES / (w_copy * 1024.0)
+        f_kib = _mean(d["FETCH_SIZE"] for d in fetch.values())
+        w_kib = _mean(d["WRITE_SIZE"] for d in write.values())
+        hbm = f_kib * 1024 * f_scale + w_kib * 1024 * w_scale
+        L += ["copy_kernel_bytes_each_way: %d" % COPY_BYTES,
+              "copy_fetch_size_kib: %.1f" % f_copy, "copy_write_size_kib: %.1f" % w_copy,
+              "fetch_scale: %.4f" % f_scale, "write_scale: %.4f" % w_scale,
+              "kernel_fetch_size_kib: %.1f" % f_kib, "kernel_write_size_kib: %.1f" % w_kib,
+              "hbm_read_bytes_per_launch: %.0f" % (f_kib * 1024 * f_scale),
+              "hbm_write_bytes_per_launch: %.0f" % (w_kib * 1024 * w_scale),
+              "hbm_bytes_per_launch: %.0f" % hbm,
+              "compulsory_bytes: %d" % model.compulsory_bytes(w.M, w.N, w.K, w.batch)]
+    merged = {}
+    for c in sq_csvs:
+        for d in _per_dispatch(_read_csv(c), kernel_part).values():
+            for k, v in d.items():
+                if k not in ("name", "dur_s"):
+                    merged.setdefault(k, []).append(v)
+            if "GRBM_GUI_ACTIVE" in d and "SQ_VALU_MFMA_BUSY_CYCLES" in d:
+                merged.setdefault("_util", []).append(
+                    d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] / 8 * 1024))
+                merged.setdefault("_clk", []).append(d["GRBM_GUI_ACTIVE"] / 8 / d["dur_s"])
+            merged.setdefault("_name", []).append(d["name"])
+    if merged.get("_name"):
+        L.append("kernel: %s" % merged["_name"][0])
+    for k in sorted(merged):
+        if not k.startswith("_"):
+            L.append("%s: %.6g" % (k, _mean(merged[k])))
+    if "_util" in merged:
+        L.append("mfma_busy_fraction: %.4f" % _mean(merged["_util"]))
+        L.append("effective_clock_ghz_under_profiler: %.3f" % (_mean(merged["_clk"]) / 1e9))
+    if path == "mfma" and "SQ_INSTS_VALU_MFMA_F32" in merged:
+        cfg = sg.select_config(w.M, w.N, w.K, w.batch)
+        info = sg.config_info(cfg)
+        mi = 16 if info["name"].startswith("mfma16") else 32
+        # the counter is summed over the 8 dies x 4 shader engines it is read from
+        want = model.mfma_instructions(w.M, w.N, w.K, info["bm"], info["bn"], info["bk"], mi,
+                                       w.batch)
+        L.append("mfma_instructions_closed_form: %d (tile %s)" % (want, info["name"]))
+        L.append("global_to_lds_values_model: %d" % model.global_to_shared_loads(
+            w.M, w.N, w.K, info["bm"], info["bn"], info["bk"], padded=True))
+    if path == "valu" and "SQ_INSTS_VALU_FMA_F32" in merged:
+        L.append("valu_fma_instructions_closed_form: %d" % model.valu_fma_instructions(
+            w.M, w.N, w.K, batch=w.batch))
+    if "SQ_LDS_BANK_CONFLICT" in merged and "SQ_LDS_IDX_ACTIVE" in merged:
+        c = _mean(merged["SQ_LDS_BANK_CONFLICT"])
+        a = _mean(merged["SQ_LDS_IDX_ACTIVE"])
+        L.append("lds_bank_conflicts_per_access: %.4f" % (c / max(1.0, a - c)))
+    open(out, "w").write("\n".join(L) + "\n")
 
 
 def cpu_baseline(w, A, B, target_s: float = 12.0):
@@ -99,7 +213,25 @@ def main(argv=None) -> int:
     ap.add_argument("--no-comparator", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain copy kernel of known size (counter scaling)")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
+                    help="write a text summary of a rocprofv3 kernel-stats csv to --out")
+    ap.add_argument("--summarize-counters", action="store_true",
+                    help="write a counter summary from --fetch-csv/--write-csv/--sq-csv to --out")
+    ap.add_argument("--fetch-csv")
+    ap.add_argument("--write-csv")
+    ap.add_argument("--sq-csv", action="append", default=[])
+    ap.add_argument("--kernel-part", default="sgemm_mfma_kernel")
+    ap.add_argument("--command", action="append", default=[])
+    ap.add_argument("--out")
     args = ap.parse_args(argv)
+
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.out, " ".join(args.command))
+        return 0
+    if args.summarize_counters:
+        summarize_counters(args.out, args.workload, args.path, args.kernel_part, args.fetch_csv,
+                           args.write_csv, args.sq_csv, args.command)
+        return 0
 
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs on a single MI355X and has no "
@@ -168,7 +300,7 @@ def main(argv=None) -> int:
     traffic = read_traffic(TRAFFIC_FILE, args.workload, args.path)
     roofline = {"bound": "mfma" if args.path == "mfma" else "alu",
                 "achieved": tflops,
-                "peak": PEAK_FP32_TFLOPS if args.path == "mfma" else PEAK_FP32_TFLOPS / 2,
+                "peak": PEAK_FP32_TFLOPS,
                 "unit": "TFLOP/s",
                 "frac": None,
                 "traffic": traffic,
