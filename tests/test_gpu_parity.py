@@ -87,7 +87,7 @@ def _call(path, *args, **kw):
     return run_gpu(*args, path=path, **kw)
 
 
-ALL_PATHS = ["valu"] + ["cfg%d" % i for i in range(10)]
+ALL_PATHS = ["valu"] + ["cfg%d" % i for i in range(14)]
 
 
 @pytest.mark.parametrize("path", ALL_PATHS)
@@ -179,7 +179,7 @@ def test_invalid_arguments_enqueue_nothing():
 
 # ------------------------------------------------------------------ batched
 
-@pytest.mark.parametrize("path", ["mfma", "valu", "cfg1", "cfg2", "cfg5", "cfg6", "cfg7"])
+@pytest.mark.parametrize("path", ["mfma", "valu", "cfg1", "cfg2", "cfg5", "cfg6", "cfg7", "cfg11", "cfg13"])
 def test_batched_ragged_members_differ(path):
     M, N, K, lda, ldb, ldc, batch = 45, 77, 33, 36, 80, 79, 6
     sA, sB, sC = M * lda + 5, K * ldb + 3, M * ldc + 11

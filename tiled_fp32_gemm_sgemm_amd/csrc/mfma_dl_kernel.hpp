@@ -1,0 +1,336 @@
+// FP32 GEMM on the gfx950 matrix cores with direct global->LDS staging.
+//
+// Same product, tiling, register tiles and reduction order as mfma_kernel.hpp
+// (C = A x B, row-major, beta = 0; one workgroup per BM x BN tile; K in BK
+// slices; "Tiling Strategies" sections 2-3, "CMU DLSys Lecture 12: GPU
+// Acceleration" section 5, "Tiling Hierarchy on GPUs" "Register Tiling" and
+// "Register prefetching"), with a different global->LDS loader:
+//
+//  * Each slice is copied by buffer_load_dwordx4 ... lds: one instruction moves
+//    64 lanes x 16 bytes from global memory straight into a contiguous 1 KB
+//    chunk of LDS (lane L fills bytes 16L..16L+15), with no VGPR staging and
+//    no ds_write.  On gfx950 a vector-memory or LDS-write instruction issued
+//    between MFMAs costs matrix-core cycles, so this halves the instructions
+//    that feed the matrix core.
+//  * The layout in LDS is fixed by lane order, so each lane's global source
+//    is chosen to realise the bank-conflict-free layouts: lane L of chunk c
+//    fills physical quad q = 64c + L; its source is the logical quad that the
+//    swizzle maps there.  Per-lane source offsets are computed once per block
+//    (and once more for a K-tail slice) and stay in VGPRs; the per-slice
+//    advance lives in the scalar buffer descriptor, so the loop spends no VALU
+//    instructions on global addresses.
+//  * Masking: a quad that lies wholly outside the matrix gets an offset past
+//    the descriptor's range, and the buffer unit writes zeros for it (the
+//    zero-filled masked load of Lecture 12 section 5).  A slice with quads
+//    that straddle the edge (K or N not a multiple of 4) falls back to masked
+//    loads through registers.
+//
+// LDS layouts (64 banks of 4 bytes on gfx950):
+//  * A slice As[m][k], BK floats per row, quad kq of row r stored at
+//    kq ^ ((r / rows_per_256_bytes) % (BK/4)) (as in mfma_kernel.hpp).
+//  * B slice Bs[k][n], BN floats per row with no padding.  With MI = 32 the
+//    32 lanes of a ds_read_b32 pass (ds_read_b32 sees 32 banks) read 32
+//    consecutive floats of one k row: conflict-free with no padding.  (With
+//    MI = 16 two k rows share a pass; the flip below keeps the layout
+//    consistent but does not make those reads conflict-free, so the tile
+//    table only uses MI = 32 here.)
+#pragma once
+
+#include <type_traits>
+
+#include "mfma_kernel.hpp"
+#include "tile_common.hpp"
+
+namespace sgemm_dev {
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Byte offset that is outside every descriptor range used here: the buffer
+// unit returns zeros for it.
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MI_, int OCC_, int GROUP_M_>
+struct DlTile {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_;
+    static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
+    static constexpr int MI = MI_;
+    static constexpr int OCC = OCC_;
+    static constexpr int GROUP_M = GROUP_M_;
+    static constexpr int NW = WAVES_M * WAVES_N;         // waves per workgroup
+    static constexpr int NT = 64 * NW;
+    static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
+    static constexpr int TM = WTM / MI, TN = WTN / MI;
+    static constexpr int LG = 64 / MI;
+    static constexpr int KPL = BK / LG;
+    static constexpr int QPR = BK / 4;                   // quads per A row
+    static constexpr int B_QPR = BN / 4;                 // quads per B row
+    static constexpr int LDB = BN;
+    static constexpr int A_FLOATS = BM * BK;
+    static constexpr int B_FLOATS = BK * BN;
+    static constexpr int BUF_FLOATS = A_FLOATS + B_FLOATS;
+    static constexpr int RPB = 16 / QPR;
+    static constexpr int KG = 4;
+    static constexpr int NKG = KPL / KG;
+    static constexpr int HOLD = 2;                       // k steps issued after the barrier
+    static constexpr int A_CH = BM * QPR / 64;           // 1 KB chunks per A slice
+    static constexpr int B_CH = BK * B_QPR / 64;         // 1 KB chunks per B slice
+    static constexpr int A_CHW = A_CH / NW;              // chunks per wave
+    static constexpr int B_CHW = B_CH / NW;
+    static constexpr int BFLIP = MI == 16 ? 8 : 0;       // quad flip on odd lane-group row blocks
+    // Register-staged fallback: quads per thread per slice.
+    static constexpr int A_VEC = BM * QPR / NT;
+    static constexpr int B_VEC = BK * B_QPR / NT;
+    static constexpr int LDS_BYTES = 2 * BUF_FLOATS * 4;
+
+    static_assert(MI == 16 || MI == 32, "MFMA tile edge");
+    static_assert(BK == 16 || BK == 32, "BK must be 16 or 32");
+    static_assert(KPL % KG == 0 && NKG % 2 == 0, "whole, even number of A operand groups");
+    static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must be MFMA tile multiples");
+    static_assert(A_CH % NW == 0 && B_CH % NW == 0, "slice chunks must split over the waves");
+    static_assert(BN % 64 == 0 && B_QPR % 16 == 0, "B rows must span whole bank rows");
+    static_assert((BM * QPR) % NT == 0 && (BK * B_QPR) % NT == 0, "fallback copy must split");
+    static_assert(MI == 32 || BN >= 64, "the B flip needs 64-float rows");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+
+    static __device__ __forceinline__ int swz(int r) { return (r / RPB) % QPR; }
+    // Physical quad of logical quad nq in B row k is nq ^ flip(k).
+    static __device__ __forceinline__ int flip(int k) { return ((k / KPL) & 1) * BFLIP; }
+};
+
+// The kernel body lives in a device function: it uses device-only builtins
+// and types, and keeping them out of the __global__ function's own body lets
+// the host compilation pass emit the launch stub.
+template <class T>
+__device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
+    using Op = MfmaOp<T::MI>;
+    __shared__ __attribute__((aligned(16))) float smem[2 * T::BUF_FLOATS];
+
+    const TileCoord tc = map_block(p, T::GROUP_M);
+    const int m0 = tc.tm * T::BM;
+    const int n0 = tc.tn * T::BN;
+    const float* const A = p.A + (int64_t)tc.b * p.strideA + (int64_t)m0 * p.lda;
+    const float* const B = p.B + (int64_t)tc.b * p.strideB + n0;
+    float* const C = p.C + (int64_t)tc.b * p.strideC + (int64_t)m0 * p.ldc + n0;
+    const int rows_left = p.M - m0;
+    const int cols_left = p.N - n0;
+    const bool full_mn = rows_left >= T::BM && cols_left >= T::BN;
+    const int nslices = (p.K + T::BK - 1) / T::BK;
+
+    const int tid = threadIdx.x;
+    const int lane = tid % 64;
+    const int wave = tid / 64;
+
+    // ---------------------------------------------------------------- loader
+    // A slice for k0 into buffer `buf`: descriptor over rows m0.. of A from
+    // column k0; B slice: descriptor over rows k0.. of B from column n0.
+    const uint32_t a_span = (uint32_t)(((int64_t)(T::BM - 1) * p.lda + T::BK) * 4);
+    const uint32_t b_span = (uint32_t)(((int64_t)(T::BK - 1) * p.ldb + T::BN) * 4);
+
+    uint32_t a_off[T::A_CHW];
+    uint32_t b_off[T::B_CHW];
+    // Per-lane source offsets of this wave's chunks; quads outside the matrix
+    // (or past K when `kleft` < BK) point out of range and load as zeros.
+    auto make_offsets = [&](int kleft) {
+#pragma unroll
+        for (int j = 0; j < T::A_CHW; ++j) {
+            const int q = 64 * (wave * T::A_CHW + j) + lane;
+            const int r = q / T::QPR;
+            const int kq = (q % T::QPR) ^ T::swz(r);
+            const bool ok = r < rows_left && 4 * kq < kleft;
+            a_off[j] = ok ? (uint32_t)(((int64_t)r * p.lda + 4 * kq) * 4) : kOutOfRange;
+        }
+#pragma unroll
+        for (int j = 0; j < T::B_CHW; ++j) {
+            const int q = 64 * (wave * T::B_CHW + j) + lane;
+            const int k = q / T::B_QPR;
+            const int nq = (q % T::B_QPR) ^ T::flip(k);
+            const bool ok = k < kleft && 4 * nq < cols_left;
+            b_off[j] = ok ? (uint32_t)(((int64_t)k * p.ldb + 4 * nq) * 4) : kOutOfRange;
+        }
+    };
+
+    auto load_direct = [&](int k0, int buf) {
+        float* const dstA = smem + buf * T::BUF_FLOATS;
+        float* const dstB = dstA + T::A_FLOATS;
+        const __amdgpu_buffer_rsrc_t ra =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(A + k0), (short)0, (int)a_span, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            (void*)(B + (int64_t)k0 * p.ldb), (short)0, (int)b_span, 0x00020000);
+#pragma unroll
+        for (int j = 0; j < T::A_CHW; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                ra, (lds_void_t*)(dstA + 256 * (wave * T::A_CHW + j)), 16, a_off[j], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < T::B_CHW; ++j)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rb, (lds_void_t*)(dstB + 256 * (wave * T::B_CHW + j)), 16, b_off[j], 0, 0, 0);
+    };
+
+    // Fallback for slices with quads that straddle the matrix edge: masked
+    // element loads through registers, written to the same layout.
+    auto load_staged = [&](int k0, int buf) {
+        float* const As = smem + buf * T::BUF_FLOATS;
+        float* const Bs = As + T::A_FLOATS;
+        // One quad at a time: slow, but holds no registers across the slice.
+#pragma unroll 1
+        for (int v = 0; v < T::A_VEC; ++v) {
+            const int q = tid + v * T::NT;
+            const int r = q / T::QPR;
+            const int pq = q % T::QPR;
+            const int kq = pq ^ T::swz(r);
+            const f32x4 x = ldg4_masked(A + (int64_t)r * p.lda + k0 + 4 * kq,
+                                        r < rows_left ? p.K - (k0 + 4 * kq) : 0);
+            *(f32x4*)(As + 4 * q) = x;
+        }
+#pragma unroll 1
+        for (int v = 0; v < T::B_VEC; ++v) {
+            const int q = tid + v * T::NT;
+            const int k = q / T::B_QPR;
+            const int nq = (q % T::B_QPR) ^ T::flip(k);
+            const f32x4 x = ldg4_masked(B + (int64_t)(k0 + k) * p.ldb + 4 * nq,
+                                        k0 + k < p.K ? cols_left - 4 * nq : 0);
+            *(f32x4*)(Bs + 4 * q) = x;
+        }
+    };
+
+    // Direct staging needs 31-bit descriptor spans and whole-quad edges.
+    const bool spans_fit = ((int64_t)(T::BM - 1) * p.lda + T::BK) * 4 < (int64_t)kOutOfRange &&
+                           ((int64_t)(T::BK - 1) * p.ldb + T::BN) * 4 < (int64_t)kOutOfRange;
+    const bool quads_whole_n = full_mn || (p.N % 4 == 0);
+    const bool quads_whole_k = (p.K % 4 == 0);
+    const int full_slices = p.K / T::BK;
+
+    make_offsets(T::BK);
+    // Returns true when the slice went through registers (already in LDS).
+    auto load_slice = [&](int s, int buf) {
+        const int k0 = s * T::BK;
+        const bool tail = s >= full_slices;
+        if (spans_fit && quads_whole_n && (!tail || quads_whole_k)) {
+            if (tail) make_offsets(p.K - k0);
+            load_direct(k0, buf);
+        } else {
+            load_staged(k0, buf);
+        }
+    };
+
+    // --------------------------------------------------------------- compute
+    const int wy = wave / T::WAVES_N;
+    const int wx = wave % T::WAVES_N;
+    const int li = lane % T::MI;
+    const int lg = lane / T::MI;
+
+    typename Op::acc_t acc[T::TM][T::TN];
+#pragma unroll
+    for (int mi = 0; mi < T::TM; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < T::TN; ++ni)
+#pragma unroll
+            for (int r = 0; r < Op::ACC; ++r) acc[mi][ni][r] = 0.0f;
+
+    const int a_row = wy * T::WTM + li;
+    const int a_swz = T::swz(a_row);
+    // B column of this lane in each column tile, with the row-block flip
+    // applied (every k this lane reads has k / KPL = lg).
+    int b_col[T::TN];
+#pragma unroll
+    for (int ni = 0; ni < T::TN; ++ni)
+        b_col[ni] = (wx * T::WTN + T::MI * ni + li) ^ (4 * T::flip(lg * T::KPL));
+
+    // One operand group = KG consecutive k steps: one 16-byte quad of A per
+    // row tile and KG values of B per column tile.  The operands of group g+1
+    // are read before the MFMAs of group g are issued ("Tiling Hierarchy on
+    // GPUs", "Register prefetching").
+    auto read_group = [&](int buf, int g, f32x4 (&a)[T::TM], float (&b)[T::TN][T::KG]) {
+        const float* const As = smem + buf * T::BUF_FLOATS;
+        const float* const Bl = As + T::A_FLOATS + (lg * T::KPL + g * T::KG) * T::LDB;
+        const int quad = lg * (T::KPL / 4) + g;
+#pragma unroll
+        for (int mi = 0; mi < T::TM; ++mi)
+            a[mi] = *(const f32x4*)(As + (a_row + T::MI * mi) * T::BK + ((quad ^ a_swz) << 2));
+#pragma unroll
+        for (int s = 0; s < T::KG; ++s)
+#pragma unroll
+            for (int ni = 0; ni < T::TN; ++ni) b[ni][s] = Bl[s * T::LDB + b_col[ni]];
+    };
+
+    auto mfma_steps = [&](const f32x4 (&a)[T::TM], const float (&b)[T::TN][T::KG], int s0,
+                          int s1) {
+#pragma unroll
+        for (int s = s0; s < s1; ++s)
+#pragma unroll
+            for (int mi = 0; mi < T::TM; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < T::TN; ++ni)
+                    acc[mi][ni] = Op::mma(a[mi][s], b[ni][s], acc[mi][ni]);
+    };
+
+    f32x4 opa[2][T::TM];
+    float opb[2][T::TN][T::KG];
+
+    // One slice held in LDS buffer `buf` (operand group g uses set g & 1):
+    // the next slice's copy is started first and is complete at the barrier;
+    // the last HOLD k steps of MFMAs run after the barrier, behind the reads of
+    // the next slice's first operand group, so the matrix core keeps working
+    // while the waves synchronise.
+    auto slice = [&](int buf, int s) {
+        const bool more = s + 1 < nslices;
+        if (more) load_slice(s + 1, buf ^ 1);
+#pragma unroll
+        for (int g = 0; g < T::NKG; ++g) {
+            if (g + 1 < T::NKG) {
+                if (g & 1)
+                    read_group(buf, g + 1, opa[0], opb[0]);
+                else
+                    read_group(buf, g + 1, opa[1], opb[1]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            const int s1 = g + 1 < T::NKG ? T::KG : T::KG - T::HOLD;
+            if (g & 1)
+                mfma_steps(opa[1], opb[1], 0, s1);
+            else
+                mfma_steps(opa[0], opb[0], 0, s1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (more) {
+            // The direct copies count on vmcnt: wait for this wave's, then the
+            // barrier makes every wave's part of the slice visible.
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            read_group(buf ^ 1, 0, opa[0], opb[0]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // The last group, NKG-1, is odd: operand set 1.
+        mfma_steps(opa[1], opb[1], T::KG - T::HOLD, T::KG);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    load_slice(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    read_group(0, 0, opa[0], opb[0]);
+    for (int s = 0; s < nslices; ++s) slice(s & 1, s);
+
+    // Epilogue: accumulator r of lane (li, lg) in MFMA tile (mi, ni) is row
+    // Op::row(r, lg) and column li of that tile.
+#pragma unroll
+    for (int mi = 0; mi < T::TM; ++mi) {
+#pragma unroll
+        for (int ni = 0; ni < T::TN; ++ni) {
+            const int col = wx * T::WTN + T::MI * ni + li;
+#pragma unroll
+            for (int r = 0; r < Op::ACC; ++r) {
+                const int row = wy * T::WTM + T::MI * mi + Op::row(r, lg);
+                if (full_mn || (row < rows_left && col < cols_left))
+                    C[(int64_t)row * p.ldc + col] = acc[mi][ni][r];
+            }
+        }
+    }
+}
+
+template <class T>
+__global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(T::OCC)))
+void sgemm_mfma_dl_kernel(GemmArgs p) {
+    sgemm_mfma_dl_body<T>(p);
+}
+
+}  // namespace sgemm_dev

@@ -10,6 +10,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include "mfma_dl_kernel.hpp"
 #include "mfma_kernel.hpp"
 #include "tile_common.hpp"
 #include "valu_kernel.hpp"
@@ -32,6 +33,11 @@ using Cfg64x64k32m16 = MfmaTile<64, 64, 32, 2, 2, 16, 4, 8>;     // 4 waves of 3
 // One wave per SIMD, 128x128 wave tiles, accumulators in the AGPR file.
 using Cfg256x256m32w1 = MfmaTile<256, 256, 16, 2, 2, 32, 1, 8>;
 using Cfg256x256k32m32w1 = MfmaTile<256, 256, 32, 2, 2, 32, 1, 8>;
+// Direct global->LDS staging.
+using Dl256x256k32m32 = DlTile<256, 256, 32, 2, 4, 32, 2, 8>;      // 8 waves of 128x64
+using Dl256x256k16m32 = DlTile<256, 256, 16, 2, 4, 32, 2, 8>;      // 8 waves of 128x64
+using Dl256x128k32m32 = DlTile<256, 128, 32, 2, 2, 32, 1, 8>;      // 4 waves of 128x64
+using Dl128x128k32m32 = DlTile<128, 128, 32, 2, 2, 32, 2, 8>;      // 4 waves of 64x64
 
 struct ConfigEntry {
     const char* name;
@@ -43,6 +49,8 @@ struct ConfigEntry {
 
 #define SGEMM_CFG(T, name, eff, per_cu) \
     { name, T::BM, T::BN, T::BK, T::NT, (const void*)&sgemm_mfma_kernel<T>, eff, per_cu }
+#define SGEMM_DL_CFG(T, name, eff, per_cu) \
+    { name, T::BM, T::BN, T::BK, T::NT, (const void*)&sgemm_mfma_dl_kernel<T>, eff, per_cu }
 
 const ConfigEntry kConfigs[] = {
     SGEMM_CFG(Cfg256x128, "mfma32_256x128x16_w2x2", 0.94, 2),
@@ -55,8 +63,13 @@ const ConfigEntry kConfigs[] = {
     SGEMM_CFG(Cfg64x64k32m16, "mfma16_64x64x32_w2x2", 0.60, 4),
     SGEMM_CFG(Cfg256x256m32w1, "mfma32_256x256x16_w2x2", 0.98, 1),
     SGEMM_CFG(Cfg256x256k32m32w1, "mfma32_256x256x32_w2x2", 0.98, 1),
+    SGEMM_DL_CFG(Dl256x256k32m32, "dl32_256x256x32_w2x4", 1.04, 1),
+    SGEMM_DL_CFG(Dl256x256k16m32, "dl32_256x256x16_w2x4", 1.02, 1),
+    SGEMM_DL_CFG(Dl256x128k32m32, "dl32_256x128x32_w2x2", 0.96, 1),
+    SGEMM_DL_CFG(Dl128x128k32m32, "dl32_128x128x32_w2x2", 0.92, 2),
 };
 #undef SGEMM_CFG
+#undef SGEMM_DL_CFG
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 constexpr int kNumCu = 256;  // MI355X compute units
 
