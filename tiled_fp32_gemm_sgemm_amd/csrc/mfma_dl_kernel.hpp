@@ -118,7 +118,9 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
 
     const int tid = threadIdx.x;
     const int lane = tid % 64;
-    const int wave = tid / 64;
+    // The wave index is uniform across the wave; saying so keeps every
+    // per-wave address (LDS chunk bases for M0 in particular) in SGPRs.
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
 
     // ---------------------------------------------------------------- loader
     // A slice for k0 into buffer `buf`: descriptor over rows m0.. of A from
@@ -128,8 +130,8 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
 
     uint32_t a_off[T::A_CHW];
     uint32_t b_off[T::B_CHW];
-    // Per-lane source offsets of this wave's chunks; quads outside the matrix
-    // (or past K when `kleft` < BK) point out of range and load as zeros.
+    // Per-lane source offsets of this wave's chunks, fixed for the block;
+    // quads outside the matrix point out of range and load as zeros.
     auto make_offsets = [&](int kleft) {
 #pragma unroll
         for (int j = 0; j < T::A_CHW; ++j) {
@@ -193,24 +195,22 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
         }
     };
 
-    // Direct staging needs 31-bit descriptor spans and whole-quad edges.
-    const bool spans_fit = ((int64_t)(T::BM - 1) * p.lda + T::BK) * 4 < (int64_t)kOutOfRange &&
-                           ((int64_t)(T::BK - 1) * p.ldb + T::BN) * 4 < (int64_t)kOutOfRange;
-    const bool quads_whole_n = full_mn || (p.N % 4 == 0);
-    const bool quads_whole_k = (p.K % 4 == 0);
+    // Direct staging needs 31-bit descriptor spans and whole-quad N edges;
+    // a partial K slice (the last one when BK does not divide K) goes through
+    // registers, so the offsets stay fixed for the whole loop.
+    const bool direct_ok =
+        ((int64_t)(T::BM - 1) * p.lda + T::BK) * 4 < (int64_t)kOutOfRange &&
+        ((int64_t)(T::BK - 1) * p.ldb + T::BN) * 4 < (int64_t)kOutOfRange &&
+        (full_mn || (p.N % 4 == 0));
     const int full_slices = p.K / T::BK;
 
     make_offsets(T::BK);
-    // Returns true when the slice went through registers (already in LDS).
     auto load_slice = [&](int s, int buf) {
         const int k0 = s * T::BK;
-        const bool tail = s >= full_slices;
-        if (spans_fit && quads_whole_n && (!tail || quads_whole_k)) {
-            if (tail) make_offsets(p.K - k0);
+        if (direct_ok && s < full_slices)
             load_direct(k0, buf);
-        } else {
+        else
             load_staged(k0, buf);
-        }
     };
 
     // --------------------------------------------------------------- compute

@@ -190,7 +190,7 @@ void sgemm_mfma_kernel(GemmArgs p) {
     };
 
     const int lane = tid % 64;
-    const int wave = tid / 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);  // uniform per wave
     const int wy = wave / T::WAVES_N;
     const int wx = wave % T::WAVES_N;
     const int li = lane % T::MI;  // row of the A operand / column of the B operand
