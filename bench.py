@@ -107,7 +107,7 @@ def summarize_trace(stats_csv: str, out: str, command: str) -> None:
 
 
 def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fetch_csv: str,
-                       write_csv: str, sq_csvs, commands) -> None:
+                       write_csv: str, sq_csvs, commands, config=None) -> None:
     """Counter summary: utilisation, instruction counts against the closed
     forms, LDS bank conflicts and HBM traffic scaled by a copy kernel of known
     size (FETCH_SIZE / WRITE_SIZE in KiB per dispatch)."""
@@ -160,16 +160,18 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
     if "_util" in merged:
         L.append("mfma_busy_fraction: %.4f" % _mean(merged["_util"]))
         L.append("effective_clock_ghz_under_profiler: %.3f" % (_mean(merged["_clk"]) / 1e9))
-    if path == "mfma" and "SQ_INSTS_VALU_MFMA_F32" in merged:
-        cfg = sg.select_config(w.M, w.N, w.K, w.batch)
+    if path == "mfma":
+        cfg = sg.select_config(w.M, w.N, w.K, w.batch) if config is None else config
         info = sg.config_info(cfg)
         mi = 16 if info["name"].startswith("mfma16") else 32
-        # the counter is summed over the 8 dies x 4 shader engines it is read from
         want = model.mfma_instructions(w.M, w.N, w.K, info["bm"], info["bn"], info["bk"], mi,
                                        w.batch)
         L.append("mfma_instructions_closed_form: %d (tile %s)" % (want, info["name"]))
-        L.append("global_to_lds_values_model: %d" % model.global_to_shared_loads(
-            w.M, w.N, w.K, info["bm"], info["bn"], info["bk"], padded=True))
+        staged = model.global_to_shared_loads(w.M, w.N, w.K, info["bm"], info["bn"],
+                                              info["bk"], padded=True) * w.batch
+        L.append("global_to_lds_values_model: %d" % staged)
+        # one 64-lane dwordx4 instruction moves 256 values
+        L.append("global_dwordx4_wave_instructions_closed_form: %d" % (staged // 256))
     if path == "valu" and "SQ_INSTS_VALU_FMA_F32" in merged:
         L.append("valu_fma_instructions_closed_form: %d" % model.valu_fma_instructions(
             w.M, w.N, w.K, batch=w.batch))
@@ -220,7 +222,7 @@ def main(argv=None) -> int:
     ap.add_argument("--fetch-csv")
     ap.add_argument("--write-csv")
     ap.add_argument("--sq-csv", action="append", default=[])
-    ap.add_argument("--kernel-part", default="sgemm_mfma_kernel")
+    ap.add_argument("--kernel-part", default="sgemm_mfma")
     ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--out")
     args = ap.parse_args(argv)
@@ -230,7 +232,7 @@ def main(argv=None) -> int:
         return 0
     if args.summarize_counters:
         summarize_counters(args.out, args.workload, args.path, args.kernel_part, args.fetch_csv,
-                           args.write_csv, args.sq_csv, args.command)
+                           args.write_csv, args.sq_csv, args.command, args.config)
         return 0
 
     if args.gpus != 1:

@@ -81,6 +81,8 @@ def test_select_config_host_logic():
                   (16384, 4096, 4096, 1), (128, 128, 128, 1024), (1, 1, 1, 1)]:
         c = sg.select_config(*shape)
         assert 0 <= c < n
+        # the unswizzled control build exists for the bank-conflict counter only
+        assert "unswizzled" not in sg.config_info(c)["name"]
     assert _native.lib().sgemm_select_config(-1, 1, 1, 1) == -1
 
 

@@ -16,24 +16,31 @@
 //    is chosen to realise the bank-conflict-free layouts: lane L of chunk c
 //    fills physical quad q = 64c + L; its source is the logical quad that the
 //    swizzle maps there.  Per-lane source offsets are computed once per block
-//    (and once more for a K-tail slice) and stay in VGPRs; the per-slice
-//    advance lives in the scalar buffer descriptor, so the loop spends no VALU
-//    instructions on global addresses.
+//    and stay in VGPRs; the per-slice advance lives in the scalar buffer
+//    descriptor, and the wave index is made wave-uniform so that every LDS
+//    destination (M0) is computed on the scalar unit: the loop spends no VALU
+//    instructions on the copies.
 //  * Masking: a quad that lies wholly outside the matrix gets an offset past
 //    the descriptor's range, and the buffer unit writes zeros for it (the
-//    zero-filled masked load of Lecture 12 section 5).  A slice with quads
-//    that straddle the edge (K or N not a multiple of 4) falls back to masked
-//    loads through registers.
+//    zero-filled masked load of Lecture 12 section 5).  Slices with quads that
+//    straddle an edge (the last slice when BK does not divide K, or N not a
+//    multiple of 4) are copied with masked loads through registers.
 //
-// LDS layouts (64 banks of 4 bytes on gfx950):
+// LDS layouts.  gfx950 serves ds_read_b128 16 lanes per pass over 64 banks of
+// 4 bytes, and ds_read_b32 32 lanes per pass over 32 banks (measured):
 //  * A slice As[m][k], BK floats per row, quad kq of row r stored at
-//    kq ^ ((r / rows_per_256_bytes) % (BK/4)) (as in mfma_kernel.hpp).
-//  * B slice Bs[k][n], BN floats per row with no padding.  With MI = 32 the
-//    32 lanes of a ds_read_b32 pass (ds_read_b32 sees 32 banks) read 32
-//    consecutive floats of one k row: conflict-free with no padding.  (With
-//    MI = 16 two k rows share a pass; the flip below keeps the layout
-//    consistent but does not make those reads conflict-free, so the tile
-//    table only uses MI = 32 here.)
+//    kq ^ ((r / rows_per_256_bytes) % (BK/4)) (as in mfma_kernel.hpp): the 16
+//    rows of a b128 pass hit 16 distinct quads of the bank row.
+//  * B slice Bs[k][n], BN floats per row.  With MI = 32 the 32 lanes of a
+//    ds_read_b32 pass read 32 consecutive floats of one k row: conflict-free
+//    with no padding.  With MI = 16 a pass covers two lane groups, 16 floats
+//    each, from rows KPL apart; the rows of odd lane groups are stored with
+//    their quads flipped by 4 (16 floats) so that the two halves land on
+//    disjoint banks.  The compiler still pairs reads of adjacent k rows into
+//    ds_read2_b32, and those conflict (measured), so the tile table uses
+//    MI = 32 only.
+//  * SWIZZLE = false stores A unswizzled: a control build whose A reads
+//    conflict, used to show that the bank-conflict counter sees the layout.
 #pragma once
 
 #include <type_traits>
@@ -49,13 +56,15 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // unit returns zeros for it.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MI_, int OCC_, int GROUP_M_>
+template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MI_, int OCC_, int GROUP_M_,
+          bool SWIZZLE_ = true>
 struct DlTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int MI = MI_;
     static constexpr int OCC = OCC_;
     static constexpr int GROUP_M = GROUP_M_;
+    static constexpr bool SWIZZLE = SWIZZLE_;
     static constexpr int NW = WAVES_M * WAVES_N;         // waves per workgroup
     static constexpr int NT = 64 * NW;
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
@@ -76,7 +85,7 @@ struct DlTile {
     static constexpr int B_CH = BK * B_QPR / 64;         // 1 KB chunks per B slice
     static constexpr int A_CHW = A_CH / NW;              // chunks per wave
     static constexpr int B_CHW = B_CH / NW;
-    static constexpr int BFLIP = MI == 16 ? 8 : 0;       // quad flip on odd lane-group row blocks
+    static constexpr int BFLIP = MI == 16 ? 4 : 0;       // quad flip on odd lane-group row blocks
     // Register-staged fallback: quads per thread per slice.
     static constexpr int A_VEC = BM * QPR / NT;
     static constexpr int B_VEC = BK * B_QPR / NT;
@@ -89,10 +98,10 @@ struct DlTile {
     static_assert(A_CH % NW == 0 && B_CH % NW == 0, "slice chunks must split over the waves");
     static_assert(BN % 64 == 0 && B_QPR % 16 == 0, "B rows must span whole bank rows");
     static_assert((BM * QPR) % NT == 0 && (BK * B_QPR) % NT == 0, "fallback copy must split");
-    static_assert(MI == 32 || BN >= 64, "the B flip needs 64-float rows");
+    static_assert(MI == 32 || BN >= 32, "the B flip needs 32-float rows");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
-    static __device__ __forceinline__ int swz(int r) { return (r / RPB) % QPR; }
+    static __device__ __forceinline__ int swz(int r) { return SWIZZLE ? (r / RPB) % QPR : 0; }
     // Physical quad of logical quad nq in B row k is nq ^ flip(k).
     static __device__ __forceinline__ int flip(int k) { return ((k / KPL) & 1) * BFLIP; }
 };

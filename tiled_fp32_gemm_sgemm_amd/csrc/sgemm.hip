@@ -38,6 +38,8 @@ using Dl256x256k32m32 = DlTile<256, 256, 32, 2, 4, 32, 2, 8>;      // 8 waves of
 using Dl256x256k16m32 = DlTile<256, 256, 16, 2, 4, 32, 2, 8>;      // 8 waves of 128x64
 using Dl256x128k32m32 = DlTile<256, 128, 32, 2, 2, 32, 1, 8>;      // 4 waves of 128x64
 using Dl128x128k32m32 = DlTile<128, 128, 32, 2, 2, 32, 2, 8>;      // 4 waves of 64x64
+// Control build: A stored unswizzled (bank conflicts on purpose); never chosen.
+using Dl256x256k32m32Plain = DlTile<256, 256, 32, 2, 4, 32, 2, 8, false>;
 
 struct ConfigEntry {
     const char* name;
@@ -67,6 +69,7 @@ const ConfigEntry kConfigs[] = {
     SGEMM_DL_CFG(Dl256x256k16m32, "dl32_256x256x16_w2x4", 1.02, 1),
     SGEMM_DL_CFG(Dl256x128k32m32, "dl32_256x128x32_w2x2", 0.96, 1),
     SGEMM_DL_CFG(Dl128x128k32m32, "dl32_128x128x32_w2x2", 0.92, 2),
+    SGEMM_DL_CFG(Dl256x256k32m32Plain, "dl32_256x256x32_w2x4_unswizzled", 0.0, 1),
 };
 #undef SGEMM_CFG
 #undef SGEMM_DL_CFG
@@ -120,12 +123,14 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Shape -> configuration.  Score = useful fraction of the padded tiles x how
 // evenly the tiles fill the CUs' resident slots x a per-tile efficiency.
+// Control builds (efficiency 0) are never chosen.
 int choose_config(int64_t M, int64_t N, int64_t K, int64_t batch) {
     (void)K;
     int best = 0;
     double best_score = -1.0;
     for (int idx = 0; idx < kNumConfigs; ++idx) {
         const ConfigEntry& c = kConfigs[idx];
+        if (c.tile_efficiency <= 0.0) continue;
         const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn) * batch;
         const double useful = (double)M * N * batch / ((double)tiles * c.bm * c.bn);
         const int64_t slots = (int64_t)kNumCu * c.blocks_per_cu;
