@@ -76,7 +76,7 @@ _rng = random.Random(1234)
 RAGGED = [(1, 1, 1), (2, 2, 1), (1, 300, 7), (300, 1, 5), (33, 65, 17), (64, 64, 16),
           (65, 63, 15), (127, 129, 31), (128, 128, 16), (255, 257, 33), (256, 128, 16),
           (257, 129, 300), (100, 200, 3), (3, 5, 299), (31, 47, 64), (200, 280, 250),
-          (513, 260, 18)]
+          (513, 260, 18), (200, 192, 1000), (130, 260, 515)]
 RAGGED = [(M, N, K, K + _rng.randint(0, 3), N + _rng.randint(0, 5), N + _rng.randint(0, 7))
           for (M, N, K) in RAGGED]
 
@@ -87,7 +87,7 @@ def _call(path, *args, **kw):
     return run_gpu(*args, path=path, **kw)
 
 
-ALL_PATHS = ["valu"] + ["cfg%d" % i for i in range(15)]
+ALL_PATHS = ["valu"] + ["cfg%d" % i for i in range(19)]
 
 
 @pytest.mark.parametrize("path", ALL_PATHS)
@@ -179,7 +179,8 @@ def test_invalid_arguments_enqueue_nothing():
 
 # ------------------------------------------------------------------ batched
 
-@pytest.mark.parametrize("path", ["mfma", "valu", "cfg1", "cfg2", "cfg5", "cfg6", "cfg7", "cfg11", "cfg13"])
+@pytest.mark.parametrize("path", ["mfma", "valu", "cfg1", "cfg2", "cfg5", "cfg6", "cfg7", "cfg11", "cfg13",
+                                  "cfg15", "cfg16", "cfg17"])
 def test_batched_ragged_members_differ(path):
     M, N, K, lda, ldb, ldc, batch = 45, 77, 33, 36, 80, 79, 6
     sA, sB, sC = M * lda + 5, K * ldb + 3, M * ldc + 11

@@ -57,13 +57,14 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MI_, int OCC_, int GROUP_M_,
-          bool SWIZZLE_ = true>
+          int STAGES_ = 2, bool SWIZZLE_ = true>
 struct DlTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
     static constexpr int MI = MI_;
     static constexpr int OCC = OCC_;
     static constexpr int GROUP_M = GROUP_M_;
+    static constexpr int STAGES = STAGES_;               // LDS slice buffers in flight
     static constexpr bool SWIZZLE = SWIZZLE_;
     static constexpr int NW = WAVES_M * WAVES_N;         // waves per workgroup
     static constexpr int NT = 64 * NW;
@@ -89,14 +90,16 @@ struct DlTile {
     // Register-staged fallback: quads per thread per slice.
     static constexpr int A_VEC = BM * QPR / NT;
     static constexpr int B_VEC = BK * B_QPR / NT;
-    static constexpr int LDS_BYTES = 2 * BUF_FLOATS * 4;
+    static constexpr int LDS_BYTES = STAGES * BUF_FLOATS * 4;
+    static constexpr int LPS = A_CHW + B_CHW;            // copy instructions per wave per slice
 
     static_assert(MI == 16 || MI == 32, "MFMA tile edge");
     static_assert(BK == 16 || BK == 32, "BK must be 16 or 32");
     static_assert(KPL % KG == 0 && NKG % 2 == 0, "whole, even number of A operand groups");
     static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must be MFMA tile multiples");
     static_assert(A_CH % NW == 0 && B_CH % NW == 0, "slice chunks must split over the waves");
-    static_assert(BN % 64 == 0 && B_QPR % 16 == 0, "B rows must span whole bank rows");
+    static_assert(BN % 32 == 0, "B rows must start on the same ds_read_b32 bank");
+    static_assert(STAGES >= 2 && LPS * (STAGES - 2) <= 63, "vmcnt holds at most 63");
     static_assert((BM * QPR) % NT == 0 && (BK * B_QPR) % NT == 0, "fallback copy must split");
     static_assert(MI == 32 || BN >= 32, "the B flip needs 32-float rows");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -106,13 +109,53 @@ struct DlTile {
     static __device__ __forceinline__ int flip(int k) { return ((k / KPL) & 1) * BFLIP; }
 };
 
+// Waits until at most N vector-memory operations of this wave are still
+// outstanding; the export and LDS counters are left alone.  (s_waitcnt
+// immediate: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Waits until at most LPS * min(d, MAXD) operations are outstanding: the
+// copies of the d slices issued after the one that must have landed.
+template <int LPS, int MAXD>
+__device__ __forceinline__ void wait_slices_after(int d) {
+    if constexpr (MAXD == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (d >= MAXD)
+            wait_vmcnt<LPS * MAXD>();
+        else
+            wait_slices_after<LPS, MAXD - 1>(d);
+    }
+}
+
+// Workgroup barrier that leaves the direct copies of later slices in flight.
+// __syncthreads() (and any release fence that covers LDS) waits for every
+// outstanding vector-memory operation of the wave, because the direct copies
+// count as pending LDS writes; here the caller waits for the copies it needs
+// with wait_vmcnt, this waits for the wave's own LDS accesses (lgkmcnt 0).
+// The empty asm statements with a memory clobber keep the compiler from
+// moving memory accesses across (they emit nothing), and the scheduling
+// barriers keep the machine scheduler from moving any instruction across.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((15 << 0) | (3 << 14) | (7 << 4) | (0 << 8));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+}
+
 // The kernel body lives in a device function: it uses device-only builtins
 // and types, and keeping them out of the __global__ function's own body lets
 // the host compilation pass emit the launch stub.
 template <class T>
 __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     using Op = MfmaOp<T::MI>;
-    __shared__ __attribute__((aligned(16))) float smem[2 * T::BUF_FLOATS];
+    __shared__ __attribute__((aligned(16))) float smem[T::STAGES * T::BUF_FLOATS];
 
     const TileCoord tc = map_block(p, T::GROUP_M);
     const int m0 = tc.tm * T::BM;
@@ -214,12 +257,21 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     const int full_slices = p.K / T::BK;
 
     make_offsets(T::BK);
-    auto load_slice = [&](int s, int buf) {
+    auto load_slice = [&](int s) {
         const int k0 = s * T::BK;
+        const int buf = s % T::STAGES;
         if (direct_ok && s < full_slices)
             load_direct(k0, buf);
         else
             load_staged(k0, buf);
+    };
+    // Slice t has landed in this wave's part of LDS once only the direct
+    // copies of later slices (issued up to slice `last`) are outstanding; a
+    // register-staged slice is complete when load_staged returns.
+    auto wait_slice = [&](int t, int last) {
+        const int direct_last = (direct_ok ? full_slices : 0) - 1;
+        const int d = (last < direct_last ? last : direct_last) - t;
+        wait_slices_after<T::LPS, T::STAGES - 2>(d);
     };
 
     // --------------------------------------------------------------- compute
@@ -277,13 +329,19 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     float opb[2][T::TN][T::KG];
 
     // One slice held in LDS buffer `buf` (operand group g uses set g & 1):
-    // the next slice's copy is started first and is complete at the barrier;
-    // the last HOLD k steps of MFMAs run after the barrier, behind the reads of
-    // the next slice's first operand group, so the matrix core keeps working
-    // while the waves synchronise.
-    auto slice = [&](int buf, int s) {
-        const bool more = s + 1 < nslices;
-        if (more) load_slice(s + 1, buf ^ 1);
+    // the copy of slice s + STAGES - 1 is started first, into the buffer that
+    // slice s - 1 used (every wave finished reading it before the previous
+    // barrier); slice s + 1 is complete at this slice's barrier.  The last
+    // HOLD k steps of MFMAs run after the barrier, behind the reads of the next
+    // slice's first operand group, so the matrix core keeps working while the
+    // waves synchronise.
+    // `more` is a compile-time flag: the last slice is peeled off the loop so
+    // that no control-flow join sits in front of the held MFMAs (at a join the
+    // compiler's LDS wait would also cover the next slice's fresh reads).
+    auto slice = [&](auto more_tag, int buf, int s) {
+        constexpr bool more = decltype(more_tag)::value;
+        const int ahead = s + T::STAGES - 1;
+        if (more && ahead < nslices) load_slice(ahead);
 #pragma unroll
         for (int g = 0; g < T::NKG; ++g) {
             if (g + 1 < T::NKG) {
@@ -300,12 +358,12 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
                 mfma_steps(opa[0], opb[0], 0, s1);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (more) {
+        if constexpr (more) {
             // The direct copies count on vmcnt: wait for this wave's, then the
             // barrier makes every wave's part of the slice visible.
-            __builtin_amdgcn_s_waitcnt(0);
-            __syncthreads();
-            read_group(buf ^ 1, 0, opa[0], opb[0]);
+            wait_slice(s + 1, ahead < nslices ? ahead : nslices - 1);
+            lds_barrier();
+            read_group((s + 1) % T::STAGES, 0, opa[0], opb[0]);
         }
         __builtin_amdgcn_sched_barrier(0);
         // The last group, NKG-1, is odd: operand set 1.
@@ -313,11 +371,14 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    load_slice(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < T::STAGES - 1; ++t)
+        if (t < nslices) load_slice(t);
+    wait_slice(0, (T::STAGES - 1 < nslices ? T::STAGES - 1 : nslices) - 1);
+    lds_barrier();
     read_group(0, 0, opa[0], opb[0]);
-    for (int s = 0; s < nslices; ++s) slice(s & 1, s);
+    for (int s = 0; s + 1 < nslices; ++s) slice(std::true_type(), s % T::STAGES, s);
+    slice(std::false_type(), (nslices - 1) % T::STAGES, nslices - 1);
 
     // Epilogue: accumulator r of lane (li, lg) in MFMA tile (mi, ni) is row
     // Op::row(r, lg) and column li of that tile.

@@ -38,8 +38,13 @@ using Dl256x256k32m32 = DlTile<256, 256, 32, 2, 4, 32, 2, 8>;      // 8 waves of
 using Dl256x256k16m32 = DlTile<256, 256, 16, 2, 4, 32, 2, 8>;      // 8 waves of 128x64
 using Dl256x128k32m32 = DlTile<256, 128, 32, 2, 2, 32, 1, 8>;      // 4 waves of 128x64
 using Dl128x128k32m32 = DlTile<128, 128, 32, 2, 2, 32, 2, 8>;      // 4 waves of 64x64
+// Deeper pipelines and widths that divide ragged shapes into whole CU rounds.
+using Dl128x128k32m32s4 = DlTile<128, 128, 32, 2, 2, 32, 1, 8, 4>;  // 4 waves of 64x64
+using Dl64x64k32m32s4 = DlTile<64, 64, 32, 2, 2, 32, 2, 8, 4>;      // 4 waves of 32x32
+using Dl256x192k32m32 = DlTile<256, 192, 32, 4, 2, 32, 2, 8>;      // 8 waves of 64x96
+using Dl192x256k32m32 = DlTile<192, 256, 32, 2, 4, 32, 2, 8>;      // 8 waves of 96x64
 // Control build: A stored unswizzled (bank conflicts on purpose); never chosen.
-using Dl256x256k32m32Plain = DlTile<256, 256, 32, 2, 4, 32, 2, 8, false>;
+using Dl256x256k32m32Plain = DlTile<256, 256, 32, 2, 4, 32, 2, 8, 2, false>;
 
 struct ConfigEntry {
     const char* name;
@@ -70,6 +75,10 @@ const ConfigEntry kConfigs[] = {
     SGEMM_DL_CFG(Dl256x128k32m32, "dl32_256x128x32_w2x2", 0.96, 1),
     SGEMM_DL_CFG(Dl128x128k32m32, "dl32_128x128x32_w2x2", 0.92, 2),
     SGEMM_DL_CFG(Dl256x256k32m32Plain, "dl32_256x256x32_w2x4_unswizzled", 0.0, 1),
+    SGEMM_DL_CFG(Dl128x128k32m32s4, "dl32_128x128x32_w2x2_s4", 0.92, 1),
+    SGEMM_DL_CFG(Dl64x64k32m32s4, "dl32_64x64x32_w2x2_s4", 0.60, 2),
+    SGEMM_DL_CFG(Dl256x192k32m32, "dl32_256x192x32_w4x2", 1.00, 1),
+    SGEMM_DL_CFG(Dl192x256k32m32, "dl32_192x256x32_w2x4", 1.00, 1),
 };
 #undef SGEMM_CFG
 #undef SGEMM_DL_CFG
