@@ -121,10 +121,45 @@ int sgemm_config_info(int config, char *buf, int64_t len, int *bm, int *bn, int 
                       int *threads);
 
 /*
- * The configuration sgemm / sgemm_strided_batched would use for this shape.
- * Host only; touches no device.  Returns a negative status for bad sizes.
+ * The configuration sgemm / sgemm_strided_batched would use for this shape:
+ * the one with the smallest predicted time (sgemm_config_predict_us).  Host
+ * only; touches no device.  Returns a negative status for bad sizes.
  */
 int sgemm_select_config(int64_t M, int64_t N, int64_t K, int64_t batch);
+
+/*
+ * 1 if the automatic choice may pick configuration `config`, 0 if it is a
+ * control build kept for measurements only, SGEMM_STATUS_INVALID_CONFIG for
+ * an unknown index.  Host only.
+ */
+int sgemm_config_selectable(int config);
+
+/*
+ * Predicted microseconds of one launch of configuration `config` on this
+ * shape, from a per-configuration time model fitted to measurements (the
+ * tile-size trade-off of "Tiling Strategies" section 4, in numbers): whole
+ * rounds of 256 (or, where two workgroups fit on a CU, 512) tiles, each
+ * costing BM*BN*(a + b*K).  A negative value is a status code (unknown or
+ * control configuration, bad sizes).  Host only.
+ */
+double sgemm_config_predict_us(int config, int64_t M, int64_t N, int64_t K, int64_t batch);
+
+/*
+ * Measure instead of predicting: times every selectable configuration on the
+ * caller's operands (one warm-up launch, then `reps` launches between two
+ * events on `stream`), stores the fastest in *best_config and its mean
+ * milliseconds per launch in *best_ms (if not NULL), and finally runs the
+ * fastest once more, so that C holds A x B on return.  Arguments are checked
+ * as for sgemm_strided_batched (plus best_config != NULL and reps >= 1);
+ * empty products and K = 0 return the automatic choice without timing.  This
+ * call blocks the host until the timed work on `stream` is done and creates
+ * two HIP events; it allocates no device memory.  Returns 0 or a negative
+ * status (the first failing launch's).
+ */
+int sgemm_autotune(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                   int64_t strideA, const float *B, int64_t ldb, int64_t strideB, float *C,
+                   int64_t ldc, int64_t strideC, int64_t batch, hipStream_t stream, int reps,
+                   int *best_config, float *best_ms);
 
 /* Static text for a status code (never NULL). */
 const char *sgemm_status_string(int status);

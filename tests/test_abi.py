@@ -86,6 +86,44 @@ def test_select_config_host_logic():
     assert _native.lib().sgemm_select_config(-1, 1, 1, 1) == -1
 
 
+def test_selection_is_the_smallest_predicted_time():
+    n = sg.num_configs()
+    selectable = [c for c in range(n) if sg.config_selectable(c)]
+    assert 0 < len(selectable) < n  # the control build is listed but never chosen
+    for c in range(n):
+        if not sg.config_selectable(c):
+            assert _native.lib().sgemm_config_predict_us(c, 64, 64, 64, 1) == -7
+    for shape in [(4096, 4096, 4096, 1), (1024, 1024, 1024, 1), (4000, 3000, 4100, 1),
+                  (16384, 4096, 4096, 1), (128, 128, 128, 1024), (512, 4096, 4096, 1),
+                  (7, 9, 11, 3), (100000, 64, 64, 1)]:
+        pred = {c: sg.predict_us(c, *shape) for c in selectable}
+        assert all(t > 0 for t in pred.values())
+        chosen = sg.select_config(*shape)
+        assert pred[chosen] == min(pred.values())
+
+
+def test_predicted_time_grows_with_the_work():
+    for c in range(sg.num_configs()):
+        if not sg.config_selectable(c):
+            continue
+        t = [sg.predict_us(c, 4096, 4096, k) for k in (256, 1024, 4096)]
+        assert t[0] < t[1] < t[2]
+        assert sg.predict_us(c, 8192, 4096, 4096) >= t[2]
+
+
+def test_autotune_argument_errors():
+    lib = _native.lib()
+    best = ctypes.c_int(-1)
+    args = (4, 4, 4, FAKE, 4, 0, FAKE, 4, 0, FAKE, 4, 0, 1, 0)
+    assert lib.sgemm_autotune(*args, 0, ctypes.byref(best), None) == -1      # reps < 1
+    assert lib.sgemm_autotune(*args, 1, None, None) == -3                    # no result slot
+    assert lib.sgemm_autotune(4, 4, 4, FAKE, 3, 0, FAKE, 4, 0, FAKE, 4, 0, 1, 0, 1,
+                              ctypes.byref(best), None) == -2                # lda < K
+    # empty product: the automatic choice, nothing timed or launched
+    assert lib.sgemm_autotune(0, 4, 4, None, 4, 0, None, 4, 0, None, 4, 0, 1, 0, 1,
+                              ctypes.byref(best), None) == 0
+
+
 def test_status_strings():
     for code in list(_native.STATUS) + [12345]:
         s = sg.status_string(code)

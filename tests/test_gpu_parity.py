@@ -87,7 +87,7 @@ def _call(path, *args, **kw):
     return run_gpu(*args, path=path, **kw)
 
 
-ALL_PATHS = ["valu"] + ["cfg%d" % i for i in range(19)]
+ALL_PATHS = ["valu"] + ["cfg%d" % i for i in range(26)]
 
 
 @pytest.mark.parametrize("path", ALL_PATHS)
@@ -180,7 +180,7 @@ def test_invalid_arguments_enqueue_nothing():
 # ------------------------------------------------------------------ batched
 
 @pytest.mark.parametrize("path", ["mfma", "valu", "cfg1", "cfg2", "cfg5", "cfg6", "cfg7", "cfg11", "cfg13",
-                                  "cfg15", "cfg16", "cfg17"])
+                                  "cfg15", "cfg16", "cfg17", "cfg23", "cfg25"])
 def test_batched_ragged_members_differ(path):
     M, N, K, lda, ldb, ldc, batch = 45, 77, 33, 36, 80, 79, 6
     sA, sB, sC = M * lda + 5, K * ldb + 3, M * ldc + 11
@@ -300,6 +300,13 @@ def test_tall_workload_sampled():
     _check_sampled(w, C, A, B)
 
 
+def test_shard512_workload_sampled():
+    w = WORKLOADS["shard512"]
+    A, B = workload_operands(w)
+    C = run_gpu(w.M, w.N, w.K, A, w.lda, B, w.ldb, w.ldc)[0]
+    _check_sampled(w, C, A, B)
+
+
 @pytest.mark.parametrize("path", ["mfma", "valu"])
 def test_batched128_full(path):
     w = WORKLOADS["batched128"]
@@ -310,3 +317,37 @@ def test_batched128_full(path):
                                                 B.numpy(), w.ldb, w.strideB, w.batch)
     ratio = parity.assert_within_tolerance(C, ref, mag, w.name)
     print("batched128 %s: max ratio %.3e" % (path, ratio))
+
+
+# ---------------------------------------------------------------- autotuner
+@pytest.mark.parametrize("shape", [(300, 260, 150, 151, 262, 263), (64, 64, 1024, 1024, 64, 64)],
+                         ids=lambda s: "x".join(map(str, s[:3])))
+def test_autotune_leaves_the_product_in_c(shape):
+    M, N, K, lda, ldb, ldc = shape
+    A_cpu, B_cpu = operands(M, N, K, lda, ldb, seed=M + 3 * K, dist_a="int4")
+    dev = _dev()
+    A, B = A_cpu.to(dev), B_cpu.to(dev)
+    C = torch.full((M * ldc + GUARD,), SENTINEL, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st, cfg, ms = sg.autotune_raw(M, N, K, A.data_ptr(), lda, 0, B.data_ptr(), ldb, 0,
+                                  C.data_ptr(), ldc, 0, 1, stream, reps=2)
+    assert st == 0, sg.status_string(st)
+    assert sg.config_selectable(cfg) and ms > 0
+    torch.cuda.synchronize()
+    Ch = C.cpu().numpy()
+    got = Ch[np.arange(M)[:, None] * ldc + np.arange(N)[None, :]]
+    ref, _ = oracle_full(M, N, K, A_cpu, lda, B_cpu, ldb)
+    parity.assert_bitwise(got, ref, "autotune %s" % (shape,))
+    assert np.all(Ch[M * ldc:] == SENTINEL)
+
+
+def test_autotune_tensor_api_batched():
+    A_cpu, B_cpu = operands(96, 80, 40, 40, 80, seed=5, dist_a="int4")
+    dev = _dev()
+    A = torch.stack([A_cpu[: 96 * 40].view(96, 40)] * 3).to(dev) + \
+        torch.arange(3, dtype=torch.float32, device=dev).view(3, 1, 1)
+    B = torch.stack([B_cpu[: 40 * 80].view(40, 80)] * 3).to(dev)
+    cfg, ms, out = sg.autotune(A, B, reps=1)
+    assert sg.config_selectable(cfg)
+    ref = torch.bmm(A.double().cpu(), B.double().cpu())
+    assert torch.equal(out.cpu().double(), ref)

@@ -4,9 +4,11 @@ The product runs in libsgemm.so (hand-written HIP kernels behind the C ABI
 in include/sgemm.h); this package only passes tensors' device addresses,
 leading dimensions and the current stream to it.
 """
-from .api import (config_info, num_configs, select_config, sgemm, sgemm_raw,
-                  sgemm_strided_batched, sgemm_strided_batched_raw)
+from .api import (autotune, autotune_raw, config_info, config_selectable, num_configs,
+                  predict_us, select_config, sgemm, sgemm_raw, sgemm_strided_batched,
+                  sgemm_strided_batched_raw)
 from ._native import SgemmError, status_string
 
 __all__ = ["sgemm", "sgemm_strided_batched", "sgemm_raw", "sgemm_strided_batched_raw",
-           "num_configs", "config_info", "select_config", "SgemmError", "status_string"]
+           "num_configs", "config_info", "select_config", "config_selectable", "predict_us",
+           "autotune", "autotune_raw", "SgemmError", "status_string"]

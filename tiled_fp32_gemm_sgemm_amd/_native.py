@@ -53,6 +53,12 @@ _SIGS = {
                            ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
                            ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
     "sgemm_select_config": ([_i64, _i64, _i64, _i64], ctypes.c_int),
+    "sgemm_config_selectable": ([ctypes.c_int], ctypes.c_int),
+    "sgemm_config_predict_us": ([ctypes.c_int, _i64, _i64, _i64, _i64], ctypes.c_double),
+    "sgemm_autotune": (
+        [_i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64, _p,
+         ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float)],
+        ctypes.c_int),
     "sgemm_status_string": ([ctypes.c_int], ctypes.c_char_p),
 }
 

@@ -134,3 +134,61 @@ def select_config(M: int, N: int, K: int, batch: int = 1) -> int:
     if st < 0:
         raise _native.SgemmError(st, "sgemm_select_config")
     return st
+
+
+def config_selectable(config: int) -> bool:
+    st = _native.lib().sgemm_config_selectable(int(config))
+    if st < 0:
+        raise _native.SgemmError(st, "sgemm_config_selectable")
+    return bool(st)
+
+
+def predict_us(config: int, M: int, N: int, K: int, batch: int = 1) -> float:
+    """Predicted microseconds of one launch of `config` on this shape."""
+    t = _native.lib().sgemm_config_predict_us(int(config), M, N, K, batch)
+    if t < 0:
+        raise _native.SgemmError(int(t), "sgemm_config_predict_us")
+    return t
+
+
+def autotune_raw(M, N, K, A_ptr, lda, strideA, B_ptr, ldb, strideB, C_ptr, ldc, strideC, batch,
+                 stream=0, reps=10):
+    """(status, best config, best milliseconds per launch); C holds A x B."""
+    best = ctypes.c_int(-1)
+    ms = ctypes.c_float(0.0)
+    st = _native.lib().sgemm_autotune(M, N, K, A_ptr, lda, strideA, B_ptr, ldb, strideB, C_ptr,
+                                      ldc, strideC, batch, stream, int(reps), ctypes.byref(best),
+                                      ctypes.byref(ms))
+    return st, best.value, ms.value
+
+
+def autotune(A, B, out=None, reps: int = 10, stream=None):
+    """Time every selectable configuration on these operands (2-D: one
+    product; 3-D: a strided batch) and return (config, ms per launch, out)."""
+    import torch
+    batched = A.dim() == 3
+    _operand(A, "A", 3 if batched else 2)
+    _operand(B, "B", 3 if batched else 2)
+    if batched:
+        batch, M, K = A.shape
+        batch2, K2, N = B.shape
+    else:
+        (M, K), (K2, N) = A.shape, B.shape
+        batch = batch2 = 1
+    if K != K2 or batch != batch2:
+        raise ValueError("shapes differ: %s vs %s" % (tuple(A.shape), tuple(B.shape)))
+    shape = (batch, M, N) if batched else (M, N)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=A.device)
+    _operand(out, "out", 3 if batched else 2)
+    if tuple(out.shape) != shape:
+        raise ValueError("out must have shape %s" % (shape,))
+    sa = int(A.stride(0)) if batched else 0
+    sb = int(B.stride(0)) if batched else 0
+    sc = int(out.stride(0)) if batched else 0
+    with torch.cuda.device(A.device):
+        st, cfg, ms = autotune_raw(M, N, K, A.data_ptr(), _ld(A), sa, B.data_ptr(), _ld(B), sb,
+                                   out.data_ptr(), _ld(out), sc, batch,
+                                   _stream_handle(stream, A.device), reps)
+    _check(st, "sgemm_autotune")
+    return cfg, ms, out

@@ -57,7 +57,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MI_, int OCC_, int GROUP_M_,
-          int STAGES_ = 2, bool SWIZZLE_ = true>
+          int STAGES_ = 2, int KSPLIT_ = 1, bool SWIZZLE_ = true>
 struct DlTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -65,13 +65,16 @@ struct DlTile {
     static constexpr int OCC = OCC_;
     static constexpr int GROUP_M = GROUP_M_;
     static constexpr int STAGES = STAGES_;               // LDS slice buffers in flight
+    static constexpr int KSPLIT = KSPLIT_;               // wave groups splitting each slice's k
     static constexpr bool SWIZZLE = SWIZZLE_;
-    static constexpr int NW = WAVES_M * WAVES_N;         // waves per workgroup
+    static constexpr int NWMN = WAVES_M * WAVES_N;       // waves per k group
+    static constexpr int NW = NWMN * KSPLIT;             // waves per workgroup
     static constexpr int NT = 64 * NW;
+    static constexpr int KSUB = BK / KSPLIT;             // k values of a slice per k group
     static constexpr int WTM = BM / WAVES_M, WTN = BN / WAVES_N;
     static constexpr int TM = WTM / MI, TN = WTN / MI;
     static constexpr int LG = 64 / MI;
-    static constexpr int KPL = BK / LG;
+    static constexpr int KPL = KSUB / LG;
     static constexpr int QPR = BK / 4;                   // quads per A row
     static constexpr int B_QPR = BN / 4;                 // quads per B row
     static constexpr int LDB = BN;
@@ -94,7 +97,7 @@ struct DlTile {
     static constexpr int LPS = A_CHW + B_CHW;            // copy instructions per wave per slice
 
     static_assert(MI == 16 || MI == 32, "MFMA tile edge");
-    static_assert(BK == 16 || BK == 32, "BK must be 16 or 32");
+    static_assert(BK == 16 || BK == 32 || BK == 64, "BK must be 16, 32 or 64");
     static_assert(KPL % KG == 0 && NKG % 2 == 0, "whole, even number of A operand groups");
     static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must be MFMA tile multiples");
     static_assert(A_CH % NW == 0 && B_CH % NW == 0, "slice chunks must split over the waves");
@@ -103,6 +106,7 @@ struct DlTile {
     static_assert((BM * QPR) % NT == 0 && (BK * B_QPR) % NT == 0, "fallback copy must split");
     static_assert(MI == 32 || BN >= 32, "the B flip needs 32-float rows");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert((KSPLIT - 1) * BM * BN <= STAGES * BUF_FLOATS, "k-group exchange fits in LDS");
 
     static __device__ __forceinline__ int swz(int r) { return SWIZZLE ? (r / RPB) % QPR : 0; }
     // Physical quad of logical quad nq in B row k is nq ^ flip(k).
@@ -275,8 +279,10 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     };
 
     // --------------------------------------------------------------- compute
-    const int wy = wave / T::WAVES_N;
-    const int wx = wave % T::WAVES_N;
+    const int wave_mn = wave % T::NWMN;
+    const int kgrp = wave / T::NWMN;  // which KSUB-wide part of every slice this wave reduces
+    const int wy = wave_mn / T::WAVES_N;
+    const int wx = wave_mn % T::WAVES_N;
     const int li = lane % T::MI;
     const int lg = lane / T::MI;
 
@@ -295,7 +301,7 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     int b_col[T::TN];
 #pragma unroll
     for (int ni = 0; ni < T::TN; ++ni)
-        b_col[ni] = (wx * T::WTN + T::MI * ni + li) ^ (4 * T::flip(lg * T::KPL));
+        b_col[ni] = (wx * T::WTN + T::MI * ni + li) ^ (4 * T::flip(kgrp * T::KSUB + lg * T::KPL));
 
     // One operand group = KG consecutive k steps: one 16-byte quad of A per
     // row tile and KG values of B per column tile.  The operands of group g+1
@@ -303,8 +309,9 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     // GPUs", "Register prefetching").
     auto read_group = [&](int buf, int g, f32x4 (&a)[T::TM], float (&b)[T::TN][T::KG]) {
         const float* const As = smem + buf * T::BUF_FLOATS;
-        const float* const Bl = As + T::A_FLOATS + (lg * T::KPL + g * T::KG) * T::LDB;
-        const int quad = lg * (T::KPL / 4) + g;
+        const float* const Bl =
+            As + T::A_FLOATS + (kgrp * T::KSUB + lg * T::KPL + g * T::KG) * T::LDB;
+        const int quad = kgrp * (T::KSUB / 4) + lg * (T::KPL / 4) + g;
 #pragma unroll
         for (int mi = 0; mi < T::TM; ++mi)
             a[mi] = *(const f32x4*)(As + (a_row + T::MI * mi) * T::BK + ((quad ^ a_swz) << 2));
@@ -379,6 +386,43 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     read_group(0, 0, opa[0], opb[0]);
     for (int s = 0; s + 1 < nslices; ++s) slice(std::true_type(), s % T::STAGES, s);
     slice(std::false_type(), (nslices - 1) % T::STAGES, nslices - 1);
+
+    // k groups 1..KSPLIT-1 hand their partial sums to group 0 through LDS
+    // (lane-contiguous 16-byte records, conflict-free); group 0 adds them in
+    // group order, so the result does not depend on timing.
+    if constexpr (T::KSPLIT > 1) {
+        constexpr int NACC = T::TM * T::TN * Op::ACC;
+        static_assert(NACC % 4 == 0, "whole 16-byte records");
+        lds_barrier();  // every wave is done reading the slices
+        if (kgrp > 0) {
+            float* const dst = smem + ((kgrp - 1) * T::NWMN + wave_mn) * 64 * NACC;
+#pragma unroll
+            for (int q = 0; q < NACC / 4; ++q) {
+                f32x4 v;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int f = 4 * q + c;
+                    v[c] = acc[f / (T::TN * Op::ACC)][(f / Op::ACC) % T::TN][f % Op::ACC];
+                }
+                *(f32x4*)(dst + 4 * (q * 64 + lane)) = v;
+            }
+        }
+        lds_barrier();
+        if (kgrp > 0) return;
+#pragma unroll 1
+        for (int j = 1; j < T::KSPLIT; ++j) {
+            const float* const src = smem + ((j - 1) * T::NWMN + wave_mn) * 64 * NACC;
+#pragma unroll
+            for (int q = 0; q < NACC / 4; ++q) {
+                const f32x4 v = *(const f32x4*)(src + 4 * (q * 64 + lane));
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int f = 4 * q + c;
+                    acc[f / (T::TN * Op::ACC)][(f / Op::ACC) % T::TN][f % Op::ACC] += v[c];
+                }
+            }
+        }
+    }
 
     // Epilogue: accumulator r of lane (li, lg) in MFMA tile (mi, ni) is row
     // Op::row(r, lg) and column li of that tile.

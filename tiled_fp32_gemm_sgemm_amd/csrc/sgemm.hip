@@ -10,6 +10,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <cmath>
+
 #include "mfma_dl_kernel.hpp"
 #include "mfma_kernel.hpp"
 #include "tile_common.hpp"
@@ -43,42 +45,64 @@ using Dl128x128k32m32s4 = DlTile<128, 128, 32, 2, 2, 32, 1, 8, 4>;  // 4 waves o
 using Dl64x64k32m32s4 = DlTile<64, 64, 32, 2, 2, 32, 2, 8, 4>;      // 4 waves of 32x32
 using Dl256x192k32m32 = DlTile<256, 192, 32, 4, 2, 32, 2, 8>;      // 8 waves of 64x96
 using Dl192x256k32m32 = DlTile<192, 256, 32, 2, 4, 32, 2, 8>;      // 8 waves of 96x64
+using Dl64x64k64m32s4 = DlTile<64, 64, 64, 2, 2, 32, 1, 8, 4>;      // 4 waves of 32x32
+using Dl64x64k32m32s8 = DlTile<64, 64, 32, 2, 2, 32, 1, 8, 8>;      // 4 waves of 32x32
+using Dl128x64k32m32s4 = DlTile<128, 64, 32, 2, 2, 32, 1, 8, 4>;    // 4 waves of 64x32
+using Dl128x128k64m32s2 = DlTile<128, 128, 64, 2, 2, 32, 1, 8, 2>;  // 4 waves of 64x64
+// Two wave groups split every slice's k range (8 waves of 32x32, 2 per SIMD).
+using Dl64x64k64m32s4x2 = DlTile<64, 64, 64, 2, 2, 32, 2, 8, 4, 2>;
+using Dl64x64k32m32s4x2 = DlTile<64, 64, 32, 2, 2, 32, 2, 8, 4, 2>;
+using Dl128x64k64m32s2x2 = DlTile<128, 64, 64, 2, 2, 32, 2, 8, 2, 2>;  // 8 waves of 64x32
 // Control build: A stored unswizzled (bank conflicts on purpose); never chosen.
-using Dl256x256k32m32Plain = DlTile<256, 256, 32, 2, 4, 32, 2, 8, 2, false>;
+using Dl256x256k32m32Plain = DlTile<256, 256, 32, 2, 4, 32, 2, 8, 2, 1, false>;
 
 struct ConfigEntry {
     const char* name;
     int bm, bn, bk, threads;
     const void* kernel;
-    double tile_efficiency;  // relative per-CU throughput of a full tile (tuning input)
-    int blocks_per_cu;       // workgroups that fit on one CU at once
+    // Time model for the choice of a configuration, fitted to measurements on
+    // MI355X (python -m tiled_fp32_gemm_sgemm_amd.calibrate), per unit of tile
+    // area in microseconds: a round of 256 tiles (one workgroup per CU) takes
+    // BM*BN*(one_a + one_b*K); when two workgroups fit on a CU (per_cu = 2) a
+    // round of 512 tiles takes BM*BN*(two_a + two_b*K).  per_cu = 0 marks a
+    // control build that is never chosen.
+    int per_cu;
+    double one_a, one_b, two_a, two_b;
 };
 
-#define SGEMM_CFG(T, name, eff, per_cu) \
-    { name, T::BM, T::BN, T::BK, T::NT, (const void*)&sgemm_mfma_kernel<T>, eff, per_cu }
-#define SGEMM_DL_CFG(T, name, eff, per_cu) \
-    { name, T::BM, T::BN, T::BK, T::NT, (const void*)&sgemm_mfma_dl_kernel<T>, eff, per_cu }
+#define SGEMM_CFG(T, name, per_cu, a1, b1, a2, b2) \
+    { name, T::BM, T::BN, T::BK, T::NT, (const void*)&sgemm_mfma_kernel<T>, per_cu, a1, b1, a2, b2 }
+#define SGEMM_DL_CFG(T, name, per_cu, a1, b1, a2, b2)                                        \
+    { name, T::BM, T::BN, T::BK, T::NT, (const void*)&sgemm_mfma_dl_kernel<T>, per_cu, a1, b1, \
+      a2, b2 }
 
 const ConfigEntry kConfigs[] = {
-    SGEMM_CFG(Cfg256x128, "mfma32_256x128x16_w2x2", 0.94, 2),
-    SGEMM_CFG(Cfg128x128, "mfma32_128x128x16_w2x2", 0.90, 3),
-    SGEMM_CFG(Cfg64x64, "mfma32_64x64x16_w2x2", 0.60, 8),
-    SGEMM_CFG(Cfg256x256, "mfma32_256x256x16_w2x4", 0.96, 1),
-    SGEMM_CFG(Cfg256x256k32, "mfma32_256x256x32_w2x4", 1.00, 1),
-    SGEMM_CFG(Cfg128x128k32, "mfma32_128x128x32_w2x2", 0.90, 2),
-    SGEMM_CFG(Cfg128x128k32m16, "mfma16_128x128x32_w2x2", 0.90, 2),
-    SGEMM_CFG(Cfg64x64k32m16, "mfma16_64x64x32_w2x2", 0.60, 4),
-    SGEMM_CFG(Cfg256x256m32w1, "mfma32_256x256x16_w2x2", 0.98, 1),
-    SGEMM_CFG(Cfg256x256k32m32w1, "mfma32_256x256x32_w2x2", 0.98, 1),
-    SGEMM_DL_CFG(Dl256x256k32m32, "dl32_256x256x32_w2x4", 1.04, 1),
-    SGEMM_DL_CFG(Dl256x256k16m32, "dl32_256x256x16_w2x4", 1.02, 1),
-    SGEMM_DL_CFG(Dl256x128k32m32, "dl32_256x128x32_w2x2", 0.96, 1),
-    SGEMM_DL_CFG(Dl128x128k32m32, "dl32_128x128x32_w2x2", 0.92, 2),
-    SGEMM_DL_CFG(Dl256x256k32m32Plain, "dl32_256x256x32_w2x4_unswizzled", 0.0, 1),
-    SGEMM_DL_CFG(Dl128x128k32m32s4, "dl32_128x128x32_w2x2_s4", 0.92, 1),
-    SGEMM_DL_CFG(Dl64x64k32m32s4, "dl32_64x64x32_w2x2_s4", 0.60, 2),
-    SGEMM_DL_CFG(Dl256x192k32m32, "dl32_256x192x32_w4x2", 1.00, 1),
-    SGEMM_DL_CFG(Dl192x256k32m32, "dl32_192x256x32_w2x4", 1.00, 1),
+    SGEMM_CFG(Cfg256x128, "mfma32_256x128x16_w2x2", 1, 3.8386e-04, 4.2165e-06, 3.9847e-04, 8.1269e-06),
+    SGEMM_CFG(Cfg128x128, "mfma32_128x128x16_w2x2", 2, 4.3762e-04, 4.5313e-06, 4.8419e-04, 8.3435e-06),
+    SGEMM_CFG(Cfg64x64, "mfma32_64x64x16_w2x2", 2, 0.0000e+00, 9.0826e-06, 9.5395e-04, 9.8877e-06),
+    SGEMM_CFG(Cfg256x256, "mfma32_256x256x16_w2x4", 1, 1.9301e-04, 3.7992e-06, 3.4525e-04, 7.5872e-06),
+    SGEMM_CFG(Cfg256x256k32, "mfma32_256x256x32_w2x4", 1, 1.9927e-04, 3.7600e-06, 3.6440e-04, 7.5142e-06),
+    SGEMM_CFG(Cfg128x128k32, "mfma32_128x128x32_w2x2", 2, 3.9461e-04, 4.5436e-06, 5.7746e-04, 7.8146e-06),
+    SGEMM_CFG(Cfg128x128k32m16, "mfma16_128x128x32_w2x2", 2, 3.7491e-04, 4.7511e-06, 5.8424e-04, 8.1157e-06),
+    SGEMM_CFG(Cfg64x64k32m16, "mfma16_64x64x32_w2x2", 2, 6.9501e-04, 6.4427e-06, 1.0260e-03, 9.8135e-06),
+    SGEMM_CFG(Cfg256x256m32w1, "mfma32_256x256x16_w2x2", 1, 2.0224e-04, 3.9503e-06, 3.9565e-04, 7.8758e-06),
+    SGEMM_CFG(Cfg256x256k32m32w1, "mfma32_256x256x32_w2x2", 1, 2.2312e-04, 3.9043e-06, 4.1389e-04, 7.8000e-06),
+    SGEMM_DL_CFG(Dl256x256k32m32, "dl32_256x256x32_w2x4", 1, 2.1036e-04, 3.4720e-06, 3.7595e-04, 6.9415e-06),
+    SGEMM_DL_CFG(Dl256x256k16m32, "dl32_256x256x16_w2x4", 1, 2.0071e-04, 3.4849e-06, 3.6338e-04, 6.9601e-06),
+    SGEMM_DL_CFG(Dl256x128k32m32, "dl32_256x128x32_w2x2", 1, 3.5631e-04, 3.7684e-06, 5.3476e-04, 7.5500e-06),
+    SGEMM_DL_CFG(Dl128x128k32m32, "dl32_128x128x32_w2x2", 2, 4.3123e-04, 3.9272e-06, 5.4574e-04, 6.9695e-06),
+    SGEMM_DL_CFG(Dl256x256k32m32Plain, "dl32_256x256x32_w2x4_unswizzled", 0, 0, 0, 0, 0),
+    SGEMM_DL_CFG(Dl128x128k32m32s4, "dl32_128x128x32_w2x2_s4", 1, 4.5364e-04, 4.1307e-06, 6.7966e-04, 8.2867e-06),
+    SGEMM_DL_CFG(Dl64x64k32m32s4, "dl32_64x64x32_w2x2_s4", 2, 8.8462e-04, 5.0915e-06, 1.1556e-03, 7.6853e-06),
+    SGEMM_DL_CFG(Dl256x192k32m32, "dl32_256x192x32_w4x2", 1, 2.1452e-04, 3.5334e-06, 3.5426e-04, 7.0652e-06),
+    SGEMM_DL_CFG(Dl192x256k32m32, "dl32_192x256x32_w2x4", 1, 2.1940e-04, 3.4913e-06, 3.5898e-04, 6.9860e-06),
+    SGEMM_DL_CFG(Dl64x64k64m32s4, "dl32_64x64x64_w2x2_s4", 1, 9.1894e-04, 4.9619e-06, 1.4383e-03, 9.9365e-06),
+    SGEMM_DL_CFG(Dl64x64k32m32s8, "dl32_64x64x32_w2x2_s8", 1, 1.0063e-03, 5.0706e-06, 1.6064e-03, 1.0141e-05),
+    SGEMM_DL_CFG(Dl128x64k32m32s4, "dl32_128x64x32_w2x2_s4", 1, 6.1517e-04, 4.5946e-06, 9.0588e-04, 9.2191e-06),
+    SGEMM_DL_CFG(Dl128x128k64m32s2, "dl32_128x128x64_w2x2", 1, 4.9542e-04, 3.9598e-06, 7.7019e-04, 7.9307e-06),
+    SGEMM_DL_CFG(Dl64x64k64m32s4x2, "dl32_64x64x64_w2x2_s4_k2", 1, 1.0666e-03, 4.1455e-06, 1.7638e-03, 8.2600e-06),
+    SGEMM_DL_CFG(Dl64x64k32m32s4x2, "dl32_64x64x32_w2x2_s4_k2", 2, 9.7944e-04, 5.1438e-06, 1.4432e-03, 8.2780e-06),
+    SGEMM_DL_CFG(Dl128x64k64m32s2x2, "dl32_128x64x64_w2x2_s2_k2", 1, 6.7196e-04, 3.8131e-06, 1.0361e-03, 7.6395e-06),
 };
 #undef SGEMM_CFG
 #undef SGEMM_DL_CFG
@@ -130,24 +154,31 @@ int validate(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, int64
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Shape -> configuration.  Score = useful fraction of the padded tiles x how
-// evenly the tiles fill the CUs' resident slots x a per-tile efficiency.
-// Control builds (efficiency 0) are never chosen.
+// Predicted time of one launch: whole rounds of tiles at the fitted round
+// times; a last round of at most 256 tiles on a two-per-CU configuration runs
+// at the one-per-CU time.
+double predict_us(const ConfigEntry& c, int64_t M, int64_t N, int64_t K, int64_t batch) {
+    const double tiles = (double)(ceil_div(M, c.bm) * ceil_div(N, c.bn)) * (double)batch;
+    const double area = (double)c.bm * c.bn;
+    const double one = area * (c.one_a + c.one_b * (double)K);
+    const double two = area * (c.two_a + c.two_b * (double)K);
+    if (c.per_cu < 2) return std::ceil(tiles / kNumCu) * one;
+    const double full = std::floor(tiles / (2.0 * kNumCu));
+    const double rest = tiles - full * 2.0 * kNumCu;
+    return full * two + (rest == 0.0 ? 0.0 : rest <= kNumCu ? one : two);
+}
+
+// Shape -> configuration: the smallest predicted time; control builds are
+// never chosen.
 int choose_config(int64_t M, int64_t N, int64_t K, int64_t batch) {
-    (void)K;
-    int best = 0;
-    double best_score = -1.0;
+    int best = -1;
+    double best_us = 0.0;
     for (int idx = 0; idx < kNumConfigs; ++idx) {
         const ConfigEntry& c = kConfigs[idx];
-        if (c.tile_efficiency <= 0.0) continue;
-        const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn) * batch;
-        const double useful = (double)M * N * batch / ((double)tiles * c.bm * c.bn);
-        const int64_t slots = (int64_t)kNumCu * c.blocks_per_cu;
-        const int64_t rounds = ceil_div(tiles, slots);
-        const double fill = (double)tiles / (double)(rounds * slots);
-        const double score = useful * fill * c.tile_efficiency;
-        if (score > best_score + 1e-9) {
-            best_score = score;
+        if (c.per_cu == 0) continue;
+        const double t = predict_us(c, M, N, K, batch);
+        if (best < 0 || t < best_us * (1.0 - 1e-9)) {
+            best_us = t;
             best = idx;
         }
     }
@@ -286,6 +317,74 @@ int sgemm_select_config(int64_t M, int64_t N, int64_t K, int64_t batch) {
         return SGEMM_STATUS_SIZE_OVERFLOW;
     if (M == 0 || N == 0 || batch == 0) return 0;
     return choose_config(M, N, K, batch);
+}
+
+int sgemm_config_selectable(int config) {
+    if (config < 0 || config >= kNumConfigs) return SGEMM_STATUS_INVALID_CONFIG;
+    return kConfigs[config].per_cu > 0 ? 1 : 0;
+}
+
+double sgemm_config_predict_us(int config, int64_t M, int64_t N, int64_t K, int64_t batch) {
+    if (config < 0 || config >= kNumConfigs) return (double)SGEMM_STATUS_INVALID_CONFIG;
+    if (M < 0 || N < 0 || K < 0 || batch < 0) return (double)SGEMM_STATUS_INVALID_SIZE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim || batch > kMaxDim)
+        return (double)SGEMM_STATUS_SIZE_OVERFLOW;
+    if (kConfigs[config].per_cu == 0) return (double)SGEMM_STATUS_INVALID_CONFIG;
+    return predict_us(kConfigs[config], M, N, K, batch);
+}
+
+int sgemm_autotune(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                   int64_t strideA, const float* B, int64_t ldb, int64_t strideB, float* C,
+                   int64_t ldc, int64_t strideC, int64_t batch, hipStream_t stream, int reps,
+                   int* best_config, float* best_ms) {
+    if (best_config == nullptr) return SGEMM_STATUS_NULL_POINTER;
+    if (reps < 1) return SGEMM_STATUS_INVALID_SIZE;
+    const int st = validate(M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch);
+    if (st != SGEMM_STATUS_SUCCESS) return st;
+    *best_config = (M == 0 || N == 0 || batch == 0) ? 0 : choose_config(M, N, K, batch);
+    if (best_ms) *best_ms = 0.0f;
+    if (M == 0 || N == 0 || batch == 0 || K == 0) return SGEMM_STATUS_SUCCESS;
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess) return SGEMM_STATUS_LAUNCH_FAILED;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return SGEMM_STATUS_LAUNCH_FAILED;
+    }
+    int status = SGEMM_STATUS_SUCCESS;
+    float best = -1.0f;
+    for (int idx = 0; idx < kNumConfigs && status == SGEMM_STATUS_SUCCESS; ++idx) {
+        const ConfigEntry& c = kConfigs[idx];
+        if (c.per_cu == 0) continue;
+        auto launch = [&]() {
+            return launch_gemm(c.kernel, c.bm, c.bn, c.threads, M, N, K, A, lda, strideA, B,
+                               ldb, strideB, C, ldc, strideC, batch, stream);
+        };
+        status = launch();  // warm-up
+        if (status != SGEMM_STATUS_SUCCESS) break;
+        if (hipEventRecord(e0, stream) != hipSuccess) status = SGEMM_STATUS_LAUNCH_FAILED;
+        for (int r = 0; r < reps && status == SGEMM_STATUS_SUCCESS; ++r) status = launch();
+        if (status != SGEMM_STATUS_SUCCESS) break;
+        float ms = 0.0f;
+        if (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+            hipEventElapsedTime(&ms, e0, e1) != hipSuccess) {
+            status = SGEMM_STATUS_LAUNCH_FAILED;
+            break;
+        }
+        ms /= (float)reps;
+        if (best < 0.0f || ms < best) {
+            best = ms;
+            *best_config = idx;
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (status != SGEMM_STATUS_SUCCESS) return status;
+    // Leave C holding the product of the chosen configuration.
+    const ConfigEntry& c = kConfigs[*best_config];
+    status = launch_gemm(c.kernel, c.bm, c.bn, c.threads, M, N, K, A, lda, strideA, B, ldb,
+                         strideB, C, ldc, strideC, batch, stream);
+    if (best_ms) *best_ms = best;
+    return status;
 }
 
 const char* sgemm_status_string(int status) {

@@ -68,6 +68,10 @@ WORKLOADS = {
                        seed=2, about="4000x3000x4100, lda=K+3, ldb=N+5, ldc=N+7, seed 2"),
     "tall": Workload("tall", 16384, 4096, 4096, 4096, 4096, 4096, "normal", "normal",
                      1.0, 0.02, 3, about="16384x4096x4096, A~normal(0,1), B~normal(0,0.02)"),
+    "shard512": Workload("shard512", 512, 4096, 4096, 4096, 4096, 4096, "normal", "normal",
+                         1.0 / math.sqrt(4096), 1.0 / math.sqrt(4096), 5,
+                         about="512x4096x4096 (one of 8 row panels of 4096^3), "
+                               "normal(0,1)/sqrt(K), seed 5"),
     "batched128": Workload("batched128", 128, 128, 128, 128, 128, 128, "uniform", "uniform",
                            seed=4, batch=1024, strideA=128 * 128, strideB=128 * 128,
                            strideC=128 * 128,
