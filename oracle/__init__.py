@@ -56,6 +56,14 @@ def _load():
     lib.oracle_sgemm_strided_batched_f64.restype = ctypes.c_int
     lib.oracle_sgemm_entries_f64.argtypes = [i64, p, i64, p, i64, i64, p, p, p, p]
     lib.oracle_sgemm_entries_f64.restype = None
+    lib.oracle_sgemm_ex_f64.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64,
+                                        ctypes.c_float, p, i64, p, i64, ctypes.c_float, p, i64,
+                                        p, p, i64, ctypes.c_int]
+    lib.oracle_sgemm_ex_f64.restype = ctypes.c_int
+    lib.oracle_sgemm_ex_entries_f64.argtypes = [ctypes.c_int, ctypes.c_int, i64, ctypes.c_float,
+                                                p, i64, p, i64, ctypes.c_float, p, i64, i64, p,
+                                                p, p, p]
+    lib.oracle_sgemm_ex_entries_f64.restype = None
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -149,4 +157,73 @@ def entries_f64(K: int, A, lda: int, B, ldb: int, rows, cols):
                 raise ValueError("entry index outside the operands")
         lib.oracle_sgemm_entries_f64(K, _ptr(a), lda, _ptr(b), ldb, r.size, _ptr(r), _ptr(c),
                                      _ptr(out), _ptr(out_abs))
+    return out, out_abs
+
+
+def _stored_shape(trans: bool, rows: int, cols: int):
+    """Rows and columns of the stored matrix whose op() is rows x cols."""
+    return (cols, rows) if trans else (rows, cols)
+
+
+def _need(rows: int, cols: int, ld: int) -> int:
+    return (rows - 1) * ld + cols if rows > 0 and cols > 0 else 0
+
+
+def sgemm_ex_f64(transA: bool, transB: bool, M: int, N: int, K: int, alpha: float, A, lda: int,
+                 B, ldb: int, beta: float, C_in=None, ldc: int = 0, nthreads: int = 0):
+    """C = alpha op(A) op(B) + beta C_in (definitions in oracle.c); FP64
+    (C, Cabs, threads_used) of shape (M, N).  A is stored K x M when transA,
+    B is stored N x K when transB; C_in is read only when beta != 0."""
+    lib = _load()
+    alpha = float(np.float32(alpha))
+    beta = float(np.float32(beta))
+    a = _f32_flat(A) if A is not None else np.zeros(1, np.float32)
+    b = _f32_flat(B) if B is not None else np.zeros(1, np.float32)
+    if alpha != 0.0 and K > 0 and M > 0 and N > 0:
+        if a.size < _need(*_stored_shape(transA, M, K), lda):
+            raise ValueError("A buffer too small")
+        if b.size < _need(*_stored_shape(transB, K, N), ldb):
+            raise ValueError("B buffer too small")
+    c = np.zeros(1, np.float32)
+    if beta != 0.0:
+        c = _f32_flat(C_in)
+        if c.size < _need(M, N, ldc):
+            raise ValueError("C buffer too small")
+    out = np.empty((M, N), dtype=np.float64)
+    out_abs = np.empty((M, N), dtype=np.float64)
+    used = 1
+    if M > 0 and N > 0:
+        used = lib.oracle_sgemm_ex_f64(int(bool(transA)), int(bool(transB)), M, N, K, alpha,
+                                       _ptr(a), lda, _ptr(b), ldb, beta, _ptr(c), ldc,
+                                       _ptr(out), _ptr(out_abs), N, nthreads)
+    return out, out_abs, used
+
+
+def ex_entries_f64(transA: bool, transB: bool, K: int, alpha: float, A, lda: int, B, ldb: int,
+                   beta: float, C_in, ldc: int, rows, cols):
+    """Selected entries of :func:`sgemm_ex_f64`, bitwise equal to the full form."""
+    lib = _load()
+    alpha = float(np.float32(alpha))
+    beta = float(np.float32(beta))
+    a = _f32_flat(A)
+    b = _f32_flat(B)
+    c = _f32_flat(C_in) if beta != 0.0 else np.zeros(1, np.float32)
+    r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+    cc = np.ascontiguousarray(np.asarray(cols, dtype=np.int64))
+    if r.shape != cc.shape:
+        raise ValueError("rows and cols differ in length")
+    if r.size and K > 0 and alpha != 0.0:
+        m_need, n_need = int(r.max()) + 1, int(cc.max()) + 1
+        if a.size < _need(*_stored_shape(transA, m_need, K), lda):
+            raise ValueError("entry index outside A")
+        if b.size < _need(*_stored_shape(transB, K, n_need), ldb):
+            raise ValueError("entry index outside B")
+    if r.size and beta != 0.0 and c.size < int(r.max()) * ldc + int(cc.max()) + 1:
+        raise ValueError("entry index outside C")
+    out = np.empty(r.size, dtype=np.float64)
+    out_abs = np.empty(r.size, dtype=np.float64)
+    if r.size:
+        lib.oracle_sgemm_ex_entries_f64(int(bool(transA)), int(bool(transB)), K, alpha, _ptr(a),
+                                        lda, _ptr(b), ldb, beta, _ptr(c), ldc, r.size, _ptr(r),
+                                        _ptr(cc), _ptr(out), _ptr(out_abs))
     return out, out_abs

@@ -131,6 +131,88 @@ void oracle_sgemm_entries_f64(int64_t K, const float *A, int64_t lda, const floa
     }
 }
 
+/*
+ * General form C = alpha * op(A) op(B) + beta * C, row-major.
+ *
+ * op(A) is the M x K matrix A (stored M x K, leading dimension lda) when
+ * transA == 0, and the transpose of the stored K x M matrix when transA != 0:
+ * op(A)[i][k] = A[k*lda + i].  "CMU DLSys Lecture 12: GPU Acceleration",
+ * section 4, writes the product in exactly that form, C = A^T B with A stored
+ * K x M.  op(B) is the K x N matrix B (stored K x N, ldb) when transB == 0,
+ * else the transpose of the stored N x K matrix: op(B)[k][j] = B[j*ldb + k].
+ *
+ * alpha and beta are the usual scalar update; the pages have none (their
+ * accumulators start at zero and C is not read, which is alpha = 1, beta = 0).
+ * The reading taken is the standard one: with beta == 0, C_in is not read at
+ * all (so NaN or garbage there does not matter); with alpha == 0 or K == 0
+ * the product term is zero and A and B are not read.
+ *
+ * Every element is the same k-ascending FP64 sum as oracle_sgemm_f64; then
+ * out = alpha * sum + beta * C_in in FP64, and
+ * out_abs = |alpha| * sum_k |op(A)[i][k]| |op(B)[k][j]| + |beta| * |C_in|,
+ * the scale of the acceptance bound.  C_in (float, leading dimension ldc_in)
+ * may be NULL when beta == 0; out and out_abs are M x N with leading
+ * dimension ldo (out_abs may be NULL).
+ */
+static void element_ex(int transA, int transB, int64_t i, int64_t j, int64_t K, double alpha,
+                       const float *A, int64_t lda, const float *B, int64_t ldb, double beta,
+                       const float *C_in, int64_t ldc_in, double *out, double *out_abs) {
+    double acc = 0.0, accabs = 0.0;
+    if (alpha != 0.0) {
+        for (int64_t k = 0; k < K; ++k) {
+            const double a = (double)(transA ? A[k * lda + i] : A[i * lda + k]);
+            const double b = (double)(transB ? B[j * ldb + k] : B[k * ldb + j]);
+            acc += a * b;
+            accabs += fabs(a) * fabs(b);
+        }
+    }
+    double v = alpha * acc;
+    double vabs = fabs(alpha) * accabs;
+    if (beta != 0.0) {
+        const double c = (double)C_in[i * ldc_in + j];
+        v += beta * c;
+        vabs += fabs(beta) * fabs(c);
+    }
+    *out = v;
+    if (out_abs) *out_abs = vabs;
+}
+
+int oracle_sgemm_ex_f64(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                        const float *A, int64_t lda, const float *B, int64_t ldb, float beta,
+                        const float *C_in, int64_t ldc_in, double *out, double *out_abs,
+                        int64_t ldo, int nthreads) {
+    int used = 1;
+    if (M <= 0 || N <= 0) return used;
+#ifdef _OPENMP
+    if (nthreads <= 0) nthreads = omp_get_max_threads();
+    if (nthreads > M) nthreads = (int)M;
+    used = nthreads;
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            element_ex(transA, transB, i, j, K, (double)alpha, A, lda, B, ldb, (double)beta,
+                       C_in, ldc_in, out + i * ldo + j, out_abs ? out_abs + i * ldo + j : NULL);
+        }
+    }
+    return used;
+}
+
+/* Selected entries of the general form; bitwise equal to the full version. */
+void oracle_sgemm_ex_entries_f64(int transA, int transB, int64_t K, float alpha,
+                                 const float *A, int64_t lda, const float *B, int64_t ldb,
+                                 float beta, const float *C_in, int64_t ldc_in,
+                                 int64_t n_entries, const int64_t *rows, const int64_t *cols,
+                                 double *out, double *out_abs) {
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t e = 0; e < n_entries; ++e) {
+        element_ex(transA, transB, rows[e], cols[e], K, (double)alpha, A, lda, B, ldb,
+                   (double)beta, C_in, ldc_in, out + e, out_abs ? out_abs + e : NULL);
+    }
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();
