@@ -143,9 +143,10 @@ void oracle_sgemm_entries_f64(int64_t K, const float *A, int64_t lda, const floa
  *
  * alpha and beta are the usual scalar update; the pages have none (their
  * accumulators start at zero and C is not read, which is alpha = 1, beta = 0).
- * The reading taken is the standard one: with beta == 0, C_in is not read at
- * all (so NaN or garbage there does not matter); with alpha == 0 or K == 0
- * the product term is zero and A and B are not read.
+ * The reading taken is the standard BLAS one: with beta == 0, C_in is not
+ * read at all (so NaN or garbage there does not matter); with alpha == 0 or
+ * K == 0 there is no product term at all (A and B are not read), so the
+ * result is beta * C_in, or +0 when beta == 0.
  *
  * Every element is the same k-ascending FP64 sum as oracle_sgemm_f64; then
  * out = alpha * sum + beta * C_in in FP64, and
@@ -157,20 +158,22 @@ void oracle_sgemm_entries_f64(int64_t K, const float *A, int64_t lda, const floa
 static void element_ex(int transA, int transB, int64_t i, int64_t j, int64_t K, double alpha,
                        const float *A, int64_t lda, const float *B, int64_t ldb, double beta,
                        const float *C_in, int64_t ldc_in, double *out, double *out_abs) {
-    double acc = 0.0, accabs = 0.0;
-    if (alpha != 0.0) {
+    const int has_product = alpha != 0.0 && K > 0;
+    double v = 0.0, vabs = 0.0;
+    if (has_product) {
+        double acc = 0.0, accabs = 0.0;
         for (int64_t k = 0; k < K; ++k) {
             const double a = (double)(transA ? A[k * lda + i] : A[i * lda + k]);
             const double b = (double)(transB ? B[j * ldb + k] : B[k * ldb + j]);
             acc += a * b;
             accabs += fabs(a) * fabs(b);
         }
+        v = alpha * acc;
+        vabs = fabs(alpha) * accabs;
     }
-    double v = alpha * acc;
-    double vabs = fabs(alpha) * accabs;
     if (beta != 0.0) {
         const double c = (double)C_in[i * ldc_in + j];
-        v += beta * c;
+        v = has_product ? v + beta * c : beta * c;
         vabs += fabs(beta) * fabs(c);
     }
     *out = v;

@@ -147,6 +147,12 @@ def check_ex_scalar_closed_forms(ex):
     # K = 0: the empty sum, so only beta C remains
     out, _ = ex(False, False, M, N, 0, 5.0, nan_ab, ld, nan_ab, ld, 0.5, c, ld)
     assert np.all(out == 0.75)
+    # no product term at all (BLAS): signed zeros come from beta C alone
+    out, _ = ex(False, False, M, N, 0, -1.0, nan_ab, ld, nan_ab, ld, 0.0, None, ld)
+    assert np.all(out == 0.0) and not np.any(np.signbit(out))
+    zero_c = _padded(0.0, M, N, ld, side)
+    out, _ = ex(False, False, M, N, K, 0.0, nan_ab, ld, nan_ab, ld, -1.0, zero_c, ld)
+    assert np.all(np.signbit(out))
 
 
 EX_PIN_CHECKS = [check_ex_fraction_bruteforce, check_ex_worked_example,
@@ -193,11 +199,12 @@ EX_MUTATIONS = {
     "transB_ignored": ("(transB ? B[j * ldb + k] : B[k * ldb + j])", "(B[k * ldb + j])"),
     "transA_index_swapped": ("(transA ? A[k * lda + i] : A[i * lda + k])",
                              "(transA ? A[i * lda + k] : A[i * lda + k])"),
-    "alpha_ignored": ("double v = alpha * acc;", "double v = acc;"),
-    "beta_ignored": ("v += beta * c;", "v += c;"),
+    "alpha_ignored": ("v = alpha * acc;", "v = acc;"),
+    "beta_ignored": ("v = has_product ? v + beta * c : beta * c;",
+                     "v = has_product ? v + c : c;"),
     "abs_of_beta_term_dropped": ("vabs += fabs(beta) * fabs(c);", "vabs += beta * c;"),
-    "alpha_zero_still_reads": ("if (alpha != 0.0) {\n        for (int64_t k = 0; k < K; ++k) {",
-                               "if (1) {\n        for (int64_t k = 0; k < K; ++k) {"),
+    "alpha_zero_still_reads": ("const int has_product = alpha != 0.0 && K > 0;",
+                               "const int has_product = 1;"),
 }
 
 
