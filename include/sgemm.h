@@ -57,8 +57,11 @@ typedef enum sgemm_status {
     SGEMM_STATUS_INVALID_STRIDE = -5,
     /* HIP reported an error when the kernel was enqueued. */
     SGEMM_STATUS_LAUNCH_FAILED = -6,
-    /* The tile configuration index passed to sgemm_with_config is unknown. */
-    SGEMM_STATUS_INVALID_CONFIG = -7
+    /* The tile configuration index is unknown, or (general form) the tile is
+       not built for the general form. */
+    SGEMM_STATUS_INVALID_CONFIG = -7,
+    /* A transpose flag of the general form is neither 0 nor 1. */
+    SGEMM_STATUS_INVALID_OP = -8
 } sgemm_status_t;
 
 /*
@@ -94,6 +97,53 @@ int sgemm_valu_strided_batched(int64_t M, int64_t N, int64_t K, const float *A, 
                                int64_t strideA, const float *B, int64_t ldb, int64_t strideB,
                                float *C, int64_t ldc, int64_t strideC, int64_t batch,
                                hipStream_t stream);
+
+/*
+ * General form C = alpha * op(A) * op(B) + beta * C on the matrix cores,
+ * row-major like the plain product.  C is M x N (ldc >= max(1, N)).
+ *   transA = 0: A is stored M x K (lda >= max(1, K)), op(A) = A.
+ *   transA = 1: A is stored K x M (lda >= max(1, M)), op(A) = A^T; this is
+ *     the form "CMU DLSys Lecture 12: GPU Acceleration" section 4 writes the
+ *     product in, C = A^T B.
+ *   transB = 0: B is stored K x N (ldb >= max(1, N)); transB = 1: B is stored
+ *     N x K (ldb >= max(1, K)), op(B) = B^T.
+ * alpha and beta follow the BLAS convention (the pages have neither; their
+ * product is alpha = 1, beta = 0): beta == 0 means C is not read, so it may
+ * hold anything, NaN included; alpha == 0 or K == 0 means there is no product
+ * term, A and B are not read (and may be NULL), and C becomes beta * C (+0
+ * when beta == 0; nothing is enqueued when beta == 1).  Other flag values
+ * give SGEMM_STATUS_INVALID_OP.  Errors, ownership and stream behaviour as
+ * for sgemm; the operands are read in place, whatever their layout (each
+ * stored layout has its own global->LDS copy, nothing is transposed in
+ * memory).
+ */
+int sgemm_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+             const float *A, int64_t lda, const float *B, int64_t ldb, float beta, float *C,
+             int64_t ldc, hipStream_t stream);
+
+/* Strided batch of the general form; strides as for sgemm_strided_batched. */
+int sgemm_ex_strided_batched(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                             float alpha, const float *A, int64_t lda, int64_t strideA,
+                             const float *B, int64_t ldb, int64_t strideB, float beta, float *C,
+                             int64_t ldc, int64_t strideC, int64_t batch, hipStream_t stream);
+
+/*
+ * The general form with an explicit tile configuration, for tests and
+ * tuning; SGEMM_STATUS_INVALID_CONFIG if the index is unknown or the tile is
+ * not built for the general form (sgemm_config_has_general_form).
+ */
+int sgemm_ex_with_config(int config, int transA, int transB, int64_t M, int64_t N, int64_t K,
+                         float alpha, const float *A, int64_t lda, int64_t strideA,
+                         const float *B, int64_t ldb, int64_t strideB, float beta, float *C,
+                         int64_t ldc, int64_t strideC, int64_t batch, hipStream_t stream);
+
+/* 1 if tile configuration `config` is built for the general form (all four
+   layouts), 0 if not, SGEMM_STATUS_INVALID_CONFIG if unknown.  Host only. */
+int sgemm_config_has_general_form(int config);
+
+/* The configuration sgemm_ex would use for this shape (any layout).  Host
+   only; a negative status for bad sizes. */
+int sgemm_select_general_config(int64_t M, int64_t N, int64_t K, int64_t batch);
 
 /*
  * Matrix-core product with an explicit block-tile configuration, for tests

@@ -129,3 +129,43 @@ def test_status_strings():
         s = sg.status_string(code)
         assert isinstance(s, str) and s
     assert sg.status_string(0) == "success"
+
+
+def test_general_form_argument_errors_enqueue_nothing():
+    lib = _native.lib()
+    F = FAKE
+    # transpose flag out of range
+    assert lib.sgemm_ex(2, 0, 4, 4, 4, 1.0, F, 4, F, 4, 0.0, F, 4, 0) == -8
+    assert lib.sgemm_ex(0, -1, 4, 4, 4, 1.0, F, 4, F, 4, 0.0, F, 4, 0) == -8
+    # transposed A needs lda >= M; transposed B needs ldb >= K
+    assert lib.sgemm_ex(1, 0, 8, 4, 4, 1.0, F, 4, F, 4, 0.0, F, 4, 0) == -2
+    assert lib.sgemm_ex(0, 1, 4, 4, 8, 1.0, F, 8, F, 4, 0.0, F, 4, 0) == -2
+    # plain layouts keep the plain rules
+    assert lib.sgemm_ex(0, 0, 4, 4, 8, 1.0, F, 4, F, 4, 0.0, F, 4, 0) == -2
+    # A and B may be NULL only when they are not read
+    assert lib.sgemm_ex(0, 0, 4, 4, 4, 1.0, None, 4, F, 4, 0.0, F, 4, 0) == -3
+    assert lib.sgemm_ex(0, 0, 4, 4, 4, 1.0, F, 4, F, 4, 0.0, None, 4, 0) == -3
+    # empty products succeed without touching anything
+    assert lib.sgemm_ex(1, 1, 0, 4, 4, 1.0, None, 1, None, 4, 0.0, None, 4, 0) == 0
+    # strided batch: overlapping C matrices
+    assert lib.sgemm_ex_strided_batched(0, 0, 4, 4, 4, 1.0, F, 4, 16, F, 4, 16, 0.0, F, 4, 15,
+                                        2, 0) == -5
+    # a tile without the general form, and an unknown tile
+    plain = [c for c in range(sg.num_configs()) if not sg.config_has_general_form(c)]
+    assert plain
+    assert lib.sgemm_ex_with_config(plain[0], 0, 0, 4, 4, 4, 1.0, F, 4, 0, F, 4, 0, 0.0, F, 4,
+                                    0, 1, 0) == -7
+    assert lib.sgemm_ex_with_config(sg.num_configs(), 0, 0, 4, 4, 4, 1.0, F, 4, 0, F, 4, 0,
+                                    0.0, F, 4, 0, 1, 0) == -7
+    assert sg.status_string(-8).startswith("invalid transpose")
+
+
+def test_general_config_selection():
+    general = [c for c in range(sg.num_configs()) if sg.config_has_general_form(c)]
+    assert len(general) >= 4
+    for shape in [(4096, 4096, 4096, 1), (1024, 1024, 1024, 1), (4000, 3000, 4100, 1),
+                  (512, 4096, 4096, 1), (128, 128, 128, 1024), (3, 5, 7, 1)]:
+        c = sg.select_general_config(*shape)
+        assert c in general
+        pred = {g: sg.predict_us(g, *shape) for g in general}
+        assert pred[c] == min(pred.values())

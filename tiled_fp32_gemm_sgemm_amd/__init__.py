@@ -4,11 +4,13 @@ The product runs in libsgemm.so (hand-written HIP kernels behind the C ABI
 in include/sgemm.h); this package only passes tensors' device addresses,
 leading dimensions and the current stream to it.
 """
-from .api import (autotune, autotune_raw, config_info, config_selectable, num_configs,
-                  predict_us, select_config, sgemm, sgemm_raw, sgemm_strided_batched,
-                  sgemm_strided_batched_raw)
+from .api import (autotune, autotune_raw, config_has_general_form, config_info,
+                  config_selectable, num_configs, predict_us, select_config,
+                  select_general_config, sgemm, sgemm_ex, sgemm_ex_raw, sgemm_raw,
+                  sgemm_strided_batched, sgemm_strided_batched_raw)
 from ._native import SgemmError, status_string
 
 __all__ = ["sgemm", "sgemm_strided_batched", "sgemm_raw", "sgemm_strided_batched_raw",
            "num_configs", "config_info", "select_config", "config_selectable", "predict_us",
-           "autotune", "autotune_raw", "SgemmError", "status_string"]
+           "autotune", "autotune_raw", "sgemm_ex", "sgemm_ex_raw", "config_has_general_form",
+           "select_general_config", "SgemmError", "status_string"]

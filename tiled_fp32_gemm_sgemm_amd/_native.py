@@ -23,6 +23,7 @@ STATUS = {
     -5: "SGEMM_STATUS_INVALID_STRIDE",
     -6: "SGEMM_STATUS_LAUNCH_FAILED",
     -7: "SGEMM_STATUS_INVALID_CONFIG",
+    -8: "SGEMM_STATUS_INVALID_OP",
 }
 
 
@@ -54,6 +55,16 @@ _SIGS = {
                            ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
     "sgemm_select_config": ([_i64, _i64, _i64, _i64], ctypes.c_int),
     "sgemm_config_selectable": ([ctypes.c_int], ctypes.c_int),
+    "sgemm_ex": ([ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, ctypes.c_float, _p, _i64, _p,
+                  _i64, ctypes.c_float, _p, _i64, _p], ctypes.c_int),
+    "sgemm_ex_strided_batched": (
+        [ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, ctypes.c_float, _p, _i64, _i64, _p, _i64,
+         _i64, ctypes.c_float, _p, _i64, _i64, _i64, _p], ctypes.c_int),
+    "sgemm_ex_with_config": (
+        [ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, ctypes.c_float, _p, _i64,
+         _i64, _p, _i64, _i64, ctypes.c_float, _p, _i64, _i64, _i64, _p], ctypes.c_int),
+    "sgemm_config_has_general_form": ([ctypes.c_int], ctypes.c_int),
+    "sgemm_select_general_config": ([_i64, _i64, _i64, _i64], ctypes.c_int),
     "sgemm_config_predict_us": ([ctypes.c_int, _i64, _i64, _i64, _i64], ctypes.c_double),
     "sgemm_autotune": (
         [_i64, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _p, _i64, _i64, _i64, _p,

@@ -192,3 +192,70 @@ def autotune(A, B, out=None, reps: int = 10, stream=None):
                                    _stream_handle(stream, A.device), reps)
     _check(st, "sgemm_autotune")
     return cfg, ms, out
+
+
+def sgemm_ex_raw(transA, transB, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ldc,
+                 stream=0, config=None, batch=1, strideA=0, strideB=0, strideC=0) -> int:
+    """C = alpha op(A) op(B) + beta C on device addresses; returns the status."""
+    lib = _native.lib()
+    if config is not None:
+        return lib.sgemm_ex_with_config(int(config), int(transA), int(transB), M, N, K,
+                                        float(alpha), A_ptr, lda, strideA, B_ptr, ldb, strideB,
+                                        float(beta), C_ptr, ldc, strideC, batch, stream)
+    if batch == 1 and strideA == 0 and strideB == 0 and strideC == 0:
+        return lib.sgemm_ex(int(transA), int(transB), M, N, K, float(alpha), A_ptr, lda, B_ptr,
+                            ldb, float(beta), C_ptr, ldc, stream)
+    return lib.sgemm_ex_strided_batched(int(transA), int(transB), M, N, K, float(alpha), A_ptr,
+                                        lda, strideA, B_ptr, ldb, strideB, float(beta), C_ptr,
+                                        ldc, strideC, batch, stream)
+
+
+def sgemm_ex(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, transA: bool = False,
+             transB: bool = False, stream=None, config=None):
+    """C = alpha op(A) op(B) + beta C.  A and B are the stored matrices
+    (2-D, or 3-D for a strided batch): A is M x K, or K x M with transA; B is
+    K x N, or N x K with transB.  C (M x N, or batch x M x N) is required when
+    beta != 0 and is updated in place; otherwise a new tensor is returned."""
+    import torch
+    batched = A.dim() == 3
+    nd = 3 if batched else 2
+    _operand(A, "A", nd)
+    _operand(B, "B", nd)
+    ra, ca = A.shape[-2:]
+    rb, cb = B.shape[-2:]
+    M, K = (ca, ra) if transA else (ra, ca)
+    K2, N = (cb, rb) if transB else (rb, cb)
+    batch = A.shape[0] if batched else 1
+    if K != K2 or (batched and B.shape[0] != batch):
+        raise ValueError("shapes differ: %s vs %s" % (tuple(A.shape), tuple(B.shape)))
+    shape = (batch, M, N) if batched else (M, N)
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("C is required when beta != 0")
+        C = torch.empty(shape, dtype=torch.float32, device=A.device)
+    _operand(C, "C", nd)
+    if tuple(C.shape) != shape:
+        raise ValueError("C must have shape %s" % (shape,))
+    sa = int(A.stride(0)) if batched else 0
+    sb = int(B.stride(0)) if batched else 0
+    sc = int(C.stride(0)) if batched else 0
+    with torch.cuda.device(A.device):
+        st = sgemm_ex_raw(transA, transB, M, N, K, alpha, A.data_ptr(), _ld(A), B.data_ptr(),
+                          _ld(B), beta, C.data_ptr(), _ld(C), _stream_handle(stream, A.device),
+                          config, batch, sa, sb, sc)
+    _check(st, "sgemm_ex")
+    return C
+
+
+def config_has_general_form(config: int) -> bool:
+    st = _native.lib().sgemm_config_has_general_form(int(config))
+    if st < 0:
+        raise _native.SgemmError(st, "sgemm_config_has_general_form")
+    return bool(st)
+
+
+def select_general_config(M: int, N: int, K: int, batch: int = 1) -> int:
+    st = _native.lib().sgemm_select_general_config(M, N, K, batch)
+    if st < 0:
+        raise _native.SgemmError(st, "sgemm_select_general_config")
+    return st

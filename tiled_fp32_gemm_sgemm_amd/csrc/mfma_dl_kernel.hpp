@@ -56,8 +56,17 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // unit returns zeros for it.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
+// Four floats held as one operand group: an f32x4 for operands read as
+// 16-byte quads, this for operands read one float per k step.
+struct F4 {
+    float v[4];
+    __device__ __forceinline__ float& operator[](int i) { return v[i]; }
+    __device__ __forceinline__ const float& operator[](int i) const { return v[i]; }
+};
+
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MI_, int OCC_, int GROUP_M_,
-          int STAGES_ = 2, int KSPLIT_ = 1, bool SWIZZLE_ = true>
+          int STAGES_ = 2, int KSPLIT_ = 1, bool SWIZZLE_ = true, bool TA_ = false,
+          bool TB_ = false, bool EX_ = false>
 struct DlTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -67,6 +76,14 @@ struct DlTile {
     static constexpr int STAGES = STAGES_;               // LDS slice buffers in flight
     static constexpr int KSPLIT = KSPLIT_;               // wave groups splitting each slice's k
     static constexpr bool SWIZZLE = SWIZZLE_;
+    // Stored layouts: A is M x K (TA = false) or K x M (TA = true, op(A) = A^T);
+    // B is K x N (TB = false) or N x K (TB = true).  An operand whose k runs
+    // along its stored rows ("k-contiguous": A with TA = false, B with TB =
+    // true) is staged as [mn][k] and read as swizzled 16-byte quads; the other
+    // kind is staged as [k][mn] and read one float per k step.
+    static constexpr bool TA = TA_, TB = TB_;
+    static constexpr bool A_KC = !TA, B_KC = TB;
+    static constexpr bool EX = EX_;                      // alpha/beta epilogue
     static constexpr int NWMN = WAVES_M * WAVES_N;       // waves per k group
     static constexpr int NW = NWMN * KSPLIT;             // waves per workgroup
     static constexpr int NT = 64 * NW;
@@ -75,9 +92,11 @@ struct DlTile {
     static constexpr int TM = WTM / MI, TN = WTN / MI;
     static constexpr int LG = 64 / MI;
     static constexpr int KPL = KSUB / LG;
-    static constexpr int QPR = BK / 4;                   // quads per A row
-    static constexpr int B_QPR = BN / 4;                 // quads per B row
-    static constexpr int LDB = BN;
+    static constexpr int QPR = BK / 4;                   // quads per k-contiguous LDS row
+    static constexpr int A_QPR = A_KC ? BK / 4 : BM / 4; // quads per LDS row of A
+    static constexpr int B_QPR = B_KC ? BK / 4 : BN / 4; // quads per LDS row of B
+    static constexpr int LDA_S = BM;                     // LDS row length of A staged [k][m]
+    static constexpr int LDB = BN;                       // LDS row length of B staged [k][n]
     static constexpr int A_FLOATS = BM * BK;
     static constexpr int B_FLOATS = BK * BN;
     static constexpr int BUF_FLOATS = A_FLOATS + B_FLOATS;
@@ -85,14 +104,14 @@ struct DlTile {
     static constexpr int KG = 4;
     static constexpr int NKG = KPL / KG;
     static constexpr int HOLD = 2;                       // k steps issued after the barrier
-    static constexpr int A_CH = BM * QPR / 64;           // 1 KB chunks per A slice
-    static constexpr int B_CH = BK * B_QPR / 64;         // 1 KB chunks per B slice
+    static constexpr int A_CH = BM * BK / 256;           // 1 KB chunks per A slice
+    static constexpr int B_CH = BK * BN / 256;           // 1 KB chunks per B slice
     static constexpr int A_CHW = A_CH / NW;              // chunks per wave
     static constexpr int B_CHW = B_CH / NW;
     static constexpr int BFLIP = MI == 16 ? 4 : 0;       // quad flip on odd lane-group row blocks
     // Register-staged fallback: quads per thread per slice.
-    static constexpr int A_VEC = BM * QPR / NT;
-    static constexpr int B_VEC = BK * B_QPR / NT;
+    static constexpr int A_VEC = BM * BK / 4 / NT;
+    static constexpr int B_VEC = BK * BN / 4 / NT;
     static constexpr int LDS_BYTES = STAGES * BUF_FLOATS * 4;
     static constexpr int LPS = A_CHW + B_CHW;            // copy instructions per wave per slice
 
@@ -101,17 +120,27 @@ struct DlTile {
     static_assert(KPL % KG == 0 && NKG % 2 == 0, "whole, even number of A operand groups");
     static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must be MFMA tile multiples");
     static_assert(A_CH % NW == 0 && B_CH % NW == 0, "slice chunks must split over the waves");
-    static_assert(BN % 32 == 0, "B rows must start on the same ds_read_b32 bank");
+    static_assert(BN % 32 == 0 && BM % 32 == 0, "[k][mn] rows must start on bank 0");
     static_assert(STAGES >= 2 && LPS * (STAGES - 2) <= 63, "vmcnt holds at most 63");
-    static_assert((BM * QPR) % NT == 0 && (BK * B_QPR) % NT == 0, "fallback copy must split");
-    static_assert(MI == 32 || BN >= 32, "the B flip needs 32-float rows");
+    static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0, "fallback copy must split");
+    static_assert(MI == 32 || (BN >= 32 && BM >= 32), "the flip needs 32-float rows");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert((KSPLIT - 1) * BM * BN <= STAGES * BUF_FLOATS, "k-group exchange fits in LDS");
 
     static __device__ __forceinline__ int swz(int r) { return SWIZZLE ? (r / RPB) % QPR : 0; }
     // Physical quad of logical quad nq in B row k is nq ^ flip(k).
     static __device__ __forceinline__ int flip(int k) { return ((k / KPL) & 1) * BFLIP; }
+    using AReg = std::conditional_t<A_KC, f32x4, F4>;
+    using BReg = std::conditional_t<B_KC, f32x4, F4>;
 };
+
+// A 64-bit value that is the same in every lane, moved to scalar registers
+// (free when it already is scalar).
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
 
 // Waits until at most N vector-memory operations of this wave are still
 // outstanding; the export and LDS counters are left alone.  (s_waitcnt
@@ -164,8 +193,15 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     const TileCoord tc = map_block(p, T::GROUP_M);
     const int m0 = tc.tm * T::BM;
     const int n0 = tc.tn * T::BN;
-    const float* const A = p.A + (int64_t)tc.b * p.strideA + (int64_t)m0 * p.lda;
-    const float* const B = p.B + (int64_t)tc.b * p.strideB + n0;
+    // Tile origin in each stored operand (element offsets); k advances along
+    // rows (k-contiguous) or down rows.  The offsets are wave-uniform; saying
+    // so keeps them, and the buffer descriptors built from them, in SGPRs.
+    const int64_t a_org = uniform_i64((int64_t)tc.b * p.strideA +
+                                      (T::A_KC ? (int64_t)m0 * p.lda : (int64_t)m0));
+    const int64_t b_org = uniform_i64((int64_t)tc.b * p.strideB +
+                                      (T::B_KC ? (int64_t)n0 * p.ldb : (int64_t)n0));
+    const float* const A = p.A + a_org;
+    const float* const B = p.B + b_org;
     float* const C = p.C + (int64_t)tc.b * p.strideC + (int64_t)m0 * p.ldc + n0;
     const int rows_left = p.M - m0;
     const int cols_left = p.N - n0;
@@ -179,10 +215,14 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
 
     // ---------------------------------------------------------------- loader
-    // A slice for k0 into buffer `buf`: descriptor over rows m0.. of A from
-    // column k0; B slice: descriptor over rows k0.. of B from column n0.
-    const uint32_t a_span = (uint32_t)(((int64_t)(T::BM - 1) * p.lda + T::BK) * 4);
-    const uint32_t b_span = (uint32_t)(((int64_t)(T::BK - 1) * p.ldb + T::BN) * 4);
+    // A k-contiguous slice for k0 is a descriptor over BM stored rows from
+    // column k0; an [k][mn] one is a descriptor over BK stored rows from row k0.
+    const int64_t a_span64 = T::A_KC ? (int64_t)(T::BM - 1) * p.lda + T::BK
+                                     : (int64_t)(T::BK - 1) * p.lda + T::BM;
+    const int64_t b_span64 = T::B_KC ? (int64_t)(T::BN - 1) * p.ldb + T::BK
+                                     : (int64_t)(T::BK - 1) * p.ldb + T::BN;
+    const uint32_t a_span = (uint32_t)(a_span64 * 4);
+    const uint32_t b_span = (uint32_t)(b_span64 * 4);
 
     uint32_t a_off[T::A_CHW];
     uint32_t b_off[T::B_CHW];
@@ -192,28 +232,44 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
 #pragma unroll
         for (int j = 0; j < T::A_CHW; ++j) {
             const int q = 64 * (wave * T::A_CHW + j) + lane;
-            const int r = q / T::QPR;
-            const int kq = (q % T::QPR) ^ T::swz(r);
-            const bool ok = r < rows_left && 4 * kq < kleft;
-            a_off[j] = ok ? (uint32_t)(((int64_t)r * p.lda + 4 * kq) * 4) : kOutOfRange;
+            const int r = q / T::A_QPR;
+            if constexpr (T::A_KC) {
+                const int kq = (q % T::A_QPR) ^ T::swz(r);
+                const bool ok = r < rows_left && 4 * kq < kleft;
+                a_off[j] = ok ? (uint32_t)(((int64_t)r * p.lda + 4 * kq) * 4) : kOutOfRange;
+            } else {
+                const int mq = (q % T::A_QPR) ^ T::flip(r);
+                const bool ok = r < kleft && 4 * mq < rows_left;
+                a_off[j] = ok ? (uint32_t)(((int64_t)r * p.lda + 4 * mq) * 4) : kOutOfRange;
+            }
         }
 #pragma unroll
         for (int j = 0; j < T::B_CHW; ++j) {
             const int q = 64 * (wave * T::B_CHW + j) + lane;
-            const int k = q / T::B_QPR;
-            const int nq = (q % T::B_QPR) ^ T::flip(k);
-            const bool ok = k < kleft && 4 * nq < cols_left;
-            b_off[j] = ok ? (uint32_t)(((int64_t)k * p.ldb + 4 * nq) * 4) : kOutOfRange;
+            const int r = q / T::B_QPR;
+            if constexpr (T::B_KC) {
+                const int kq = (q % T::B_QPR) ^ T::swz(r);
+                const bool ok = r < cols_left && 4 * kq < kleft;
+                b_off[j] = ok ? (uint32_t)(((int64_t)r * p.ldb + 4 * kq) * 4) : kOutOfRange;
+            } else {
+                const int nq = (q % T::B_QPR) ^ T::flip(r);
+                const bool ok = r < kleft && 4 * nq < cols_left;
+                b_off[j] = ok ? (uint32_t)(((int64_t)r * p.ldb + 4 * nq) * 4) : kOutOfRange;
+            }
         }
     };
 
     auto load_direct = [&](int k0, int buf) {
         float* const dstA = smem + buf * T::BUF_FLOATS;
         float* const dstB = dstA + T::A_FLOATS;
+        const float* const a_base =
+            p.A + uniform_i64(a_org + (T::A_KC ? (int64_t)k0 : (int64_t)k0 * p.lda));
+        const float* const b_base =
+            p.B + uniform_i64(b_org + (T::B_KC ? (int64_t)k0 : (int64_t)k0 * p.ldb));
         const __amdgpu_buffer_rsrc_t ra =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(A + k0), (short)0, (int)a_span, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-            (void*)(B + (int64_t)k0 * p.ldb), (short)0, (int)b_span, 0x00020000);
+            __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, (int)a_span, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rb =
+            __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, (int)b_span, 0x00020000);
 #pragma unroll
         for (int j = 0; j < T::A_CHW; ++j)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -233,31 +289,45 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
 #pragma unroll 1
         for (int v = 0; v < T::A_VEC; ++v) {
             const int q = tid + v * T::NT;
-            const int r = q / T::QPR;
-            const int pq = q % T::QPR;
-            const int kq = pq ^ T::swz(r);
-            const f32x4 x = ldg4_masked(A + (int64_t)r * p.lda + k0 + 4 * kq,
-                                        r < rows_left ? p.K - (k0 + 4 * kq) : 0);
+            const int r = q / T::A_QPR;
+            f32x4 x;
+            if constexpr (T::A_KC) {
+                const int kq = (q % T::A_QPR) ^ T::swz(r);
+                x = ldg4_masked(A + (int64_t)r * p.lda + k0 + 4 * kq,
+                                r < rows_left ? p.K - (k0 + 4 * kq) : 0);
+            } else {
+                const int mq = (q % T::A_QPR) ^ T::flip(r);
+                x = ldg4_masked(A + (int64_t)(k0 + r) * p.lda + 4 * mq,
+                                k0 + r < p.K ? rows_left - 4 * mq : 0);
+            }
             *(f32x4*)(As + 4 * q) = x;
         }
 #pragma unroll 1
         for (int v = 0; v < T::B_VEC; ++v) {
             const int q = tid + v * T::NT;
-            const int k = q / T::B_QPR;
-            const int nq = (q % T::B_QPR) ^ T::flip(k);
-            const f32x4 x = ldg4_masked(B + (int64_t)(k0 + k) * p.ldb + 4 * nq,
-                                        k0 + k < p.K ? cols_left - 4 * nq : 0);
+            const int r = q / T::B_QPR;
+            f32x4 x;
+            if constexpr (T::B_KC) {
+                const int kq = (q % T::B_QPR) ^ T::swz(r);
+                x = ldg4_masked(B + (int64_t)r * p.ldb + k0 + 4 * kq,
+                                r < cols_left ? p.K - (k0 + 4 * kq) : 0);
+            } else {
+                const int nq = (q % T::B_QPR) ^ T::flip(r);
+                x = ldg4_masked(B + (int64_t)(k0 + r) * p.ldb + 4 * nq,
+                                k0 + r < p.K ? cols_left - 4 * nq : 0);
+            }
             *(f32x4*)(Bs + 4 * q) = x;
         }
     };
 
-    // Direct staging needs 31-bit descriptor spans and whole-quad N edges;
-    // a partial K slice (the last one when BK does not divide K) goes through
-    // registers, so the offsets stay fixed for the whole loop.
-    const bool direct_ok =
-        ((int64_t)(T::BM - 1) * p.lda + T::BK) * 4 < (int64_t)kOutOfRange &&
-        ((int64_t)(T::BK - 1) * p.ldb + T::BN) * 4 < (int64_t)kOutOfRange &&
-        (full_mn || (p.N % 4 == 0));
+    // Direct staging needs 31-bit descriptor spans and, for an operand staged
+    // [k][mn], whole quads along its m or n edge; a partial K slice (the last
+    // one when BK does not divide K) goes through registers, so the offsets
+    // stay fixed for the whole loop.
+    const bool direct_ok = a_span64 * 4 < (int64_t)kOutOfRange &&
+                           b_span64 * 4 < (int64_t)kOutOfRange &&
+                           (T::A_KC || rows_left >= T::BM || p.M % 4 == 0) &&
+                           (T::B_KC || cols_left >= T::BN || p.N % 4 == 0);
     const int full_slices = p.K / T::BK;
 
     make_offsets(T::BK);
@@ -294,35 +364,57 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
 #pragma unroll
             for (int r = 0; r < Op::ACC; ++r) acc[mi][ni][r] = 0.0f;
 
+    // Row (k-contiguous) or column ([k][mn]) of this lane in each MFMA tile.
+    // The swizzle of a k-contiguous row is the same for every tile of the
+    // wave (tiles are MI rows apart); a [k][mn] column carries the row-block
+    // flip of the k values this lane reads (all with k / KPL = kgrp * LG + lg).
     const int a_row = wy * T::WTM + li;
     const int a_swz = T::swz(a_row);
-    // B column of this lane in each column tile, with the row-block flip
-    // applied (every k this lane reads has k / KPL = lg).
+    const int b_row = wx * T::WTN + li;
+    const int b_swz = T::swz(b_row);
+    const int kflip = 4 * T::flip(kgrp * T::KSUB + lg * T::KPL);
+    int a_col[T::TM];
+#pragma unroll
+    for (int mi = 0; mi < T::TM; ++mi) a_col[mi] = (wy * T::WTM + T::MI * mi + li) ^ kflip;
     int b_col[T::TN];
 #pragma unroll
-    for (int ni = 0; ni < T::TN; ++ni)
-        b_col[ni] = (wx * T::WTN + T::MI * ni + li) ^ (4 * T::flip(kgrp * T::KSUB + lg * T::KPL));
+    for (int ni = 0; ni < T::TN; ++ni) b_col[ni] = (wx * T::WTN + T::MI * ni + li) ^ kflip;
 
     // One operand group = KG consecutive k steps: one 16-byte quad of A per
     // row tile and KG values of B per column tile.  The operands of group g+1
     // are read before the MFMAs of group g are issued ("Tiling Hierarchy on
     // GPUs", "Register prefetching").
-    auto read_group = [&](int buf, int g, f32x4 (&a)[T::TM], float (&b)[T::TN][T::KG]) {
+    using AReg = typename T::AReg;
+    using BReg = typename T::BReg;
+    auto read_group = [&](int buf, int g, AReg (&a)[T::TM], BReg (&b)[T::TN]) {
         const float* const As = smem + buf * T::BUF_FLOATS;
-        const float* const Bl =
-            As + T::A_FLOATS + (kgrp * T::KSUB + lg * T::KPL + g * T::KG) * T::LDB;
-        const int quad = kgrp * (T::KSUB / 4) + lg * (T::KPL / 4) + g;
+        const float* const Bs = As + T::A_FLOATS;
+        const int krow = kgrp * T::KSUB + lg * T::KPL + g * T::KG;  // first k of the group
+        const int quad = krow / 4;
+        if constexpr (T::A_KC) {
 #pragma unroll
-        for (int mi = 0; mi < T::TM; ++mi)
-            a[mi] = *(const f32x4*)(As + (a_row + T::MI * mi) * T::BK + ((quad ^ a_swz) << 2));
+            for (int mi = 0; mi < T::TM; ++mi)
+                a[mi] = *(const f32x4*)(As + (a_row + T::MI * mi) * T::BK + ((quad ^ a_swz) << 2));
+        } else {
 #pragma unroll
-        for (int s = 0; s < T::KG; ++s)
+            for (int s = 0; s < T::KG; ++s)
 #pragma unroll
-            for (int ni = 0; ni < T::TN; ++ni) b[ni][s] = Bl[s * T::LDB + b_col[ni]];
+                for (int mi = 0; mi < T::TM; ++mi)
+                    a[mi][s] = As[(krow + s) * T::LDA_S + a_col[mi]];
+        }
+        if constexpr (T::B_KC) {
+#pragma unroll
+            for (int ni = 0; ni < T::TN; ++ni)
+                b[ni] = *(const f32x4*)(Bs + (b_row + T::MI * ni) * T::BK + ((quad ^ b_swz) << 2));
+        } else {
+#pragma unroll
+            for (int s = 0; s < T::KG; ++s)
+#pragma unroll
+                for (int ni = 0; ni < T::TN; ++ni) b[ni][s] = Bs[(krow + s) * T::LDB + b_col[ni]];
+        }
     };
 
-    auto mfma_steps = [&](const f32x4 (&a)[T::TM], const float (&b)[T::TN][T::KG], int s0,
-                          int s1) {
+    auto mfma_steps = [&](const AReg (&a)[T::TM], const BReg (&b)[T::TN], int s0, int s1) {
 #pragma unroll
         for (int s = s0; s < s1; ++s)
 #pragma unroll
@@ -332,8 +424,8 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
                     acc[mi][ni] = Op::mma(a[mi][s], b[ni][s], acc[mi][ni]);
     };
 
-    f32x4 opa[2][T::TM];
-    float opb[2][T::TN][T::KG];
+    AReg opa[2][T::TM];
+    BReg opb[2][T::TN];
 
     // One slice held in LDS buffer `buf` (operand group g uses set g & 1):
     // the copy of slice s + STAGES - 1 is started first, into the buffer that
@@ -425,20 +517,44 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     }
 
     // Epilogue: accumulator r of lane (li, lg) in MFMA tile (mi, ni) is row
-    // Op::row(r, lg) and column li of that tile.
+    // Op::row(r, lg) and column li of that tile.  The general form stores
+    // alpha * acc, plus beta * C when beta != 0 (C is not read otherwise); the
+    // choice is made once, outside the store loop.
+    auto store = [&](auto read_c_tag, auto masked_tag) {
+        constexpr bool read_c = decltype(read_c_tag)::value;
+        constexpr bool masked = decltype(masked_tag)::value;
 #pragma unroll
-    for (int mi = 0; mi < T::TM; ++mi) {
+        for (int mi = 0; mi < T::TM; ++mi) {
 #pragma unroll
-        for (int ni = 0; ni < T::TN; ++ni) {
-            const int col = wx * T::WTN + T::MI * ni + li;
+            for (int ni = 0; ni < T::TN; ++ni) {
+                const int col = wx * T::WTN + T::MI * ni + li;
 #pragma unroll
-            for (int r = 0; r < Op::ACC; ++r) {
-                const int row = wy * T::WTM + T::MI * mi + Op::row(r, lg);
-                if (full_mn || (row < rows_left && col < cols_left))
-                    C[(int64_t)row * p.ldc + col] = acc[mi][ni][r];
+                for (int r = 0; r < Op::ACC; ++r) {
+                    const int row = wy * T::WTM + T::MI * mi + Op::row(r, lg);
+                    if (!masked || (row < rows_left && col < cols_left)) {
+                        float* const c = C + (int64_t)row * p.ldc + col;
+                        if constexpr (!T::EX) {
+                            *c = acc[mi][ni][r];
+                        } else if constexpr (read_c) {
+                            *c = __builtin_fmaf(p.beta, *c, p.alpha * acc[mi][ni][r]);
+                        } else {
+                            *c = p.alpha * acc[mi][ni][r];
+                        }
+                    }
+                }
             }
         }
-    }
+    };
+    auto store_tile = [&](auto read_c_tag) {
+        if (full_mn)
+            store(read_c_tag, std::false_type());
+        else
+            store(read_c_tag, std::true_type());
+    };
+    if (T::EX && p.beta != 0.0f)
+        store_tile(std::true_type());
+    else
+        store_tile(std::false_type());
 }
 
 template <class T>

@@ -68,13 +68,28 @@ struct ConfigEntry {
     // control build that is never chosen.
     int per_cu;
     double one_a, one_b, two_a, two_b;
+    // General form C = alpha op(A) op(B) + beta C, by operand layout
+    // (transA + 2 * transB); NULL where this tile is not built for it.
+    const void* general[4];
 };
+
+// The same tile with stored-operand layouts and the alpha/beta epilogue.
+template <class T, bool TA, bool TB>
+using DlGeneral = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::OCC, T::GROUP_M,
+                         T::STAGES, T::KSPLIT, T::SWIZZLE, TA, TB, true>;
 
 #define SGEMM_CFG(T, name, per_cu, a1, b1, a2, b2) \
     { name, T::BM, T::BN, T::BK, T::NT, (const void*)&sgemm_mfma_kernel<T>, per_cu, a1, b1, a2, b2 }
 #define SGEMM_DL_CFG(T, name, per_cu, a1, b1, a2, b2)                                        \
     { name, T::BM, T::BN, T::BK, T::NT, (const void*)&sgemm_mfma_dl_kernel<T>, per_cu, a1, b1, \
       a2, b2 }
+#define SGEMM_DLX_CFG(T, name, per_cu, a1, b1, a2, b2)                                       \
+    { name, T::BM, T::BN, T::BK, T::NT, (const void*)&sgemm_mfma_dl_kernel<T>, per_cu, a1, b1, \
+      a2, b2,                                                                                 \
+      { (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, false, false>>,                       \
+        (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, false>>,                        \
+        (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, false, true>>,                        \
+        (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, true>> } }
 
 const ConfigEntry kConfigs[] = {
     SGEMM_CFG(Cfg256x128, "mfma32_256x128x16_w2x2", 1, 3.8386e-04, 4.2165e-06, 3.9847e-04, 8.1269e-06),
@@ -87,25 +102,26 @@ const ConfigEntry kConfigs[] = {
     SGEMM_CFG(Cfg64x64k32m16, "mfma16_64x64x32_w2x2", 2, 6.9501e-04, 6.4427e-06, 1.0260e-03, 9.8135e-06),
     SGEMM_CFG(Cfg256x256m32w1, "mfma32_256x256x16_w2x2", 1, 2.0224e-04, 3.9503e-06, 3.9565e-04, 7.8758e-06),
     SGEMM_CFG(Cfg256x256k32m32w1, "mfma32_256x256x32_w2x2", 1, 2.2312e-04, 3.9043e-06, 4.1389e-04, 7.8000e-06),
-    SGEMM_DL_CFG(Dl256x256k32m32, "dl32_256x256x32_w2x4", 1, 2.1036e-04, 3.4720e-06, 3.7595e-04, 6.9415e-06),
+    SGEMM_DLX_CFG(Dl256x256k32m32, "dl32_256x256x32_w2x4", 1, 2.1036e-04, 3.4720e-06, 3.7595e-04, 6.9415e-06),
     SGEMM_DL_CFG(Dl256x256k16m32, "dl32_256x256x16_w2x4", 1, 2.0071e-04, 3.4849e-06, 3.6338e-04, 6.9601e-06),
     SGEMM_DL_CFG(Dl256x128k32m32, "dl32_256x128x32_w2x2", 1, 3.5631e-04, 3.7684e-06, 5.3476e-04, 7.5500e-06),
-    SGEMM_DL_CFG(Dl128x128k32m32, "dl32_128x128x32_w2x2", 2, 4.3123e-04, 3.9272e-06, 5.4574e-04, 6.9695e-06),
+    SGEMM_DLX_CFG(Dl128x128k32m32, "dl32_128x128x32_w2x2", 2, 4.3123e-04, 3.9272e-06, 5.4574e-04, 6.9695e-06),
     SGEMM_DL_CFG(Dl256x256k32m32Plain, "dl32_256x256x32_w2x4_unswizzled", 0, 0, 0, 0, 0),
     SGEMM_DL_CFG(Dl128x128k32m32s4, "dl32_128x128x32_w2x2_s4", 1, 4.5364e-04, 4.1307e-06, 6.7966e-04, 8.2867e-06),
-    SGEMM_DL_CFG(Dl64x64k32m32s4, "dl32_64x64x32_w2x2_s4", 2, 8.8462e-04, 5.0915e-06, 1.1556e-03, 7.6853e-06),
-    SGEMM_DL_CFG(Dl256x192k32m32, "dl32_256x192x32_w4x2", 1, 2.1452e-04, 3.5334e-06, 3.5426e-04, 7.0652e-06),
-    SGEMM_DL_CFG(Dl192x256k32m32, "dl32_192x256x32_w2x4", 1, 2.1940e-04, 3.4913e-06, 3.5898e-04, 6.9860e-06),
+    SGEMM_DLX_CFG(Dl64x64k32m32s4, "dl32_64x64x32_w2x2_s4", 2, 8.8462e-04, 5.0915e-06, 1.1556e-03, 7.6853e-06),
+    SGEMM_DLX_CFG(Dl256x192k32m32, "dl32_256x192x32_w4x2", 1, 2.1452e-04, 3.5334e-06, 3.5426e-04, 7.0652e-06),
+    SGEMM_DLX_CFG(Dl192x256k32m32, "dl32_192x256x32_w2x4", 1, 2.1940e-04, 3.4913e-06, 3.5898e-04, 6.9860e-06),
     SGEMM_DL_CFG(Dl64x64k64m32s4, "dl32_64x64x64_w2x2_s4", 1, 9.1894e-04, 4.9619e-06, 1.4383e-03, 9.9365e-06),
     SGEMM_DL_CFG(Dl64x64k32m32s8, "dl32_64x64x32_w2x2_s8", 1, 1.0063e-03, 5.0706e-06, 1.6064e-03, 1.0141e-05),
     SGEMM_DL_CFG(Dl128x64k32m32s4, "dl32_128x64x32_w2x2_s4", 1, 6.1517e-04, 4.5946e-06, 9.0588e-04, 9.2191e-06),
     SGEMM_DL_CFG(Dl128x128k64m32s2, "dl32_128x128x64_w2x2", 1, 4.9542e-04, 3.9598e-06, 7.7019e-04, 7.9307e-06),
-    SGEMM_DL_CFG(Dl64x64k64m32s4x2, "dl32_64x64x64_w2x2_s4_k2", 1, 1.0666e-03, 4.1455e-06, 1.7638e-03, 8.2600e-06),
+    SGEMM_DLX_CFG(Dl64x64k64m32s4x2, "dl32_64x64x64_w2x2_s4_k2", 1, 1.0666e-03, 4.1455e-06, 1.7638e-03, 8.2600e-06),
     SGEMM_DL_CFG(Dl64x64k32m32s4x2, "dl32_64x64x32_w2x2_s4_k2", 2, 9.7944e-04, 5.1438e-06, 1.4432e-03, 8.2780e-06),
-    SGEMM_DL_CFG(Dl128x64k64m32s2x2, "dl32_128x64x64_w2x2_s2_k2", 1, 6.7196e-04, 3.8131e-06, 1.0361e-03, 7.6395e-06),
+    SGEMM_DLX_CFG(Dl128x64k64m32s2x2, "dl32_128x64x64_w2x2_s2_k2", 1, 6.7196e-04, 3.8131e-06, 1.0361e-03, 7.6395e-06),
 };
 #undef SGEMM_CFG
 #undef SGEMM_DL_CFG
+#undef SGEMM_DLX_CFG
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 constexpr int kNumCu = 256;  // MI355X compute units
 
@@ -129,13 +145,23 @@ int64_t span_end(int64_t rows, int64_t cols, int64_t ld, int64_t stride, int64_t
     return boff;
 }
 
-int validate(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, int64_t strideA,
-             const float* B, int64_t ldb, int64_t strideB, const float* C, int64_t ldc,
-             int64_t strideC, int64_t batch) {
+// Argument checks for C = alpha op(A) op(B) + beta C; the plain product is
+// transA = transB = 0 with alpha = 1 (A and B needed whenever K > 0).  A is
+// stored M x K (lda >= K) or, transposed, K x M (lda >= M); B is stored K x N
+// (ldb >= N) or N x K (ldb >= K).
+int validate_general(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+                     const float* A, int64_t lda, int64_t strideA, const float* B, int64_t ldb,
+                     int64_t strideB, const float* C, int64_t ldc, int64_t strideC,
+                     int64_t batch) {
+    if ((transA != 0 && transA != 1) || (transB != 0 && transB != 1))
+        return SGEMM_STATUS_INVALID_OP;
     if (M < 0 || N < 0 || K < 0 || batch < 0) return SGEMM_STATUS_INVALID_SIZE;
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim || batch > kMaxDim)
         return SGEMM_STATUS_SIZE_OVERFLOW;
-    if (lda < (K > 1 ? K : 1) || ldb < (N > 1 ? N : 1) || ldc < (N > 1 ? N : 1))
+    const int64_t a_rows = transA ? K : M, a_cols = transA ? M : K;
+    const int64_t b_rows = transB ? N : K, b_cols = transB ? K : N;
+    if (lda < (a_cols > 1 ? a_cols : 1) || ldb < (b_cols > 1 ? b_cols : 1) ||
+        ldc < (N > 1 ? N : 1))
         return SGEMM_STATUS_INVALID_LD;
     if (strideA < 0 || strideB < 0 || strideC < 0) return SGEMM_STATUS_INVALID_STRIDE;
     if (M == 0 || N == 0 || batch == 0) return SGEMM_STATUS_SUCCESS;
@@ -145,11 +171,20 @@ int validate(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, int64
         if (strideC < one_c) return SGEMM_STATUS_INVALID_STRIDE;
     }
     if (C == nullptr) return SGEMM_STATUS_NULL_POINTER;
-    if (K > 0 && (A == nullptr || B == nullptr)) return SGEMM_STATUS_NULL_POINTER;
-    if (span_end(M, K, lda, strideA, batch) < 0 || span_end(K, N, ldb, strideB, batch) < 0 ||
+    const bool reads_ab = K > 0 && alpha != 0.0f;
+    if (reads_ab && (A == nullptr || B == nullptr)) return SGEMM_STATUS_NULL_POINTER;
+    if (span_end(a_rows, a_cols, lda, strideA, batch) < 0 ||
+        span_end(b_rows, b_cols, ldb, strideB, batch) < 0 ||
         span_end(M, N, ldc, strideC, batch) < 0)
         return SGEMM_STATUS_SIZE_OVERFLOW;
     return SGEMM_STATUS_SUCCESS;
+}
+
+int validate(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, int64_t strideA,
+             const float* B, int64_t ldb, int64_t strideB, const float* C, int64_t ldc,
+             int64_t strideC, int64_t batch) {
+    return validate_general(0, 0, M, N, K, 1.0f, A, lda, strideA, B, ldb, strideB, C, ldc,
+                            strideC, batch);
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -169,13 +204,14 @@ double predict_us(const ConfigEntry& c, int64_t M, int64_t N, int64_t K, int64_t
 }
 
 // Shape -> configuration: the smallest predicted time; control builds are
-// never chosen.
-int choose_config(int64_t M, int64_t N, int64_t K, int64_t batch) {
+// never chosen.  `general` restricts the choice to tiles built for the
+// general form (every layout is built for the same tiles).
+int choose_config(int64_t M, int64_t N, int64_t K, int64_t batch, bool general = false) {
     int best = -1;
     double best_us = 0.0;
     for (int idx = 0; idx < kNumConfigs; ++idx) {
         const ConfigEntry& c = kConfigs[idx];
-        if (c.per_cu == 0) continue;
+        if (c.per_cu == 0 || (general && c.general[0] == nullptr)) continue;
         const double t = predict_us(c, M, N, K, batch);
         if (best < 0 || t < best_us * (1.0 - 1e-9)) {
             best_us = t;
@@ -188,7 +224,7 @@ int choose_config(int64_t M, int64_t N, int64_t K, int64_t batch) {
 int launch_gemm(const void* kernel, int bm, int bn, int threads, int64_t M, int64_t N, int64_t K,
                 const float* A, int64_t lda, int64_t strideA, const float* B, int64_t ldb,
                 int64_t strideB, float* C, int64_t ldc, int64_t strideC, int64_t batch,
-                hipStream_t stream) {
+                hipStream_t stream, float alpha = 1.0f, float beta = 0.0f) {
     if (K == 0) {
         const int64_t total = M * N * batch;
         int64_t blocks = ceil_div(total, 256);
@@ -228,6 +264,8 @@ int launch_gemm(const void* kernel, int bm, int bn, int threads, int64_t M, int6
         p.tiles_n = (int)tiles_n;
         p.batch_base = (int)b0;
         p.batch_count = (int)nb;
+        p.alpha = alpha;
+        p.beta = beta;
         void* args[] = {&p};
         hipError_t e = hipLaunchKernel(kernel, dim3((unsigned)(per_matrix * nb)), dim3(threads),
                                        args, 0, stream);
@@ -246,6 +284,40 @@ int run_mfma(int config, int64_t M, int64_t N, int64_t K, const float* A, int64_
     const ConfigEntry& c = kConfigs[config];
     return launch_gemm(c.kernel, c.bm, c.bn, c.threads, M, N, K, A, lda, strideA, B, ldb,
                        strideB, C, ldc, strideC, batch, stream);
+}
+
+// C = beta * C over the M x N windows (+0 when beta == 0, C not read).
+int launch_scale(int64_t M, int64_t N, float* C, int64_t ldc, int64_t strideC, int64_t batch,
+                 float beta, hipStream_t stream) {
+    int64_t blocks = ceil_div(M * N * batch, 256);
+    if (blocks > 65536) blocks = 65536;
+    int Mi = (int)M, Ni = (int)N, bi = (int)batch;
+    void* args[] = {&C, &ldc, &strideC, &Mi, &Ni, &bi, &beta};
+    hipError_t e = hipLaunchKernel((const void*)&scale_kernel, dim3((unsigned)blocks), dim3(256),
+                                   args, 0, stream);
+    return e == hipSuccess ? SGEMM_STATUS_SUCCESS : SGEMM_STATUS_LAUNCH_FAILED;
+}
+
+int run_general(int config, int transA, int transB, int64_t M, int64_t N, int64_t K,
+                float alpha, const float* A, int64_t lda, int64_t strideA, const float* B,
+                int64_t ldb, int64_t strideB, float beta, float* C, int64_t ldc,
+                int64_t strideC, int64_t batch, hipStream_t stream) {
+    const int st = validate_general(transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb,
+                                    strideB, C, ldc, strideC, batch);
+    if (st != SGEMM_STATUS_SUCCESS) return st;
+    const int layout = transA + 2 * transB;
+    if (config >= 0 && (config >= kNumConfigs || kConfigs[config].general[layout] == nullptr))
+        return SGEMM_STATUS_INVALID_CONFIG;
+    if (M == 0 || N == 0 || batch == 0) return SGEMM_STATUS_SUCCESS;
+    if (K == 0 || alpha == 0.0f) {
+        // No product term: C = beta * C (nothing to do for beta == 1).
+        if (beta == 1.0f) return SGEMM_STATUS_SUCCESS;
+        return launch_scale(M, N, C, ldc, strideC, batch, beta, stream);
+    }
+    if (config < 0) config = choose_config(M, N, K, batch, true);
+    const ConfigEntry& c = kConfigs[config];
+    return launch_gemm(c.general[layout], c.bm, c.bn, c.threads, M, N, K, A, lda, strideA, B,
+                       ldb, strideB, C, ldc, strideC, batch, stream, alpha, beta);
 }
 
 int run_valu(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, int64_t strideA,
@@ -317,6 +389,42 @@ int sgemm_select_config(int64_t M, int64_t N, int64_t K, int64_t batch) {
         return SGEMM_STATUS_SIZE_OVERFLOW;
     if (M == 0 || N == 0 || batch == 0) return 0;
     return choose_config(M, N, K, batch);
+}
+
+int sgemm_ex(int transA, int transB, int64_t M, int64_t N, int64_t K, float alpha,
+             const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+             int64_t ldc, hipStream_t stream) {
+    return run_general(-1, transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, beta, C, ldc,
+                       0, 1, stream);
+}
+
+int sgemm_ex_strided_batched(int transA, int transB, int64_t M, int64_t N, int64_t K,
+                             float alpha, const float* A, int64_t lda, int64_t strideA,
+                             const float* B, int64_t ldb, int64_t strideB, float beta, float* C,
+                             int64_t ldc, int64_t strideC, int64_t batch, hipStream_t stream) {
+    return run_general(-1, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb, strideB,
+                       beta, C, ldc, strideC, batch, stream);
+}
+
+int sgemm_ex_with_config(int config, int transA, int transB, int64_t M, int64_t N, int64_t K,
+                         float alpha, const float* A, int64_t lda, int64_t strideA,
+                         const float* B, int64_t ldb, int64_t strideB, float beta, float* C,
+                         int64_t ldc, int64_t strideC, int64_t batch, hipStream_t stream) {
+    if (config < 0 || config >= kNumConfigs) return SGEMM_STATUS_INVALID_CONFIG;
+    return run_general(config, transA, transB, M, N, K, alpha, A, lda, strideA, B, ldb,
+                       strideB, beta, C, ldc, strideC, batch, stream);
+}
+
+int sgemm_config_has_general_form(int config) {
+    if (config < 0 || config >= kNumConfigs) return SGEMM_STATUS_INVALID_CONFIG;
+    return kConfigs[config].general[0] != nullptr ? 1 : 0;
+}
+
+int sgemm_select_general_config(int64_t M, int64_t N, int64_t K, int64_t batch) {
+    if (M < 0 || N < 0 || K < 0 || batch < 0) return SGEMM_STATUS_INVALID_SIZE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim || batch > kMaxDim)
+        return SGEMM_STATUS_SIZE_OVERFLOW;
+    return choose_config(M, N, K, batch, true);
 }
 
 int sgemm_config_selectable(int config) {
@@ -397,6 +505,7 @@ const char* sgemm_status_string(int status) {
         case SGEMM_STATUS_INVALID_STRIDE: return "invalid batch stride";
         case SGEMM_STATUS_LAUNCH_FAILED: return "kernel launch failed";
         case SGEMM_STATUS_INVALID_CONFIG: return "unknown tile configuration";
+        case SGEMM_STATUS_INVALID_OP: return "invalid transpose flag (must be 0 or 1)";
         default: return "unknown status";
     }
 }

@@ -143,3 +143,26 @@ def workload_operands(w: Workload, pad: float = float("nan")):
     return operands(w.M, w.N, w.K, w.lda, w.ldb, w.seed, w.dist_a, w.dist_b,
                     w.scale_a, w.scale_b, pad, batch=w.batch, strideA=w.strideA,
                     strideB=w.strideB)
+
+
+def stored_operands(transA: bool, transB: bool, M: int, N: int, K: int, lda: int, ldb: int,
+                    seed: int, dist_a: str = "uniform", dist_b: str | None = None,
+                    pad: float = float("nan")):
+    """Flat float32 CPU buffers (A, B) as stored for the general form: A is
+    M x K, or K x M when transA; B is K x N, or N x K when transB.  A is drawn
+    before B."""
+    dist_b = dist_a if dist_b is None else dist_b
+    gen = torch.Generator("cpu").manual_seed(seed)
+    ra, ca = (K, M) if transA else (M, K)
+    rb, cb = (N, K) if transB else (K, N)
+    A = place(draw(gen, ra * ca, dist_a), ra, ca, lda, pad)
+    B = place(draw(gen, rb * cb, dist_b), rb, cb, ldb, pad)
+    return A, B
+
+
+def matrix(rows: int, cols: int, ld: int, seed: int, dist: str = "uniform",
+           pad: float = float("nan")) -> torch.Tensor:
+    """One flat float32 CPU buffer holding a rows x cols matrix (e.g. C's
+    initial values for beta != 0)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    return place(draw(gen, rows * cols, dist), rows, cols, ld, pad)
