@@ -64,6 +64,8 @@ def _load():
                                                 p, i64, p, i64, ctypes.c_float, p, i64, i64, p,
                                                 p, p, p]
     lib.oracle_sgemm_ex_entries_f64.restype = None
+    lib.oracle_window_sum_f64.argtypes = [i64, i64, p, p, p]
+    lib.oracle_window_sum_f64.restype = None
     lib.oracle_max_threads.argtypes = []
     lib.oracle_max_threads.restype = ctypes.c_int
     _lib = lib
@@ -227,3 +229,19 @@ def ex_entries_f64(transA: bool, transB: bool, K: int, alpha: float, A, lda: int
                                         lda, _ptr(b), ldb, beta, _ptr(c), ldc, r.size, _ptr(r),
                                         _ptr(cc), _ptr(out), _ptr(out_abs))
     return out, out_abs
+
+
+def window_sum_f64(n: int, W: int, x):
+    """y[i] = sum_{d<W} x[i+d] for i < n (the lecture's sliding window, see
+    oracle.c); returns FP64 (y, yabs).  x holds at least n + W - 1 floats."""
+    lib = _load()
+    xx = _f32_flat(x)
+    if n < 0 or W < 1:
+        raise ValueError("need n >= 0 and W >= 1")
+    if n > 0 and xx.size < n + W - 1:
+        raise ValueError("x holds fewer than n + W - 1 values")
+    y = np.empty(n, dtype=np.float64)
+    yabs = np.empty(n, dtype=np.float64)
+    if n > 0:
+        lib.oracle_window_sum_f64(n, W, _ptr(xx), _ptr(y), _ptr(yabs))
+    return y, yabs

@@ -216,6 +216,31 @@ void oracle_sgemm_ex_entries_f64(int transA, int transB, int64_t K, float alpha,
     }
 }
 
+/*
+ * Sliding window sums ("CMU DLSys Lecture 12: GPU Acceleration", section 3):
+ * y[i] = sum_{d=0}^{W-1} x[i+d] for 0 <= i < n, where n counts outputs and the
+ * input holds n + W - 1 valid elements (the lecture's five-wide case is
+ * W = 5; its general width is W = 2R + 1, and any W >= 1 is read the same
+ * way).  The terms are added for d = 0, 1, ..., W-1 in FP64 (exact for FP32
+ * inputs up to W ~ 2^29), and yabs[i] = sum_d |x[i+d]| is the scale of the
+ * acceptance bound.  yabs may be NULL.
+ */
+void oracle_window_sum_f64(int64_t n, int64_t W, const float *x, double *y, double *yabs) {
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t i = 0; i < n; ++i) {
+        double s = 0.0, sa = 0.0;
+        for (int64_t d = 0; d < W; ++d) {
+            const double v = (double)x[i + d];
+            s += v;
+            sa += fabs(v);
+        }
+        y[i] = s;
+        if (yabs) yabs[i] = sa;
+    }
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();

@@ -118,3 +118,25 @@ def valu_fma_instructions(M: int, N: int, K: int, BM: int = 128, BN: int = 128, 
     64-lane instruction per 64 FMAs, padded tiles included."""
     tiles = ceil_div(M, BM) * ceil_div(N, BN) * batch
     return tiles * BM * BN * ceil_div(K, BK) * BK // 64
+
+
+def window_independent_loads(n: int, W: int) -> int:
+    """Input reads of n window sums when every output loads its own W values
+    ("CMU DLSys Lecture 12", section 3: T(2R+1) for a block of T outputs)."""
+    return n * W
+
+
+def window_staged_loads(n: int, W: int, T: int) -> int:
+    """Input values staged by blocks of T outputs: each full block loads its T
+    outputs' span plus the W - 1 halo values (T + 2R with W = 2R + 1); a last
+    partial block of r outputs loads r + W - 1 (section 3)."""
+    if T <= 0:
+        raise ValueError("block size must be positive")
+    full, rest = divmod(n, T)
+    return full * (T + W - 1) + (rest + W - 1 if rest else 0)
+
+
+def window_bytes(n: int, W: int, elem: int = 4) -> int:
+    """Compulsory traffic of the window sum: the n + W - 1 inputs read once
+    and the n outputs written once."""
+    return elem * ((n + W - 1 if n > 0 else 0) + n)
