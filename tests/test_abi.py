@@ -169,3 +169,14 @@ def test_general_config_selection():
         assert c in general
         pred = {g: sg.predict_us(g, *shape) for g in general}
         assert pred[c] == min(pred.values())
+
+
+def test_window_sum_argument_errors():
+    lib = _native.lib()
+    assert lib.window_sum(-1, 5, FAKE, FAKE, 0) == -1
+    assert lib.window_sum(10, 0, FAKE, FAKE, 0) == -1
+    assert lib.window_sum(10, 1025, FAKE, FAKE, 0) == -1
+    assert lib.window_sum(10, 5, None, FAKE, 0) == -3
+    assert lib.window_sum(10, 5, FAKE, None, 0) == -3
+    assert lib.window_sum(2 ** 62, 5, FAKE, FAKE, 0) == -4     # more than 2^31 blocks
+    assert lib.window_sum(0, 5, None, None, 0) == 0            # nothing to do

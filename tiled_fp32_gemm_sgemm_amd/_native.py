@@ -12,7 +12,8 @@ import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libsgemm.so")
-HEADER = os.path.join(os.path.dirname(PKG), "include", "sgemm.h")
+INCLUDE = os.path.join(os.path.dirname(PKG), "include")
+HEADER = os.path.join(INCLUDE, "sgemm.h")
 
 STATUS = {
     0: "SGEMM_STATUS_SUCCESS",
@@ -71,6 +72,7 @@ _SIGS = {
          ctypes.c_int, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float)],
         ctypes.c_int),
     "sgemm_status_string": ([ctypes.c_int], ctypes.c_char_p),
+    "window_sum": ([_i64, _i64, _p, _p, _p], ctypes.c_int),
 }
 
 
@@ -95,8 +97,14 @@ def status_string(status: int) -> str:
     return lib().sgemm_status_string(int(status)).decode()
 
 
-def header_functions(path: str = HEADER):
-    """Names of the functions include/sgemm.h declares."""
-    text = open(path).read()
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sgemm\w*)\s*\(", text)))
+def header_functions(path: str | None = None):
+    """Names of the functions the headers under include/ declare (one header
+    when `path` is given)."""
+    paths = [path] if path else sorted(os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE)
+                                       if f.endswith(".h"))
+    names = set()
+    for p in paths:
+        text = re.sub(r"/\*.*?\*/", " ", open(p).read(), flags=re.S)
+        text = re.sub(r"#.*", " ", text)
+        names.update(re.findall(r"^\s*(?:const\s+)?\w+\s*\**\s*(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)

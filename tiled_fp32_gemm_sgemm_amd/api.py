@@ -259,3 +259,29 @@ def select_general_config(M: int, N: int, K: int, batch: int = 1) -> int:
     if st < 0:
         raise _native.SgemmError(st, "sgemm_select_general_config")
     return st
+
+
+def window_sum_raw(n: int, W: int, x_ptr: int, y_ptr: int, stream=0) -> int:
+    """y[i] = sum_{d<W} x[i+d], i < n, on device addresses; returns the status."""
+    return _native.lib().window_sum(n, W, x_ptr, y_ptr, stream)
+
+
+def window_sum(x, W: int, out=None, stream=None):
+    """Sliding window sums of a 1-D float32 CUDA tensor x: n = len(x) - W + 1
+    outputs (x[i] + ... + x[i+W-1])."""
+    import torch
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.float32 or x.device.type != "cuda":
+        raise TypeError("x must be a float32 CUDA tensor")
+    if x.dim() != 1 or (x.numel() > 1 and x.stride(0) != 1):
+        raise ValueError("x must be a contiguous 1-D tensor")
+    n = x.numel() - W + 1
+    if W < 1 or n < 0:
+        raise ValueError("need 1 <= W <= len(x) + 1")
+    if out is None:
+        out = torch.empty(n, dtype=torch.float32, device=x.device)
+    if out.dim() != 1 or out.numel() != n or (n > 1 and out.stride(0) != 1):
+        raise ValueError("out must be a contiguous 1-D tensor of %d values" % n)
+    with torch.cuda.device(x.device):
+        st = window_sum_raw(n, W, x.data_ptr(), out.data_ptr(), _stream_handle(stream, x.device))
+    _check(st, "window_sum")
+    return out

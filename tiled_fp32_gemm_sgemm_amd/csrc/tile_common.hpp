@@ -111,34 +111,4 @@ __device__ __forceinline__ void stg4_masked(float* p, f32x4 v, int valid) {
     }
 }
 
-// C's window set to +0 (K == 0: every output is the empty sum).
-__global__ void zero_fill_kernel(float* C, int64_t ldc, int64_t strideC, int M, int N,
-                                 int batch) {
-    const int64_t total = (int64_t)M * N * batch;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-         e += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t b = e / ((int64_t)M * N);
-        const int64_t rem = e - b * (int64_t)M * N;
-        const int64_t i = rem / N;
-        const int64_t j = rem - i * N;
-        C[b * strideC + i * ldc + j] = 0.0f;
-    }
-}
-
-// C's window scaled by beta (the general form with K == 0 or alpha == 0:
-// the product term is zero).  beta == 0 writes +0 without reading C.
-__global__ void scale_kernel(float* C, int64_t ldc, int64_t strideC, int M, int N, int batch,
-                             float beta) {
-    const int64_t total = (int64_t)M * N * batch;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
-         e += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t b = e / ((int64_t)M * N);
-        const int64_t rem = e - b * (int64_t)M * N;
-        const int64_t i = rem / N;
-        const int64_t j = rem - i * N;
-        float* const c = C + b * strideC + i * ldc + j;
-        *c = beta == 0.0f ? 0.0f : beta * *c;
-    }
-}
-
 }  // namespace sgemm_dev

@@ -1,0 +1,89 @@
+// Sliding window sums y[i] = sum_{d<W} x[i+d], 0 <= i < n, with cooperative
+// staging ("CMU DLSys Lecture 12: GPU Acceleration", section 3: a block loads
+// the union of its outputs' windows -- its T outputs plus the W - 1 halo
+// values -- into shared memory once, synchronises, and every thread reads its
+// windows there; the input holds n + W - 1 valid values and the load guard is
+// against that count, not n).
+//
+// gfx950 shape of the same idea.  The work is a few additions per value, so
+// it is bound by HBM bandwidth (8 bytes per output), not by arithmetic:
+//  * A workgroup of 256 lanes owns T = 4096 consecutive outputs; lane t owns
+//    the quads of outputs 4t + 1024j (j = 0..3), so every 16-byte store of a
+//    wave covers 1 KB of y contiguously.
+//  * The block's T + W - 1 input values are copied straight into LDS with
+//    buffer_load_dwordx4 ... lds (1 KB per wave instruction, no VGPR staging).
+//    The buffer descriptor's range ends at the last valid input, so the
+//    buffer unit returns zeros past it: the lecture's guard against n + W - 1,
+//    done by the hardware.
+//  * Each lane sums its four outputs with a rolling window of four values:
+//    one LDS read per step d, and each output adds its terms in the order
+//    d = 0, 1, ..., W-1 like the definition.
+#pragma once
+
+#include "tile_common.hpp"
+
+namespace sgemm_dev {
+
+struct WindowTile {
+    static constexpr int NT = 256;                 // lanes per workgroup
+    static constexpr int QUADS = 4;                // output quads per lane
+    static constexpr int T = NT * 4 * QUADS;       // outputs per workgroup
+    static constexpr int MAX_W = 1024;             // widest window supported
+    static constexpr int CHUNK = 256;              // floats per direct-copy wave instruction
+    static constexpr int TILE = ((T + MAX_W - 1 + CHUNK - 1) / CHUNK) * CHUNK;  // LDS floats
+};
+
+typedef __attribute__((address_space(3))) void lds_void_w;
+
+__device__ __forceinline__ void window_sum_body(const float* x, float* y, int64_t n, int W) {
+    using WT = WindowTile;
+    __shared__ __attribute__((aligned(16))) float tile[WT::TILE];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % 64;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+    const int64_t base = (int64_t)blockIdx.x * WT::T;
+
+    // Inputs of this block: [base, base + T + W - 1), clipped to the n + W - 1
+    // valid values; everything past the clip reads as zero.
+    const int64_t valid = n + W - 1 - base;
+    const int64_t span = (int64_t)WT::T + W - 1;
+    const int count = (int)(valid < span ? valid : span);
+    const int chunks = (WT::T + W - 1 + WT::CHUNK - 1) / WT::CHUNK;
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(x + base), (short)0, count * 4, 0x00020000);
+    for (int c = wave; c < chunks; c += WT::NT / 64)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_w*)(tile + WT::CHUNK * c), 16,
+                                                 (WT::CHUNK * c + 4 * lane) * 4, 0, 0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+
+#pragma unroll
+    for (int j = 0; j < WT::QUADS; ++j) {
+        const int o = 4 * tid + WT::NT * 4 * j;  // first output of this quad, in the block
+        if (base + o >= n) break;
+        const float* const t = tile + o;
+        float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+        float r0 = t[0], r1 = t[1], r2 = t[2];
+        for (int d = 0; d < W; ++d) {
+            const float r3 = t[d + 3];
+            a0 += r0;
+            a1 += r1;
+            a2 += r2;
+            a3 += r3;
+            r0 = r1;
+            r1 = r2;
+            r2 = r3;
+        }
+        const f32x4 v = {a0, a1, a2, a3};
+        const int64_t left = n - (base + o);
+        stg4_masked(y + base + o, v, left >= 4 ? 4 : (int)left);
+    }
+}
+
+__global__ __launch_bounds__(WindowTile::NT) void window_sum_kernel(const float* x, float* y,
+                                                                    int64_t n, int W) {
+    window_sum_body(x, y, n, W);
+}
+
+}  // namespace sgemm_dev
