@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--path mfma|valu]
                     [--workload square4096] [--no-cpu-baseline]
+    python bench.py --workload window5      (sliding window sums, GB/s)
 
 One step is one call of the library on the named workload (default: the
 4096^3 product, A and B ~ normal(0,1)/sqrt(K), seed 1), inputs resident in
@@ -37,20 +38,27 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sgemm_mfma_square4096_counters.tx
 COPY_BYTES = 512 * 1024 * 1024   # larger than the 256 MB last-level cache
 
 
-def kernel_source_hash() -> str:
+# Sources each kernel family is compiled from (a counter summary is used only
+# while these hash to the value recorded in it).
+GEMM_SOURCES = ("sgemm.hip", "tile_common.hpp", "mfma_dl_kernel.hpp", "mfma_kernel.hpp",
+                "valu_kernel.hpp")
+WINDOW_SOURCES = ("window.hip", "window_kernel.hpp", "tile_common.hpp")
+WINDOW_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "window_sum_window5_counters.txt")
+
+
+def kernel_source_hash(names=GEMM_SOURCES) -> str:
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".hpp", ".h")):
-            h.update(name.encode())
-            with open(os.path.join(CSRC, name), "rb") as f:
-                h.update(f.read())
+    for name in sorted(names):
+        h.update(name.encode())
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(path: str, workload: str, kpath: str):
-    """HBM bytes per launch from the committed counter summary, or None when
-    it is missing or was taken on a different kernel source."""
-    if kpath != "mfma" or workload != "square4096" or not os.path.exists(path):
+def read_traffic(path: str, names=GEMM_SOURCES):
+    """HBM bytes per launch from a committed counter summary, or None when it
+    is missing or was taken on a different kernel source."""
+    if not os.path.exists(path):
         return None
     vals = {}
     with open(path) as f:
@@ -58,7 +66,7 @@ def read_traffic(path: str, workload: str, kpath: str):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash(names):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -90,9 +98,18 @@ def _mean(vals):
     return sum(vals) / len(vals) if vals else float("nan")
 
 
-def summarize_trace(stats_csv: str, out: str, command: str) -> None:
-    """Text summary of a rocprofv3 --kernel-trace --stats kernel_stats.csv."""
+def summarize_trace(stats_csv: str, out: str, command: str, trace_csv: str = None,
+                    timed: int = 0) -> None:
+    """Text summary of a rocprofv3 --kernel-trace --stats kernel_stats.csv.
+    With the kernel_trace.csv and the bench's timed step count, also the
+    average over the last `timed` dispatches of each kernel (the launches the
+    bench times; the others are its warm-up)."""
     rows = _read_csv(stats_csv)
+    per_kernel = {}
+    if trace_csv:
+        for r in sorted(_read_csv(trace_csv), key=lambda r: int(r["Dispatch_Id"])):
+            per_kernel.setdefault(r["Kernel_Name"], []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines = ["# rocprofv3 kernel statistics (durations in microseconds)",
              "# command: " + command, ""]
     for r in rows:
@@ -103,6 +120,10 @@ def summarize_trace(stats_csv: str, out: str, command: str) -> None:
         lines.append("  calls: %d  average_us: %.2f  min_us: %.2f  max_us: %.2f  percent: %s"
                      % (calls, avg_us, float(r.get("MinNs", 0)) / 1e3,
                         float(r.get("MaxNs", 0)) / 1e3, r.get("Percentage", "")))
+        durs = per_kernel.get(name, [])
+        if timed and len(durs) >= timed:
+            lines.append("  timed_average_us (last %d dispatches): %.2f"
+                         % (timed, sum(durs[-timed:]) / timed))
     open(out, "w").write("\n".join(lines) + "\n")
 
 
@@ -111,14 +132,16 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
     """Counter summary: utilisation, instruction counts against the closed
     forms, LDS bank conflicts and HBM traffic scaled by a copy kernel of known
     size (FETCH_SIZE / WRITE_SIZE in KiB per dispatch)."""
-    from workloads import WORKLOADS
+    from workloads import WINDOW_WORKLOADS, WORKLOADS
     from tiled_fp32_gemm_sgemm_amd import model
     import tiled_fp32_gemm_sgemm_amd as sg
-    w = WORKLOADS[workload]
+    window = workload in WINDOW_WORKLOADS
+    w = WINDOW_WORKLOADS[workload] if window else WORKLOADS[workload]
     L = ["# rocprofv3 hardware counters, %s path, workload %s" % (path, w.describe()),
          "# commands (one counter pass each, run from the repository root):"]
     L += ["#   " + c for c in commands]
-    L.append("kernel_source_sha256_16: %s" % kernel_source_hash())
+    L.append("kernel_source_sha256_16: %s" % kernel_source_hash(
+        WINDOW_SOURCES if window else GEMM_SOURCES))
     copy_part = "MulFunctor"
     fetch = _per_dispatch(_read_csv(fetch_csv), kernel_part) if fetch_csv else {}
     write = _per_dispatch(_read_csv(write_csv), kernel_part) if write_csv else {}
@@ -140,7 +163,8 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
               "hbm_read_bytes_per_launch: %.0f" % (f_kib * 1024 * f_scale),
               "hbm_write_bytes_per_launch: %.0f" % (w_kib * 1024 * w_scale),
               "hbm_bytes_per_launch: %.0f" % hbm,
-              "compulsory_bytes: %d" % model.compulsory_bytes(w.M, w.N, w.K, w.batch)]
+              "compulsory_bytes: %d" % (w.bytes if window else
+                                        model.compulsory_bytes(w.M, w.N, w.K, w.batch))]
     merged = {}
     for c in sq_csvs:
         for d in _per_dispatch(_read_csv(c), kernel_part).values():
@@ -160,7 +184,7 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
     if "_util" in merged:
         L.append("mfma_busy_fraction: %.4f" % _mean(merged["_util"]))
         L.append("effective_clock_ghz_under_profiler: %.3f" % (_mean(merged["_clk"]) / 1e9))
-    if path == "mfma":
+    if path == "mfma" and not window:
         cfg = sg.select_config(w.M, w.N, w.K, w.batch) if config is None else config
         info = sg.config_info(cfg)
         mi = 16 if info["name"].startswith("mfma16") else 32
@@ -203,12 +227,105 @@ def cpu_baseline(w, A, B, target_s: float = 12.0):
             "seconds": dt}
 
 
+def window_cpu_baseline(w, x_cpu):
+    """The oracle, untouched, over the whole window workload (one pass)."""
+    import oracle
+    x = x_cpu.numpy()
+    t0 = time.perf_counter()
+    oracle.window_sum_f64(w.n, w.W, x)
+    dt = time.perf_counter() - t0
+    return {"value": w.bytes / dt / 1e9, "unit": "GB/s", "cores": int(oracle.max_threads()),
+            "kind": "oracle",
+            "sample": "the whole workload (%d outputs, W = %d) in %.2f s, FP64 sums, OpenMP "
+                      "over outputs" % (w.n, w.W, dt),
+            "seconds": dt}
+
+
+def bench_window(args) -> int:
+    """Sliding window sums: algorithmic bytes (inputs once, outputs once) per
+    second, against the HBM roofline."""
+    import torch
+    from workloads import WINDOW_WORKLOADS, window_input
+    import tiled_fp32_gemm_sgemm_amd as sg
+
+    w = WINDOW_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x_cpu = window_input(w)
+    x = x_cpu.to(dev)
+    y = torch.empty(w.n, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream
+
+    def step():
+        st = sg.window_sum_raw(w.n, w.W, x.data_ptr(), y.data_ptr(), handle)
+        if st != 0:
+            raise sg.SgemmError(st, "window_sum")
+
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    def timed(fn, n_steps, n_warm):
+        for _ in range(n_warm):
+            fn()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(n_steps):
+            fn()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n_steps
+
+    ms = timed(step, args.steps, args.warmup)
+    gbs = w.bytes / (ms * 1e-3) / 1e9
+    comparators = {}
+    if not args.no_comparator:
+        # A plain device copy of the same bytes (n floats read, n written).
+        dst = torch.empty_like(y)
+        cms = timed(lambda: dst.copy_(x[:w.n]), max(5, args.steps // 2), 3)
+        comparators["copy"] = {"GB/s": 8.0 * w.n / (cms * 1e-3) / 1e9, "ms_per_step": cms}
+        del dst
+    traffic = (read_traffic(WINDOW_TRAFFIC_FILE, WINDOW_SOURCES)
+               if args.workload == "window5" else None)
+    out = {
+        "metric": "sliding window sum GB/s (inputs read once, outputs written once)",
+        "value": gbs,
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.describe(), "n": w.n, "W": w.W},
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": gbs / PEAK_HBM_GBS, "traffic": traffic,
+                     "kernel": "window_sum_kernel", "avg_kernel_ms": ms},
+        "cpu_baseline": None if args.no_cpu_baseline else window_cpu_baseline(w, x_cpu),
+        "comparators": comparators,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--path", choices=["mfma", "valu"], default="mfma")
+    ap.add_argument("--path", choices=["mfma", "valu", "window"], default="mfma",
+                    help="GEMM path (window: counter summaries of the window kernel only)")
     ap.add_argument("--workload", default="square4096")
     ap.add_argument("--config", type=int, default=None, help="force a matrix-core tile config")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -217,6 +334,9 @@ def main(argv=None) -> int:
                     help="first run a plain copy kernel of known size (counter scaling)")
     ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
                     help="write a text summary of a rocprofv3 kernel-stats csv to --out")
+    ap.add_argument("--trace-csv", help="kernel_trace.csv for --summarize-trace")
+    ap.add_argument("--timed", type=int, default=0,
+                    help="timed dispatches at the end of the trace (--summarize-trace)")
     ap.add_argument("--summarize-counters", action="store_true",
                     help="write a counter summary from --fetch-csv/--write-csv/--sq-csv to --out")
     ap.add_argument("--fetch-csv")
@@ -228,7 +348,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.summarize_trace:
-        summarize_trace(args.summarize_trace, args.out, " ".join(args.command))
+        summarize_trace(args.summarize_trace, args.out, " ".join(args.command), args.trace_csv,
+                        args.timed)
         return 0
     if args.summarize_counters:
         summarize_counters(args.out, args.workload, args.path, args.kernel_part, args.fetch_csv,
@@ -238,6 +359,15 @@ def main(argv=None) -> int:
     if args.gpus != 1:
         print("bench.py measures one GPU: this build runs on a single MI355X and has no "
               "multi-GPU path (asked for --gpus %d)" % args.gpus, file=sys.stderr)
+        return 2
+
+    from workloads import WINDOW_WORKLOADS
+    if args.workload in WINDOW_WORKLOADS:
+        return bench_window(args)
+
+    if args.path == "window":
+        print("--path window names the window kernel in counter summaries; run "
+              "--workload window5 to time it", file=sys.stderr)
         return 2
 
     import torch
@@ -299,7 +429,9 @@ def main(argv=None) -> int:
     else:
         tile = "valu_128x128x8_t8x8"
 
-    traffic = read_traffic(TRAFFIC_FILE, args.workload, args.path)
+    traffic = (read_traffic(TRAFFIC_FILE)
+               if args.path == "mfma" and args.workload == "square4096" and args.config is None
+               else None)
     roofline = {"bound": "mfma" if args.path == "mfma" else "alu",
                 "achieved": tflops,
                 "peak": PEAK_FP32_TFLOPS,

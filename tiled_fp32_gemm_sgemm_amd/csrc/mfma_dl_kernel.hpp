@@ -31,14 +31,17 @@
 //  * A slice As[m][k], BK floats per row, quad kq of row r stored at
 //    kq ^ ((r / rows_per_256_bytes) % (BK/4)) (as in mfma_kernel.hpp): the 16
 //    rows of a b128 pass hit 16 distinct quads of the bank row.
-//  * B slice Bs[k][n], BN floats per row.  With MI = 32 the 32 lanes of a
-//    ds_read_b32 pass read 32 consecutive floats of one k row: conflict-free
-//    with no padding.  With MI = 16 a pass covers two lane groups, 16 floats
-//    each, from rows KPL apart; the rows of odd lane groups are stored with
-//    their quads flipped by 4 (16 floats) so that the two halves land on
-//    disjoint banks.  The compiler still pairs reads of adjacent k rows into
-//    ds_read2_b32, and those conflict (measured), so the tile table uses
-//    MI = 32 only.
+//  * B slice Bs[k][n], BN floats per row, unpadded.  The output columns are
+//    interleaved over a wave's column tiles (DlTile::bcol): lane li of column
+//    tile ni owns column li * BV + ni % BV of each BV-tile run, so the BV
+//    values a lane needs at one k are adjacent and come in one ds_read_b64
+//    (BV = 2) or ds_read_b128 (BV = 4), and a pass reads one contiguous run of
+//    a k row, all 64 banks once.  Against one ds_read_b32 per column tile
+//    (BV = 1, same banks) this halves the B read instructions and lets the
+//    epilogue store BV adjacent outputs per lane at once: 1.8 % faster at
+//    4096^3 (same-process A/B).  With MI = 16 and BV = 1 a ds_read_b32 pass
+//    covers two lane groups from rows KPL apart; those rows are stored with
+//    their quads flipped by 4 (16 floats) so the halves use disjoint banks.
 //  * SWIZZLE = false stores A unswizzled: a control build whose A reads
 //    conflict, used to show that the bank-conflict counter sees the layout.
 #pragma once
@@ -66,7 +69,7 @@ struct F4 {
 
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MI_, int OCC_, int GROUP_M_,
           int STAGES_ = 2, int KSPLIT_ = 1, bool SWIZZLE_ = true, bool TA_ = false,
-          bool TB_ = false, bool EX_ = false>
+          bool TB_ = false, bool EX_ = false, bool BIL_ = true>
 struct DlTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -108,7 +111,21 @@ struct DlTile {
     static constexpr int B_CH = BK * BN / 256;           // 1 KB chunks per B slice
     static constexpr int A_CHW = A_CH / NW;              // chunks per wave
     static constexpr int B_CHW = B_CH / NW;
-    static constexpr int BFLIP = MI == 16 ? 4 : 0;       // quad flip on odd lane-group row blocks
+    // Column interleave of a B operand staged [k][n] (BIL): lane li of column
+    // tile ni owns output column (ni / BV) * MI * BV + li * BV + ni % BV of the
+    // wave tile, so the BV values a lane needs at one k are adjacent in LDS and
+    // come in one ds_read_b64 / ds_read_b128, and the lane's outputs in one row
+    // are BV adjacent columns (one vector store).  Each k row of a pass is then
+    // read as one contiguous run: 32 lanes x 8 bytes or 16 lanes x 16 bytes,
+    // all 64 banks once.  With MI = 16 only BV = 4 keeps a pass inside one k
+    // row; other widths keep BV = 1 and the row flip below.
+    static constexpr bool BIL = BIL_;
+    static constexpr int BV = (B_KC || !BIL) ? 1
+                              : MI == 16 ? (TN % 4 == 0 ? 4 : 1)
+                                         : (TN % 4 == 0 ? 4 : TN % 2 == 0 ? 2 : 1);
+    // Quad flip on odd lane-group row blocks of an operand staged [k][mn].
+    static constexpr int AFLIP = MI == 16 ? 4 : 0;
+    static constexpr int BFLIP = (MI == 16 && BV == 1) ? 4 : 0;
     // Register-staged fallback: quads per thread per slice.
     static constexpr int A_VEC = BM * BK / 4 / NT;
     static constexpr int B_VEC = BK * BN / 4 / NT;
@@ -124,12 +141,19 @@ struct DlTile {
     static_assert(STAGES >= 2 && LPS * (STAGES - 2) <= 63, "vmcnt holds at most 63");
     static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0, "fallback copy must split");
     static_assert(MI == 32 || (BN >= 32 && BM >= 32), "the flip needs 32-float rows");
+    static_assert(TN % BV == 0, "whole vectors of column tiles");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert((KSPLIT - 1) * BM * BN <= STAGES * BUF_FLOATS, "k-group exchange fits in LDS");
 
     static __device__ __forceinline__ int swz(int r) { return SWIZZLE ? (r / RPB) % QPR : 0; }
-    // Physical quad of logical quad nq in B row k is nq ^ flip(k).
-    static __device__ __forceinline__ int flip(int k) { return ((k / KPL) & 1) * BFLIP; }
+    // Physical quad of logical quad q in row k of an operand staged [k][mn] is
+    // q ^ flip(k).
+    static __device__ __forceinline__ int flipA(int k) { return ((k / KPL) & 1) * AFLIP; }
+    static __device__ __forceinline__ int flipB(int k) { return ((k / KPL) & 1) * BFLIP; }
+    // Wave-tile column of lane li in column tile ni (see BIL).
+    static __device__ __forceinline__ int bcol(int ni, int li) {
+        return (ni / BV) * MI * BV + li * BV + ni % BV;
+    }
     using AReg = std::conditional_t<A_KC, f32x4, F4>;
     using BReg = std::conditional_t<B_KC, f32x4, F4>;
 };
@@ -238,7 +262,7 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
                 const bool ok = r < rows_left && 4 * kq < kleft;
                 a_off[j] = ok ? (uint32_t)(((int64_t)r * p.lda + 4 * kq) * 4) : kOutOfRange;
             } else {
-                const int mq = (q % T::A_QPR) ^ T::flip(r);
+                const int mq = (q % T::A_QPR) ^ T::flipA(r);
                 const bool ok = r < kleft && 4 * mq < rows_left;
                 a_off[j] = ok ? (uint32_t)(((int64_t)r * p.lda + 4 * mq) * 4) : kOutOfRange;
             }
@@ -252,7 +276,7 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
                 const bool ok = r < cols_left && 4 * kq < kleft;
                 b_off[j] = ok ? (uint32_t)(((int64_t)r * p.ldb + 4 * kq) * 4) : kOutOfRange;
             } else {
-                const int nq = (q % T::B_QPR) ^ T::flip(r);
+                const int nq = (q % T::B_QPR) ^ T::flipB(r);
                 const bool ok = r < kleft && 4 * nq < cols_left;
                 b_off[j] = ok ? (uint32_t)(((int64_t)r * p.ldb + 4 * nq) * 4) : kOutOfRange;
             }
@@ -296,7 +320,7 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
                 x = ldg4_masked(A + (int64_t)r * p.lda + k0 + 4 * kq,
                                 r < rows_left ? p.K - (k0 + 4 * kq) : 0);
             } else {
-                const int mq = (q % T::A_QPR) ^ T::flip(r);
+                const int mq = (q % T::A_QPR) ^ T::flipA(r);
                 x = ldg4_masked(A + (int64_t)(k0 + r) * p.lda + 4 * mq,
                                 k0 + r < p.K ? rows_left - 4 * mq : 0);
             }
@@ -312,7 +336,7 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
                 x = ldg4_masked(B + (int64_t)r * p.ldb + k0 + 4 * kq,
                                 r < cols_left ? p.K - (k0 + 4 * kq) : 0);
             } else {
-                const int nq = (q % T::B_QPR) ^ T::flip(r);
+                const int nq = (q % T::B_QPR) ^ T::flipB(r);
                 x = ldg4_masked(B + (int64_t)(k0 + r) * p.ldb + 4 * nq,
                                 k0 + r < p.K ? cols_left - 4 * nq : 0);
             }
@@ -372,13 +396,17 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     const int a_swz = T::swz(a_row);
     const int b_row = wx * T::WTN + li;
     const int b_swz = T::swz(b_row);
-    const int kflip = 4 * T::flip(kgrp * T::KSUB + lg * T::KPL);
+    const int kfirst = kgrp * T::KSUB + lg * T::KPL;
+    const int kflip_a = 4 * T::flipA(kfirst);
+    const int kflip_b = 4 * T::flipB(kfirst);
     int a_col[T::TM];
 #pragma unroll
-    for (int mi = 0; mi < T::TM; ++mi) a_col[mi] = (wy * T::WTM + T::MI * mi + li) ^ kflip;
-    int b_col[T::TN];
+    for (int mi = 0; mi < T::TM; ++mi) a_col[mi] = (wy * T::WTM + T::MI * mi + li) ^ kflip_a;
+    // First column of each BV-wide run of column tiles (BV = 1: every tile).
+    constexpr int NBV = T::TN / T::BV;
+    int b_col[NBV];
 #pragma unroll
-    for (int ni = 0; ni < T::TN; ++ni) b_col[ni] = (wx * T::WTN + T::MI * ni + li) ^ kflip;
+    for (int h = 0; h < NBV; ++h) b_col[h] = (wx * T::WTN + T::bcol(h * T::BV, li)) ^ kflip_b;
 
     // One operand group = KG consecutive k steps: one 16-byte quad of A per
     // row tile and KG values of B per column tile.  The operands of group g+1
@@ -406,11 +434,21 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
 #pragma unroll
             for (int ni = 0; ni < T::TN; ++ni)
                 b[ni] = *(const f32x4*)(Bs + (b_row + T::MI * ni) * T::BK + ((quad ^ b_swz) << 2));
-        } else {
+        } else if constexpr (T::BV == 1) {
 #pragma unroll
             for (int s = 0; s < T::KG; ++s)
 #pragma unroll
                 for (int ni = 0; ni < T::TN; ++ni) b[ni][s] = Bs[(krow + s) * T::LDB + b_col[ni]];
+        } else {
+            typedef float bvec_t __attribute__((ext_vector_type(T::BV)));
+#pragma unroll
+            for (int s = 0; s < T::KG; ++s)
+#pragma unroll
+                for (int h = 0; h < NBV; ++h) {
+                    const bvec_t v = *(const bvec_t*)(Bs + (krow + s) * T::LDB + b_col[h]);
+#pragma unroll
+                    for (int u = 0; u < T::BV; ++u) b[h * T::BV + u][s] = v[u];
+                }
         }
     };
 
@@ -517,29 +555,54 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     }
 
     // Epilogue: accumulator r of lane (li, lg) in MFMA tile (mi, ni) is row
-    // Op::row(r, lg) and column li of that tile.  The general form stores
+    // Op::row(r, lg) of that tile and wave-tile column bcol(ni, li).  The
+    // general form stores
     // alpha * acc, plus beta * C when beta != 0 (C is not read otherwise); the
     // choice is made once, outside the store loop.
+    // With BV > 1 a lane's BV outputs of one row are adjacent columns: an
+    // interior tile stores them as one vector (rows with an odd ldc start on
+    // any 4-byte boundary, which vector stores accept), an edge tile element
+    // by element.
+    typedef float cvec_t __attribute__((ext_vector_type(T::BV), aligned(4)));
     auto store = [&](auto read_c_tag, auto masked_tag) {
         constexpr bool read_c = decltype(read_c_tag)::value;
         constexpr bool masked = decltype(masked_tag)::value;
 #pragma unroll
         for (int mi = 0; mi < T::TM; ++mi) {
 #pragma unroll
-            for (int ni = 0; ni < T::TN; ++ni) {
-                const int col = wx * T::WTN + T::MI * ni + li;
+            for (int h = 0; h < NBV; ++h) {
+                const int col = wx * T::WTN + T::bcol(h * T::BV, li);
 #pragma unroll
                 for (int r = 0; r < Op::ACC; ++r) {
                     const int row = wy * T::WTM + T::MI * mi + Op::row(r, lg);
-                    if (!masked || (row < rows_left && col < cols_left)) {
-                        float* const c = C + (int64_t)row * p.ldc + col;
-                        if constexpr (!T::EX) {
-                            *c = acc[mi][ni][r];
-                        } else if constexpr (read_c) {
-                            *c = __builtin_fmaf(p.beta, *c, p.alpha * acc[mi][ni][r]);
+                    float* const c = C + (int64_t)row * p.ldc + col;
+                    cvec_t v;
+#pragma unroll
+                    for (int u = 0; u < T::BV; ++u) v[u] = acc[mi][h * T::BV + u][r];
+                    if constexpr (T::EX) {
+                        if constexpr (read_c) {
+                            if (!masked) {
+                                const cvec_t old = *(const cvec_t*)c;
+#pragma unroll
+                                for (int u = 0; u < T::BV; ++u)
+                                    v[u] = __builtin_fmaf(p.beta, old[u], p.alpha * v[u]);
+                            } else {
+#pragma unroll
+                                for (int u = 0; u < T::BV; ++u)
+                                    if (row < rows_left && col + u < cols_left)
+                                        v[u] = __builtin_fmaf(p.beta, c[u], p.alpha * v[u]);
+                            }
                         } else {
-                            *c = p.alpha * acc[mi][ni][r];
+#pragma unroll
+                            for (int u = 0; u < T::BV; ++u) v[u] = p.alpha * v[u];
                         }
+                    }
+                    if (!masked) {
+                        *(cvec_t*)c = v;
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < T::BV; ++u)
+                            if (row < rows_left && col + u < cols_left) c[u] = v[u];
                     }
                 }
             }

@@ -110,7 +110,7 @@ struct ConfigEntry {
 // The same tile with stored-operand layouts and the alpha/beta epilogue.
 template <class T, bool TA, bool TB>
 using DlGeneral = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::OCC, T::GROUP_M,
-                         T::STAGES, T::KSPLIT, T::SWIZZLE, TA, TB, true>;
+                         T::STAGES, T::KSPLIT, T::SWIZZLE, TA, TB, true, T::BIL>;
 
 #define SGEMM_CFG(T, name, per_cu, a1, b1, a2, b2) \
     { name, T::BM, T::BN, T::BK, T::NT, (const void*)&sgemm_mfma_kernel<T>, per_cu, a1, b1, a2, b2 }

@@ -79,6 +79,42 @@ WORKLOADS = {
 }
 
 
+@dataclass(frozen=True)
+class WindowWorkload:
+    """Sliding window sums y[i] = sum_{d<W} x[i+d], i < n; x holds n + W - 1
+    values."""
+    name: str
+    n: int
+    W: int
+    dist: str
+    seed: int
+    about: str = field(default="", compare=False)
+
+    @property
+    def bytes(self) -> int:
+        # each input read once, each output written once
+        return 4 * (self.n + self.W - 1) + 4 * self.n
+
+    def describe(self) -> str:
+        return "window_sum n=%d W=%d x~%s seed=%d" % (self.n, self.W, self.dist, self.seed)
+
+
+# The lecture's five-wide window over 2^28 outputs (1 GiB in, 1 GiB out), and a
+# wide one.
+WINDOW_WORKLOADS = {
+    "window5": WindowWorkload("window5", 1 << 28, 5, "uniform", 6,
+                              about="2^28 outputs, W = 5, uniform[-1,1), seed 6"),
+    "window33": WindowWorkload("window33", 1 << 28, 33, "uniform", 7,
+                               about="2^28 outputs, W = 33, uniform[-1,1), seed 7"),
+}
+
+
+def window_input(w: WindowWorkload) -> torch.Tensor:
+    """The n + W - 1 float32 inputs of a window workload (CPU)."""
+    gen = torch.Generator("cpu").manual_seed(w.seed)
+    return draw(gen, w.n + w.W - 1, w.dist)
+
+
 def draw(gen: torch.Generator, n: int, dist: str, scale: float = 1.0) -> torch.Tensor:
     """n float32 values from one of the recipes, using ``gen``."""
     if dist == "uniform":
