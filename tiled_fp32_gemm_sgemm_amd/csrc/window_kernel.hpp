@@ -15,9 +15,13 @@
 //    The buffer descriptor's range ends at the last valid input, so the
 //    buffer unit returns zeros past it: the lecture's guard against n + W - 1,
 //    done by the hardware.
-//  * Each lane sums its four outputs with a rolling window of four values:
-//    one LDS read per step d, and each output adds its terms in the order
-//    d = 0, 1, ..., W-1 like the definition.
+//  * Each lane sums its four outputs from 16-byte quads of the staged span:
+//    quad q holds x[o+4q .. o+4q+3], so the four values of step d come from
+//    quads d/4 and d/4 + 1, and (W + 3) / 4 + 1 ds_read_b128 serve all W
+//    steps.  The lanes of a pass read consecutive quads (no bank conflicts;
+//    one float per step at a 16-byte lane stride conflicted 1.7 times per
+//    access).  Each output adds its terms in the order d = 0, 1, ..., W-1,
+//    like the definition.
 #pragma once
 
 #include "tile_common.hpp"
@@ -30,7 +34,9 @@ struct WindowTile {
     static constexpr int T = NT * 4 * QUADS;       // outputs per workgroup
     static constexpr int MAX_W = 1024;             // widest window supported
     static constexpr int CHUNK = 256;              // floats per direct-copy wave instruction
-    static constexpr int TILE = ((T + MAX_W - 1 + CHUNK - 1) / CHUNK) * CHUNK;  // LDS floats
+    // LDS floats: the T + MAX_W - 1 staged inputs, plus the last quad read
+    // past a lane's window (whole quads up to o + 4 * ceil(W / 4) + 3).
+    static constexpr int TILE = ((T + MAX_W + 7 + CHUNK - 1) / CHUNK) * CHUNK;
 };
 
 typedef __attribute__((address_space(3))) void lds_void_w;
@@ -62,20 +68,23 @@ __device__ __forceinline__ void window_sum_body(const float* x, float* y, int64_
     for (int j = 0; j < WT::QUADS; ++j) {
         const int o = 4 * tid + WT::NT * 4 * j;  // first output of this quad, in the block
         if (base + o >= n) break;
-        const float* const t = tile + o;
-        float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
-        float r0 = t[0], r1 = t[1], r2 = t[2];
-        for (int d = 0; d < W; ++d) {
-            const float r3 = t[d + 3];
-            a0 += r0;
-            a1 += r1;
-            a2 += r2;
-            a3 += r3;
-            r0 = r1;
-            r1 = r2;
-            r2 = r3;
+        const f32x4* const t = (const f32x4*)(tile + o);  // o is a multiple of 4
+        f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 cur = t[0];
+        for (int q = 0; 4 * q < W; ++q) {
+            const f32x4 nxt = t[q + 1];
+            // Steps d = 4q + r: output i adds x[o + i + d], the element
+            // r + i of the pair (cur, nxt).
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (4 * q + r < W) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[i] += r + i < 4 ? cur[r + i] : nxt[r + i - 4];
+                }
+            }
+            cur = nxt;
         }
-        const f32x4 v = {a0, a1, a2, a3};
+        const f32x4 v = acc;
         const int64_t left = n - (base + o);
         stg4_masked(y + base + o, v, left >= 4 ? 4 : (int)left);
     }
