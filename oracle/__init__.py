@@ -1,4 +1,5 @@
-"""CPU oracle for C = A x B in FP32 inputs with an FP64 result.
+"""CPU oracle for C = A x B in FP32 inputs with an FP64 result (and for the
+sliding window sum and the 2-D convolution built on the same staging idea).
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  The GPU library never
@@ -56,6 +57,10 @@ def _load():
     lib.oracle_sgemm_strided_batched_f64.restype = ctypes.c_int
     lib.oracle_sgemm_entries_f64.argtypes = [i64, p, i64, p, i64, i64, p, p, p, p]
     lib.oracle_sgemm_entries_f64.restype = None
+    lib.oracle_conv2d_nhwc_f64.argtypes = [i64] * 13 + [p, p, p, p]
+    lib.oracle_conv2d_nhwc_f64.restype = ctypes.c_int
+    lib.oracle_conv2d_nhwc_entries_f64.argtypes = [i64] * 13 + [p, p, i64, p, p, p]
+    lib.oracle_conv2d_nhwc_entries_f64.restype = ctypes.c_int
     lib.oracle_sgemm_ex_f64.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64,
                                         ctypes.c_float, p, i64, p, i64, ctypes.c_float, p, i64,
                                         p, p, i64, ctypes.c_int]
@@ -244,4 +249,58 @@ def window_sum_f64(n: int, W: int, x):
     yabs = np.empty(n, dtype=np.float64)
     if n > 0:
         lib.oracle_window_sum_f64(n, W, _ptr(xx), _ptr(y), _ptr(yabs))
+    return y, yabs
+
+
+def conv_out_size(size: int, pad: int, f: int, stride: int, dil: int) -> int:
+    """Output extent of the convolution along one axis (see oracle.c)."""
+    span = size + 2 * pad - dil * (f - 1) - 1
+    return 0 if span < 0 else span // stride + 1
+
+
+def conv2d_nhwc_f64(x, wt, N: int, H: int, W: int, C: int, K: int, R: int, S: int,
+                    pad=(0, 0), stride=(1, 1), dil=(1, 1)):
+    """2-D convolution of NHWC input x (N*H*W*C floats) with KRSC filters wt
+    (K*R*S*C floats), zero padding, stride and dilation (see oracle.c).
+    Returns FP64 (y, yabs), each shaped (N, P, Q, K)."""
+    lib = _load()
+    xx = _f32_flat(x)
+    ww = _f32_flat(wt)
+    if min(stride) < 1 or min(dil) < 1 or min(pad) < 0:
+        raise ValueError("stride and dilation must be positive, padding not negative")
+    if xx.size < N * H * W * C or ww.size < K * R * S * C:
+        raise ValueError("input or filter buffer too small")
+    P = conv_out_size(H, pad[0], R, stride[0], dil[0])
+    Q = conv_out_size(W, pad[1], S, stride[1], dil[1])
+    y = np.empty((N, P, Q, K), dtype=np.float64)
+    yabs = np.empty((N, P, Q, K), dtype=np.float64)
+    st = lib.oracle_conv2d_nhwc_f64(N, H, W, C, K, R, S, pad[0], pad[1], stride[0], stride[1],
+                                    dil[0], dil[1], _ptr(xx), _ptr(ww), _ptr(y), _ptr(yabs))
+    if st != 0:
+        raise ValueError("invalid convolution arguments")
+    return y, yabs
+
+
+def conv2d_nhwc_entries_f64(x, wt, N: int, H: int, W: int, C: int, K: int, R: int, S: int,
+                            idx, pad=(0, 0), stride=(1, 1), dil=(1, 1)):
+    """Selected outputs (flat indices into the N x P x Q x K output) of the
+    convolution above; returns FP64 (y, yabs) of len(idx)."""
+    lib = _load()
+    xx = _f32_flat(x)
+    ww = _f32_flat(wt)
+    if min(stride) < 1 or min(dil) < 1 or min(pad) < 0:
+        raise ValueError("stride and dilation must be positive, padding not negative")
+    P = conv_out_size(H, pad[0], R, stride[0], dil[0])
+    Q = conv_out_size(W, pad[1], S, stride[1], dil[1])
+    ii = np.ascontiguousarray(np.asarray(idx, dtype=np.int64).ravel())
+    if ii.size and (ii.min() < 0 or ii.max() >= N * P * Q * K):
+        raise ValueError("output index out of range")
+    y = np.empty(ii.size, dtype=np.float64)
+    yabs = np.empty(ii.size, dtype=np.float64)
+    if ii.size:
+        st = lib.oracle_conv2d_nhwc_entries_f64(N, H, W, C, K, R, S, pad[0], pad[1], stride[0],
+                                                stride[1], dil[0], dil[1], _ptr(xx), _ptr(ww),
+                                                ii.size, _ptr(ii), _ptr(y), _ptr(yabs))
+        if st != 0:
+            raise ValueError("invalid convolution arguments")
     return y, yabs

@@ -241,6 +241,119 @@ void oracle_window_sum_f64(int64_t n, int64_t W, const float *x, double *y, doub
     }
 }
 
+/*
+ * 2-D convolution, the "Convolution" row of the tiled-kernel table in "Tiling
+ * Strategies", section 5 ("Tiling Beyond GEMM"): input patches and filter
+ * weights are the operands, and every weight is used at every output position.
+ * The pages give no formula; this is the usual deep-learning form
+ * (cross-correlation, zero padding, stride, dilation), channels innermost:
+ *   x[n][h][w][c]    (N x H x W x C input, NHWC)
+ *   wt[k][r][s][c]   (K x R x S x C filters, KRSC)
+ *   y[n][p][q][k]    (N x P x Q x K output, NHWC),
+ *   P = (H + 2 pad_h - dil_h (R - 1) - 1) / stride_h + 1 (floor; 0 if negative),
+ *   Q = (W + 2 pad_w - dil_w (S - 1) - 1) / stride_w + 1,
+ *   y[n][p][q][k] = sum_{r<R} sum_{s<S} sum_{c<C}
+ *       x[n][p stride_h - pad_h + r dil_h][q stride_w - pad_w + s dil_w][c] * wt[k][r][s][c],
+ * an input position outside 0 <= h < H, 0 <= w < W reading as zero.  The terms
+ * are added in the order r, s, c (each ascending) in FP64, exact products as
+ * for the matrix product; yabs is the same sum of |x| |wt| (the scale of the
+ * acceptance bound).  y and yabs hold N * P * Q * K doubles.  Returns 0, or -1
+ * for a negative size or a non-positive stride or dilation.
+ */
+static int64_t conv_out_size(int64_t in, int64_t pad, int64_t f, int64_t stride, int64_t dil) {
+    const int64_t span = in + 2 * pad - dil * (f - 1) - 1;
+    return span < 0 ? 0 : span / stride + 1;
+}
+
+typedef struct {
+    int64_t N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, P, Q;
+} conv_shape;
+
+/* Output (n, p, q, k): terms in the order r, s, c. */
+static void conv_one(const conv_shape *g, const float *x, const float *wt, int64_t n, int64_t p,
+                     int64_t q, int64_t k, double *out, double *outabs) {
+    double acc = 0.0, accabs = 0.0;
+    for (int64_t r = 0; r < g->R; ++r) {
+        const int64_t h = p * g->stride_h - g->pad_h + r * g->dil_h;
+        if (h < 0 || h >= g->H) continue;
+        for (int64_t s = 0; s < g->S; ++s) {
+            const int64_t w = q * g->stride_w - g->pad_w + s * g->dil_w;
+            if (w < 0 || w >= g->W) continue;
+            const float *const xp = x + ((n * g->H + h) * g->W + w) * g->C;
+            const float *const wp = wt + ((k * g->R + r) * g->S + s) * g->C;
+            for (int64_t c = 0; c < g->C; ++c) {
+                const double prod = (double)xp[c] * (double)wp[c];
+                acc += prod;
+                accabs += fabs(prod);
+            }
+        }
+    }
+    *out = acc;
+    *outabs = accabs;
+}
+
+static int conv_setup(conv_shape *g, int64_t N, int64_t H, int64_t W, int64_t C, int64_t K,
+                      int64_t R, int64_t S, int64_t pad_h, int64_t pad_w, int64_t stride_h,
+                      int64_t stride_w, int64_t dil_h, int64_t dil_w) {
+    if (N < 0 || H < 0 || W < 0 || C < 0 || K < 0 || R < 0 || S < 0 || pad_h < 0 || pad_w < 0)
+        return -1;
+    if (stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1) return -1;
+    g->N = N; g->H = H; g->W = W; g->C = C; g->K = K; g->R = R; g->S = S;
+    g->pad_h = pad_h; g->pad_w = pad_w; g->stride_h = stride_h; g->stride_w = stride_w;
+    g->dil_h = dil_h; g->dil_w = dil_w;
+    g->P = conv_out_size(H, pad_h, R, stride_h, dil_h);
+    g->Q = conv_out_size(W, pad_w, S, stride_w, dil_w);
+    return 0;
+}
+
+int oracle_conv2d_nhwc_f64(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R,
+                           int64_t S, int64_t pad_h, int64_t pad_w, int64_t stride_h,
+                           int64_t stride_w, int64_t dil_h, int64_t dil_w, const float *x,
+                           const float *wt, double *y, double *yabs) {
+    conv_shape g;
+    if (conv_setup(&g, N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w))
+        return -1;
+    const int64_t outs = N * g.P * g.Q * K;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t e = 0; e < outs; ++e) {
+        int64_t t = e;
+        const int64_t k = t % K;
+        t /= K;
+        const int64_t q = t % g.Q;
+        t /= g.Q;
+        const int64_t p = t % g.P;
+        conv_one(&g, x, wt, t / g.P, p, q, k, y + e, yabs + e);
+    }
+    return 0;
+}
+
+/* Selected outputs of the convolution above: flat output indices idx[e] into
+ * the N x P x Q x K array; y[e], yabs[e] as there.  Returns 0 or -1. */
+int oracle_conv2d_nhwc_entries_f64(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K,
+                                   int64_t R, int64_t S, int64_t pad_h, int64_t pad_w,
+                                   int64_t stride_h, int64_t stride_w, int64_t dil_h,
+                                   int64_t dil_w, const float *x, const float *wt, int64_t count,
+                                   const int64_t *idx, double *y, double *yabs) {
+    conv_shape g;
+    if (conv_setup(&g, N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w))
+        return -1;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t e = 0; e < count; ++e) {
+        int64_t t = idx[e];
+        const int64_t k = t % K;
+        t /= K;
+        const int64_t q = t % g.Q;
+        t /= g.Q;
+        const int64_t p = t % g.P;
+        conv_one(&g, x, wt, t / g.P, p, q, k, y + e, yabs + e);
+    }
+    return 0;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();
