@@ -180,3 +180,38 @@ def test_window_sum_argument_errors():
     assert lib.window_sum(10, 5, FAKE, None, 0) == -3
     assert lib.window_sum(2 ** 62, 5, FAKE, FAKE, 0) == -4     # more than 2^31 blocks
     assert lib.window_sum(0, 5, None, None, 0) == 0            # nothing to do
+
+
+def test_conv2d_host_logic_and_argument_errors():
+    lib = _native.lib()
+    # output extents: (H + 2 pad - dil (R - 1) - 1) / stride + 1, floored, 0 when negative
+    assert sg.conv2d_output_size(56, 56, 3, 3, 1, 1, 1) == (56, 56)
+    assert sg.conv2d_output_size(56, 56, 3, 3, 1, 2, 1) == (28, 28)
+    assert sg.conv2d_output_size(7, 9, 3, 2, (0, 1), (2, 1), (1, 3)) == (3, 8)
+    assert sg.conv2d_output_size(2, 2, 5, 5) == (0, 0)
+    ok = [c for c in range(sg.num_configs()) if sg.conv2d_config_available(c)]
+    assert ok and all(sg.config_has_general_form(c) for c in ok)
+    for shape in [(64, 14, 14, 256, 256, 3, 3, 1), (64, 28, 28, 128, 128, 3, 3, 1),
+                  (8, 32, 32, 3, 64, 7, 7, 3, 2)]:
+        assert sg.conv2d_select_config(*shape) in ok
+    # a tile whose BK divides C is preferred (direct staging)
+    assert sg.config_info(sg.conv2d_select_config(64, 14, 14, 256, 256, 3, 3, 1))["bk"] % 32 == 0
+
+    def call(*a, **kw):
+        return sg.conv2d_nhwc_raw(*a, **kw)
+    base = (1, 8, 8, 16, 16, 3, 3)
+    assert call(*base, FAKE, FAKE, FAKE, stride=(0, 1)) == -1
+    assert call(*base, FAKE, FAKE, FAKE, dil=(1, 0)) == -1
+    assert call(*base, FAKE, FAKE, FAKE, pad=(-1, 1)) == -1
+    assert call(-1, 8, 8, 16, 16, 3, 3, FAKE, FAKE, FAKE) == -1
+    assert call(*base, None, FAKE, FAKE, pad=1) == -3
+    assert call(*base, FAKE, None, FAKE, pad=1) == -3
+    assert call(*base, FAKE, FAKE, None, pad=1) == -3
+    assert call(*base, FAKE, FAKE, FAKE, pad=1, config=0) == -7
+    assert call(*base, FAKE, FAKE, FAKE, pad=1, config=10 ** 6) == -7
+    assert call(1, 2 ** 29, 8, 16, 16, 3, 3, FAKE, FAKE, FAKE) == -4   # padded span too large
+    assert call(2 ** 20, 2 ** 10, 2 ** 10, 1, 1, 1, 1, FAKE, FAKE, FAKE) == -4  # N*P*Q >= 2^31
+    assert call(0, 8, 8, 16, 16, 3, 3, None, None, None) == 0         # no outputs
+    assert call(1, 2, 2, 16, 16, 5, 5, None, None, None) == 0         # P = Q = 0
+    assert call(1, 8, 8, 16, 0, 3, 3, None, None, None) == 0          # no output channels
+    assert lib.conv2d_config_available(-1) == -7

@@ -1,4 +1,5 @@
-"""ctypes view of libsgemm.so (the C ABI in include/sgemm.h).
+"""ctypes view of libsgemm.so (the C ABI in include/sgemm.h, window_sum.h and
+conv2d.h).
 
 Argument marshalling only: every operation runs in the HIP library.  If the
 library has not been built, loading fails with an error that says so; there is
@@ -73,6 +74,12 @@ _SIGS = {
         ctypes.c_int),
     "sgemm_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "window_sum": ([_i64, _i64, _p, _p, _p], ctypes.c_int),
+    "conv2d_nhwc": ([_i64] * 13 + [_p, _p, _p, _p], ctypes.c_int),
+    "conv2d_nhwc_with_config": ([ctypes.c_int] + [_i64] * 13 + [_p, _p, _p, _p], ctypes.c_int),
+    "conv2d_nhwc_output_size": ([_i64] * 10 + [ctypes.POINTER(_i64), ctypes.POINTER(_i64)],
+                                ctypes.c_int),
+    "conv2d_config_available": ([ctypes.c_int], ctypes.c_int),
+    "conv2d_select_config": ([_i64] * 13, ctypes.c_int),
 }
 
 

@@ -285,3 +285,81 @@ def window_sum(x, W: int, out=None, stream=None):
         st = window_sum_raw(n, W, x.data_ptr(), out.data_ptr(), _stream_handle(stream, x.device))
     _check(st, "window_sum")
     return out
+
+
+def _pair(v, name):
+    if isinstance(v, int):
+        return (v, v)
+    t = tuple(int(e) for e in v)
+    if len(t) != 2:
+        raise ValueError("%s must be an int or a pair" % name)
+    return t
+
+
+def conv2d_output_size(H: int, W: int, R: int, S: int, pad=0, stride=1, dil=1):
+    """(P, Q) of a convolution (the library's conv2d_nhwc_output_size)."""
+    ph, pw = _pair(pad, "pad")
+    sh, sw = _pair(stride, "stride")
+    dh, dw = _pair(dil, "dil")
+    P, Q = ctypes.c_int64(), ctypes.c_int64()
+    st = _native.lib().conv2d_nhwc_output_size(H, W, R, S, ph, pw, sh, sw, dh, dw,
+                                               ctypes.byref(P), ctypes.byref(Q))
+    _check(st, "conv2d_nhwc_output_size")
+    return P.value, Q.value
+
+
+def conv2d_nhwc_raw(N, H, W, C, K, R, S, x_ptr, w_ptr, y_ptr, pad=0, stride=1, dil=1, stream=0,
+                    config=None) -> int:
+    """2-D convolution on device addresses: NHWC input, KRSC filters, NPQK
+    output (include/conv2d.h); returns the status."""
+    ph, pw = _pair(pad, "pad")
+    sh, sw = _pair(stride, "stride")
+    dh, dw = _pair(dil, "dil")
+    lib = _native.lib()
+    if config is not None:
+        return lib.conv2d_nhwc_with_config(int(config), N, H, W, C, K, R, S, ph, pw, sh, sw, dh,
+                                           dw, x_ptr, w_ptr, y_ptr, stream)
+    return lib.conv2d_nhwc(N, H, W, C, K, R, S, ph, pw, sh, sw, dh, dw, x_ptr, w_ptr, y_ptr,
+                           stream)
+
+
+def conv2d_nhwc(x, wt, pad=0, stride=1, dil=1, out=None, stream=None, config=None):
+    """Convolution of a contiguous float32 CUDA tensor x (N, H, W, C) with
+    filters wt (K, R, S, C); returns y (N, P, Q, K)."""
+    import torch
+    for t, name in ((x, "x"), (wt, "wt")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.device.type != "cuda":
+            raise TypeError("%s must be a float32 CUDA tensor" % name)
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous 4-D tensor" % name)
+    N, H, W, C = x.shape
+    K, R, S, C2 = wt.shape
+    if C2 != C:
+        raise ValueError("channel counts differ: x has %d, wt has %d" % (C, C2))
+    P, Q = conv2d_output_size(H, W, R, S, pad, stride, dil)
+    if out is None:
+        out = torch.empty((N, P, Q, K), dtype=torch.float32, device=x.device)
+    if tuple(out.shape) != (N, P, Q, K) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (%d, %d, %d, %d) tensor" % (N, P, Q, K))
+    with torch.cuda.device(x.device):
+        st = conv2d_nhwc_raw(N, H, W, C, K, R, S, x.data_ptr(), wt.data_ptr(), out.data_ptr(),
+                             pad, stride, dil, _stream_handle(stream, x.device), config)
+    _check(st, "conv2d_nhwc")
+    return out
+
+
+def conv2d_config_available(config: int) -> bool:
+    st = _native.lib().conv2d_config_available(int(config))
+    if st < 0:
+        raise _native.SgemmError(st, "conv2d_config_available")
+    return bool(st)
+
+
+def conv2d_select_config(N, H, W, C, K, R, S, pad=0, stride=1, dil=1) -> int:
+    ph, pw = _pair(pad, "pad")
+    sh, sw = _pair(stride, "stride")
+    dh, dw = _pair(dil, "dil")
+    st = _native.lib().conv2d_select_config(N, H, W, C, K, R, S, ph, pw, sh, sw, dh, dw)
+    if st < 0:
+        raise _native.SgemmError(st, "conv2d_select_config")
+    return st

@@ -69,7 +69,7 @@ struct F4 {
 
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MI_, int OCC_, int GROUP_M_,
           int STAGES_ = 2, int KSPLIT_ = 1, bool SWIZZLE_ = true, bool TA_ = false,
-          bool TB_ = false, bool EX_ = false, bool BIL_ = true>
+          bool TB_ = false, bool EX_ = false, bool BIL_ = true, bool CONV_ = false>
 struct DlTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -87,6 +87,10 @@ struct DlTile {
     static constexpr bool TA = TA_, TB = TB_;
     static constexpr bool A_KC = !TA, B_KC = TB;
     static constexpr bool EX = EX_;                      // alpha/beta epilogue
+    // CONV: A is the implicit im2col matrix of an NHWC image (GemmArgs::conv):
+    // row m = output position (n, p, q), k = (r, s, c); B holds KRSC filters,
+    // stored N x K.
+    static constexpr bool CONV = CONV_;
     static constexpr int NWMN = WAVES_M * WAVES_N;       // waves per k group
     static constexpr int NW = NWMN * KSPLIT;             // waves per workgroup
     static constexpr int NT = 64 * NW;
@@ -142,6 +146,7 @@ struct DlTile {
     static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0, "fallback copy must split");
     static_assert(MI == 32 || (BN >= 32 && BM >= 32), "the flip needs 32-float rows");
     static_assert(TN % BV == 0, "whole vectors of column tiles");
+    static_assert(!CONV || (A_KC && B_KC && !EX), "convolution: k-contiguous A and B, beta = 0");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert((KSPLIT - 1) * BM * BN <= STAGES * BUF_FLOATS, "k-group exchange fits in LDS");
 
@@ -220,8 +225,9 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     // Tile origin in each stored operand (element offsets); k advances along
     // rows (k-contiguous) or down rows.  The offsets are wave-uniform; saying
     // so keeps them, and the buffer descriptors built from them, in SGPRs.
-    const int64_t a_org = uniform_i64((int64_t)tc.b * p.strideA +
-                                      (T::A_KC ? (int64_t)m0 * p.lda : (int64_t)m0));
+    const int64_t a_org = T::CONV ? 0
+                                  : uniform_i64((int64_t)tc.b * p.strideA +
+                                                (T::A_KC ? (int64_t)m0 * p.lda : (int64_t)m0));
     const int64_t b_org = uniform_i64((int64_t)tc.b * p.strideB +
                                       (T::B_KC ? (int64_t)n0 * p.ldb : (int64_t)n0));
     const float* const A = p.A + a_org;
@@ -254,7 +260,7 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     // quads outside the matrix point out of range and load as zeros.
     auto make_offsets = [&](int kleft) {
 #pragma unroll
-        for (int j = 0; j < T::A_CHW; ++j) {
+        for (int j = 0; j < T::A_CHW && !T::CONV; ++j) {
             const int q = 64 * (wave * T::A_CHW + j) + lane;
             const int r = q / T::A_QPR;
             if constexpr (T::A_KC) {
@@ -283,15 +289,66 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
         }
     };
 
+    // Convolution gather ("Tiling Strategies" section 5: input patches are the
+    // tiled operand).  Each of this wave's A chunks fills one row m of the tile
+    // at logical quad kq of the slice; the row's output position (n, p, q) is
+    // decoded once per block.  A slice lies inside one filter tap (r, s) when
+    // C is a multiple of BK, so its quads are c0 + 4 kq .. + 3 of the input
+    // pixel (p sh - ph + r dh, q sw - pw + s dw): per-lane offsets for c0 = 0
+    // are rebuilt when a slice starts a new tap, and c0 goes into the
+    // descriptor base.  Pixels outside the image get an out-of-range offset
+    // and load as zeros (the zero padding).
+    const ConvGeom& cg = p.conv;
+    int64_t cv_base[T::A_CHW];  // n * H * W * C + 4 kq
+    int cv_ih0[T::A_CHW], cv_iw0[T::A_CHW];
+    bool cv_row[T::A_CHW];
+    if constexpr (T::CONV) {
+#pragma unroll
+        for (int j = 0; j < T::A_CHW; ++j) {
+            const int q = 64 * (wave * T::A_CHW + j) + lane;
+            const int r = q / T::A_QPR;
+            const int kq = (q % T::A_QPR) ^ T::swz(r);
+            cv_row[j] = r < rows_left;
+            const int m = cv_row[j] ? m0 + r : 0;
+            const int oq = m % cg.Q;
+            const int t = m / cg.Q;
+            const int op = t % cg.P;
+            const int n = t / cg.P;
+            cv_base[j] = (int64_t)n * cg.H * cg.W * cg.C + 4 * kq;
+            cv_ih0[j] = op * cg.stride_h - cg.pad_h;
+            cv_iw0[j] = oq * cg.stride_w - cg.pad_w;
+        }
+    }
+    auto conv_offsets = [&](int tap) {
+        const int fr = tap / cg.S;
+        const int fs = tap - fr * cg.S;
+#pragma unroll
+        for (int j = 0; j < T::A_CHW; ++j) {
+            const int ih = cv_ih0[j] + fr * cg.dil_h;
+            const int iw = cv_iw0[j] + fs * cg.dil_w;
+            const bool ok = cv_row[j] && (unsigned)ih < (unsigned)cg.H && (unsigned)iw < (unsigned)cg.W;
+            a_off[j] = ok ? (uint32_t)((cv_base[j] + ((int64_t)ih * cg.W + iw) * cg.C) * 4)
+                          : kOutOfRange;
+        }
+    };
+
     auto load_direct = [&](int k0, int buf) {
         float* const dstA = smem + buf * T::BUF_FLOATS;
         float* const dstB = dstA + T::A_FLOATS;
-        const float* const a_base =
-            p.A + uniform_i64(a_org + (T::A_KC ? (int64_t)k0 : (int64_t)k0 * p.lda));
+        int a_range = (int)a_span;
+        int64_t a_step = T::A_KC ? (int64_t)k0 : (int64_t)k0 * p.lda;
+        if constexpr (T::CONV) {
+            const int tap = __builtin_amdgcn_readfirstlane(k0 / cg.C);
+            const int c0 = k0 - tap * cg.C;
+            if (c0 == 0) conv_offsets(tap);
+            a_step = c0;
+            a_range = (int)((cg.x_elems - c0) * 4);
+        }
+        const float* const a_base = p.A + uniform_i64(a_org + a_step);
         const float* const b_base =
             p.B + uniform_i64(b_org + (T::B_KC ? (int64_t)k0 : (int64_t)k0 * p.ldb));
         const __amdgpu_buffer_rsrc_t ra =
-            __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, (int)a_span, 0x00020000);
+            __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, a_range, 0x00020000);
         const __amdgpu_buffer_rsrc_t rb =
             __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, (int)b_span, 0x00020000);
 #pragma unroll
@@ -315,7 +372,32 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
             const int q = tid + v * T::NT;
             const int r = q / T::A_QPR;
             f32x4 x;
-            if constexpr (T::A_KC) {
+            if constexpr (T::CONV) {
+                // Element by element: the four k of a quad may straddle taps.
+                const int kq = (q % T::A_QPR) ^ T::swz(r);
+                x = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (r < rows_left) {
+                    const int m = m0 + r;
+                    const int oq = m % cg.Q;
+                    const int t = m / cg.Q;
+                    const int op = t % cg.P;
+                    const int n = t / cg.P;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int k = k0 + 4 * kq + e;
+                        if (k < p.K) {
+                            const int tap = k / cg.C;
+                            const int c = k - tap * cg.C;
+                            const int fr = tap / cg.S;
+                            const int fs = tap - fr * cg.S;
+                            const int ih = op * cg.stride_h - cg.pad_h + fr * cg.dil_h;
+                            const int iw = oq * cg.stride_w - cg.pad_w + fs * cg.dil_w;
+                            if ((unsigned)ih < (unsigned)cg.H && (unsigned)iw < (unsigned)cg.W)
+                                x[e] = p.A[(((int64_t)n * cg.H + ih) * cg.W + iw) * cg.C + c];
+                        }
+                    }
+                }
+            } else if constexpr (T::A_KC) {
                 const int kq = (q % T::A_QPR) ^ T::swz(r);
                 x = ldg4_masked(A + (int64_t)r * p.lda + k0 + 4 * kq,
                                 r < rows_left ? p.K - (k0 + 4 * kq) : 0);
@@ -348,7 +430,10 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     // [k][mn], whole quads along its m or n edge; a partial K slice (the last
     // one when BK does not divide K) goes through registers, so the offsets
     // stay fixed for the whole loop.
-    const bool direct_ok = a_span64 * 4 < (int64_t)kOutOfRange &&
+    // A convolution stages directly when every slice lies inside one filter
+    // tap (C a multiple of BK) and the image's byte offsets fit 31 bits.
+    const bool direct_ok = (T::CONV ? (cg.C % T::BK == 0 && cg.x_elems * 4 < (int64_t)kOutOfRange)
+                                    : a_span64 * 4 < (int64_t)kOutOfRange) &&
                            b_span64 * 4 < (int64_t)kOutOfRange &&
                            (T::A_KC || rows_left >= T::BM || p.M % 4 == 0) &&
                            (T::B_KC || cols_left >= T::BN || p.N % 4 == 0);

@@ -4,6 +4,7 @@
 // status from HIP is returned ("CMU DLSys Lecture 12: GPU Acceleration"
 // section 2: launches are asynchronous, and API and launch errors are checked).
 #include "sgemm.h"
+#include "conv2d.h"
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -105,12 +106,20 @@ struct ConfigEntry {
     // General form C = alpha op(A) op(B) + beta C, by operand layout
     // (transA + 2 * transB); NULL where this tile is not built for it.
     const void* general[4];
+    // Implicit-GEMM 2-D convolution; NULL where not built.
+    const void* conv;
 };
 
 // The same tile with stored-operand layouts and the alpha/beta epilogue.
 template <class T, bool TA, bool TB>
 using DlGeneral = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::OCC, T::GROUP_M,
                          T::STAGES, T::KSPLIT, T::SWIZZLE, TA, TB, true, T::BIL>;
+
+// The same tile as an implicit-GEMM convolution (A gathered from an NHWC
+// image, B = KRSC filters stored N x K).
+template <class T>
+using DlConv = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::OCC, T::GROUP_M,
+                      T::STAGES, T::KSPLIT, T::SWIZZLE, false, true, false, T::BIL, true>;
 
 #define SGEMM_CFG(T, name, per_cu, a1, b1, a2, b2) \
     { name, T::BM, T::BN, T::BK, T::NT, (const void*)&sgemm_mfma_kernel<T>, per_cu, a1, b1, a2, b2 }
@@ -123,7 +132,8 @@ using DlGeneral = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::
       { (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, false, false>>,                       \
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, false>>,                        \
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, false, true>>,                        \
-        (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, true>> } }
+        (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, true>> },                        \
+      (const void*)&sgemm_mfma_dl_kernel<DlConv<T>> }
 
 const ConfigEntry kConfigs[] = {
     SGEMM_CFG(Cfg256x128, "mfma32_256x128x16_w2x2", 1, 3.8386e-04, 4.2165e-06, 3.9847e-04, 8.1269e-06),
@@ -255,10 +265,29 @@ int choose_config(int64_t M, int64_t N, int64_t K, int64_t batch, bool general =
     return best;
 }
 
+// Convolution tiles: the smallest predicted time for the implicit GEMM
+// (M = N*P*Q, N = output channels, K = R*S*C); a tile whose BK does not divide
+// C gathers through registers and is counted four times slower.
+int choose_conv_config(int64_t M, int64_t N, int64_t K, int64_t C) {
+    int best = -1;
+    double best_us = 0.0;
+    for (int idx = 0; idx < kNumConfigs; ++idx) {
+        const ConfigEntry& c = kConfigs[idx];
+        if (c.per_cu == 0 || c.conv == nullptr) continue;
+        const double t = predict_us(c, M, N, K, 1) * (C % c.bk == 0 ? 1.0 : 4.0);
+        if (best < 0 || t < best_us * (1.0 - 1e-9)) {
+            best_us = t;
+            best = idx;
+        }
+    }
+    return best;
+}
+
 int launch_gemm(const void* kernel, int bm, int bn, int threads, int64_t M, int64_t N, int64_t K,
                 const float* A, int64_t lda, int64_t strideA, const float* B, int64_t ldb,
                 int64_t strideB, float* C, int64_t ldc, int64_t strideC, int64_t batch,
-                hipStream_t stream, float alpha = 1.0f, float beta = 0.0f) {
+                hipStream_t stream, float alpha = 1.0f, float beta = 0.0f,
+                const ConvGeom* conv = nullptr) {
     if (K == 0) {
         const int64_t total = M * N * batch;
         int64_t blocks = ceil_div(total, 256);
@@ -281,7 +310,8 @@ int launch_gemm(const void* kernel, int bm, int bn, int threads, int64_t M, int6
     const int64_t per_launch = kMaxGridX / per_matrix;  // batch members per launch
     for (int64_t b0 = 0; b0 < batch; b0 += per_launch) {
         const int64_t nb = (batch - b0) < per_launch ? (batch - b0) : per_launch;
-        GemmArgs p;
+        GemmArgs p = {};
+        if (conv != nullptr) p.conv = *conv;
         p.A = A;
         p.B = B;
         p.C = C;
@@ -352,6 +382,83 @@ int run_general(int config, int transA, int transB, int64_t M, int64_t N, int64_
     const ConfigEntry& c = kConfigs[config];
     return launch_gemm(c.general[layout], c.bm, c.bn, c.threads, M, N, K, A, lda, strideA, B,
                        ldb, strideB, C, ldc, strideC, batch, stream, alpha, beta);
+}
+
+// Output extent of a convolution along one axis; -1 for invalid arguments.
+int64_t conv_extent(int64_t in, int64_t pad, int64_t f, int64_t stride, int64_t dil) {
+    if (in < 0 || pad < 0 || f < 0 || stride < 1 || dil < 1) return -1;
+    const int64_t span = in + 2 * pad - dil * (f - 1) - 1;
+    return span < 0 ? 0 : span / stride + 1;
+}
+
+constexpr int64_t kConvMaxExtent = (int64_t)1 << 29;  // image extents and padded spans
+
+// Checked sizes of a convolution run as an implicit GEMM.
+struct ConvPlan {
+    int64_t P, Q, Mg, Kg, x_elems;
+};
+
+int conv_plan(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S,
+              int64_t pad_h, int64_t pad_w, int64_t stride_h, int64_t stride_w, int64_t dil_h,
+              int64_t dil_w, ConvPlan* out) {
+    if (N < 0 || H < 0 || W < 0 || C < 0 || K < 0 || R < 0 || S < 0 || pad_h < 0 || pad_w < 0 ||
+        stride_h < 1 || stride_w < 1 || dil_h < 1 || dil_w < 1)
+        return SGEMM_STATUS_INVALID_SIZE;
+    // Every in-kernel index (p * stride - pad + r * dil, and the like) stays
+    // inside int32 when the padded spans are below 2^29.
+    if (H + 2 * pad_h >= kConvMaxExtent || W + 2 * pad_w >= kConvMaxExtent ||
+        (R > 0 && (R - 1) > kConvMaxExtent / dil_h) || (S > 0 && (S - 1) > kConvMaxExtent / dil_w) ||
+        stride_h >= kConvMaxExtent || stride_w >= kConvMaxExtent || N > kMaxDim || C > kMaxDim ||
+        K > kMaxDim)
+        return SGEMM_STATUS_SIZE_OVERFLOW;
+    ConvPlan pl;
+    pl.P = conv_extent(H, pad_h, R, stride_h, dil_h);
+    pl.Q = conv_extent(W, pad_w, S, stride_w, dil_w);
+    int64_t t, y_elems, w_elems;
+    if (__builtin_mul_overflow(N, pl.P, &t) || __builtin_mul_overflow(t, pl.Q, &pl.Mg) ||
+        __builtin_mul_overflow(R, S, &t) || __builtin_mul_overflow(t, C, &pl.Kg) ||
+        __builtin_mul_overflow(N, H, &t) || __builtin_mul_overflow(t, W, &t) ||
+        __builtin_mul_overflow(t, C, &pl.x_elems) || __builtin_mul_overflow(K, pl.Kg, &w_elems) ||
+        __builtin_mul_overflow(pl.Mg, K, &y_elems) || pl.Mg > kMaxDim || pl.Kg > kMaxDim)
+        return SGEMM_STATUS_SIZE_OVERFLOW;
+    *out = pl;
+    return SGEMM_STATUS_SUCCESS;
+}
+
+int run_conv(int config, int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R,
+             int64_t S, int64_t pad_h, int64_t pad_w, int64_t stride_h, int64_t stride_w,
+             int64_t dil_h, int64_t dil_w, const float* x, const float* w, float* y,
+             hipStream_t stream) {
+    ConvPlan pl;
+    const int st = conv_plan(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w,
+                             &pl);
+    if (st != SGEMM_STATUS_SUCCESS) return st;
+    if (config >= 0 && (config >= kNumConfigs || kConfigs[config].conv == nullptr))
+        return SGEMM_STATUS_INVALID_CONFIG;
+    if (pl.Mg == 0 || K == 0) return SGEMM_STATUS_SUCCESS;
+    if (y == nullptr) return SGEMM_STATUS_NULL_POINTER;
+    if (pl.Kg == 0)  // every output is the empty sum: +0
+        return launch_gemm(nullptr, 1, 1, 1, pl.Mg, K, 0, nullptr, 1, 0, nullptr, 1, 0, y, K, 0,
+                           1, stream);
+    if (x == nullptr || w == nullptr) return SGEMM_STATUS_NULL_POINTER;
+    if (config < 0) config = choose_conv_config(pl.Mg, K, pl.Kg, C);
+    const ConfigEntry& c = kConfigs[config];
+    ConvGeom g;
+    g.H = (int)H;
+    g.W = (int)W;
+    g.C = (int)C;
+    g.P = (int)pl.P;
+    g.Q = (int)pl.Q;
+    g.S = (int)S;
+    g.pad_h = (int)pad_h;
+    g.pad_w = (int)pad_w;
+    g.stride_h = (int)stride_h;
+    g.stride_w = (int)stride_w;
+    g.dil_h = (int)dil_h;
+    g.dil_w = (int)dil_w;
+    g.x_elems = pl.x_elems;
+    return launch_gemm(c.conv, c.bm, c.bn, c.threads, pl.Mg, K, pl.Kg, x, pl.Kg, 0, w, pl.Kg, 0, y,
+                       K, 0, 1, stream, 1.0f, 0.0f, &g);
 }
 
 int run_valu(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, int64_t strideA,
@@ -527,6 +634,48 @@ int sgemm_autotune(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                          strideB, C, ldc, strideC, batch, stream);
     if (best_ms) *best_ms = best;
     return status;
+}
+
+int conv2d_nhwc(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, int64_t S,
+                int64_t pad_h, int64_t pad_w, int64_t stride_h, int64_t stride_w, int64_t dil_h,
+                int64_t dil_w, const float* x, const float* w, float* y, hipStream_t stream) {
+    return run_conv(-1, N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, x,
+                    w, y, stream);
+}
+
+int conv2d_nhwc_with_config(int config, int64_t N, int64_t H, int64_t W, int64_t C, int64_t K,
+                            int64_t R, int64_t S, int64_t pad_h, int64_t pad_w, int64_t stride_h,
+                            int64_t stride_w, int64_t dil_h, int64_t dil_w, const float* x,
+                            const float* w, float* y, hipStream_t stream) {
+    if (config < 0 || config >= kNumConfigs) return SGEMM_STATUS_INVALID_CONFIG;
+    return run_conv(config, N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w,
+                    x, w, y, stream);
+}
+
+int conv2d_nhwc_output_size(int64_t H, int64_t W, int64_t R, int64_t S, int64_t pad_h,
+                            int64_t pad_w, int64_t stride_h, int64_t stride_w, int64_t dil_h,
+                            int64_t dil_w, int64_t* P, int64_t* Q) {
+    const int64_t p = conv_extent(H, pad_h, R, stride_h, dil_h);
+    const int64_t q = conv_extent(W, pad_w, S, stride_w, dil_w);
+    if (p < 0 || q < 0) return SGEMM_STATUS_INVALID_SIZE;
+    if (P) *P = p;
+    if (Q) *Q = q;
+    return SGEMM_STATUS_SUCCESS;
+}
+
+int conv2d_config_available(int config) {
+    if (config < 0 || config >= kNumConfigs) return SGEMM_STATUS_INVALID_CONFIG;
+    return kConfigs[config].conv != nullptr ? 1 : 0;
+}
+
+int conv2d_select_config(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R,
+                         int64_t S, int64_t pad_h, int64_t pad_w, int64_t stride_h,
+                         int64_t stride_w, int64_t dil_h, int64_t dil_w) {
+    ConvPlan pl;
+    const int st = conv_plan(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w,
+                             &pl);
+    if (st != SGEMM_STATUS_SUCCESS) return st;
+    return choose_conv_config(pl.Mg > 0 ? pl.Mg : 1, K > 0 ? K : 1, pl.Kg > 0 ? pl.Kg : 1, C);
 }
 
 const char* sgemm_status_string(int status) {

@@ -15,6 +15,16 @@
 
 namespace sgemm_dev {
 
+// Geometry of a 2-D convolution run as an implicit GEMM (NHWC input, KRSC
+// filters, NPQK output): GEMM row m = (n * P + p) * Q + q, column = output
+// channel, reduction index k = (r * S + s) * C + c.  Unused by plain GEMMs.
+struct ConvGeom {
+    int H, W, C;          // input image
+    int P, Q, S;          // output image, filter width (R = K / (S * C))
+    int pad_h, pad_w, stride_h, stride_w, dil_h, dil_w;
+    int64_t x_elems;      // N * H * W * C
+};
+
 // Kernel arguments.  Sizes are validated on the host: M, N, K < 2^31, all
 // element offsets fit in int64.
 struct GemmArgs {
@@ -28,6 +38,7 @@ struct GemmArgs {
     int batch_base;                     // first batch index of this launch
     int batch_count;                    // batch members in this launch
     float alpha, beta;                  // C = alpha op(A) op(B) + beta C (general form only)
+    ConvGeom conv;                      // implicit-GEMM convolution only
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -115,6 +115,62 @@ def window_input(w: WindowWorkload) -> torch.Tensor:
     return draw(gen, w.n + w.W - 1, w.dist)
 
 
+@dataclass(frozen=True)
+class ConvWorkload:
+    """2-D convolution: NHWC input (N, H, W, C), KRSC filters (K, R, S, C)."""
+    name: str
+    N: int
+    H: int
+    W: int
+    C: int
+    K: int
+    R: int
+    S: int
+    pad: tuple
+    stride: tuple
+    dil: tuple
+    seed: int
+    about: str = field(default="", compare=False)
+
+    @property
+    def out_hw(self):
+        P = (self.H + 2 * self.pad[0] - self.dil[0] * (self.R - 1) - 1) // self.stride[0] + 1
+        Q = (self.W + 2 * self.pad[1] - self.dil[1] * (self.S - 1) - 1) // self.stride[1] + 1
+        return max(P, 0), max(Q, 0)
+
+    @property
+    def flops(self) -> int:
+        # every multiply-add of the definition, zero-padded taps included
+        P, Q = self.out_hw
+        return 2 * self.N * P * Q * self.K * self.R * self.S * self.C
+
+    def describe(self) -> str:
+        return ("conv2d_nhwc N=%d H=%d W=%d C=%d K=%d R=%d S=%d pad=%s stride=%s dil=%s "
+                "x~normal(0,1) w~normal(0,1/sqrt(RSC)) seed=%d" % (
+                    self.N, self.H, self.W, self.C, self.K, self.R, self.S, self.pad,
+                    self.stride, self.dil, self.seed))
+
+
+# ResNet-style 3x3 layers at batch 64 (14.8 GFLOP each), and a strided one.
+CONV_WORKLOADS = {
+    "conv3x3_c256": ConvWorkload("conv3x3_c256", 64, 14, 14, 256, 256, 3, 3, (1, 1), (1, 1),
+                                 (1, 1), 8, about="64 x 14x14x256 -> 256, 3x3, pad 1"),
+    "conv3x3_c128": ConvWorkload("conv3x3_c128", 64, 28, 28, 128, 128, 3, 3, (1, 1), (1, 1),
+                                 (1, 1), 9, about="64 x 28x28x128 -> 128, 3x3, pad 1"),
+    "conv3x3_s2": ConvWorkload("conv3x3_s2", 64, 28, 28, 128, 256, 3, 3, (1, 1), (2, 2),
+                               (1, 1), 10, about="64 x 28x28x128 -> 256, 3x3, pad 1, stride 2"),
+}
+
+
+def conv_operands(w: ConvWorkload):
+    """Flat float32 CPU buffers (x, wt) of a convolution workload: x drawn
+    first, normal(0, 1); filters normal(0, 1/sqrt(R*S*C))."""
+    gen = torch.Generator("cpu").manual_seed(w.seed)
+    x = draw(gen, w.N * w.H * w.W * w.C, "normal")
+    wt = draw(gen, w.K * w.R * w.S * w.C, "normal", 1.0 / math.sqrt(w.R * w.S * w.C))
+    return x, wt
+
+
 def draw(gen: torch.Generator, n: int, dist: str, scale: float = 1.0) -> torch.Tensor:
     """n float32 values from one of the recipes, using ``gen``."""
     if dist == "uniform":
