@@ -3,6 +3,7 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--path mfma|valu]
                     [--workload square4096] [--no-cpu-baseline]
     python bench.py --workload window5      (sliding window sums, GB/s)
+    python bench.py --workload conv3x3_c256 (2-D convolution, TFLOP/s)
 
 One step is one call of the library on the named workload (default: the
 4096^3 product, A and B ~ normal(0,1)/sqrt(K), seed 1), inputs resident in
@@ -38,12 +39,13 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sgemm_mfma_square4096_counters.tx
 COPY_BYTES = 512 * 1024 * 1024   # larger than the 256 MB last-level cache
 
 
-# Sources each kernel family is compiled from (a counter summary is used only
-# while these hash to the value recorded in it).
-GEMM_SOURCES = ("sgemm.hip", "tile_common.hpp", "mfma_dl_kernel.hpp", "mfma_kernel.hpp",
-                "valu_kernel.hpp")
+# Device sources each kernel family is compiled from.  A counter summary is
+# used only while these hash to the value recorded in it and it names the tile
+# the run uses (the tile's template arguments live in the host table).
+GEMM_SOURCES = ("tile_common.hpp", "mfma_dl_kernel.hpp", "mfma_kernel.hpp", "valu_kernel.hpp")
 WINDOW_SOURCES = ("window.hip", "window_kernel.hpp", "tile_common.hpp")
 WINDOW_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "window_sum_window5_counters.txt")
+CONV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv2d_conv3x3_c256_counters.txt")
 
 
 def kernel_source_hash(names=GEMM_SOURCES) -> str:
@@ -55,9 +57,9 @@ def kernel_source_hash(names=GEMM_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(path: str, names=GEMM_SOURCES):
+def read_traffic(path: str, names=GEMM_SOURCES, tile=None):
     """HBM bytes per launch from a committed counter summary, or None when it
-    is missing or was taken on a different kernel source."""
+    is missing, was taken on a different kernel source or on another tile."""
     if not os.path.exists(path):
         return None
     vals = {}
@@ -67,6 +69,9 @@ def read_traffic(path: str, names=GEMM_SOURCES):
                 k, v = line.split(":", 1)
                 vals[k.strip()] = v.strip()
     if vals.get("kernel_source_sha256_16") != kernel_source_hash(names):
+        return None
+    if tile is not None and not vals.get("mfma_instructions_closed_form", "").endswith(
+            "(tile %s)" % tile):
         return None
     try:
         return float(vals["hbm_bytes_per_launch"])
@@ -127,6 +132,12 @@ def summarize_trace(stats_csv: str, out: str, command: str, trace_csv: str = Non
     open(out, "w").write("\n".join(lines) + "\n")
 
 
+def conv_compulsory_bytes(w) -> int:
+    """Input, filters and output, each moved once."""
+    P, Q = w.out_hw
+    return 4 * (w.N * w.H * w.W * w.C + w.K * w.R * w.S * w.C + w.N * P * Q * w.K)
+
+
 def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fetch_csv: str,
                        write_csv: str, sq_csvs, commands, config=None) -> None:
     """Counter summary: utilisation, instruction counts against the closed
@@ -135,13 +146,18 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
     from workloads import WINDOW_WORKLOADS, WORKLOADS
     from tiled_fp32_gemm_sgemm_amd import model
     import tiled_fp32_gemm_sgemm_amd as sg
+    from workloads import CONV_WORKLOADS
     window = workload in WINDOW_WORKLOADS
-    w = WINDOW_WORKLOADS[workload] if window else WORKLOADS[workload]
+    conv = workload in CONV_WORKLOADS
+    w = (WINDOW_WORKLOADS[workload] if window else
+         CONV_WORKLOADS[workload] if conv else WORKLOADS[workload])
     L = ["# rocprofv3 hardware counters, %s path, workload %s" % (path, w.describe()),
          "# commands (one counter pass each, run from the repository root):"]
     L += ["#   " + c for c in commands]
     L.append("kernel_source_sha256_16: %s" % kernel_source_hash(
         WINDOW_SOURCES if window else GEMM_SOURCES))
+    if conv:
+        L.append("flops_per_launch: %d" % w.flops)
     copy_part = "MulFunctor"
     fetch = _per_dispatch(_read_csv(fetch_csv), kernel_part) if fetch_csv else {}
     write = _per_dispatch(_read_csv(write_csv), kernel_part) if write_csv else {}
@@ -164,6 +180,7 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
               "hbm_write_bytes_per_launch: %.0f" % (w_kib * 1024 * w_scale),
               "hbm_bytes_per_launch: %.0f" % hbm,
               "compulsory_bytes: %d" % (w.bytes if window else
+                                        conv_compulsory_bytes(w) if conv else
                                         model.compulsory_bytes(w.M, w.N, w.K, w.batch))]
     merged = {}
     for c in sq_csvs:
@@ -184,7 +201,15 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
     if "_util" in merged:
         L.append("mfma_busy_fraction: %.4f" % _mean(merged["_util"]))
         L.append("effective_clock_ghz_under_profiler: %.3f" % (_mean(merged["_clk"]) / 1e9))
-    if path == "mfma" and not window:
+    if conv:
+        P, Q = w.out_hw
+        cfg = config if config is not None else sg.conv2d_select_config(
+            w.N, w.H, w.W, w.C, w.K, w.R, w.S, w.pad, w.stride, w.dil)
+        info = sg.config_info(cfg)
+        want = model.mfma_instructions(w.N * P * Q, w.K, w.R * w.S * w.C, info["bm"], info["bn"],
+                                       info["bk"], 32, 1)
+        L.append("mfma_instructions_closed_form: %d (tile %s)" % (want, info["name"]))
+    if path == "mfma" and not window and not conv:
         cfg = sg.select_config(w.M, w.N, w.K, w.batch) if config is None else config
         info = sg.config_info(cfg)
         mi = 16 if info["name"].startswith("mfma16") else 32
@@ -319,6 +344,120 @@ def bench_window(args) -> int:
     return 0
 
 
+def conv_cpu_baseline(w, x_cpu, wt_cpu, target_s: float = 10.0):
+    """The oracle, untouched, on the first images of the convolution workload
+    (the same layer at a smaller batch)."""
+    import oracle
+    x = x_cpu.numpy()
+    wt = wt_cpu.numpy()
+    P, Q = w.out_hw
+    per_image = 2.0 * P * Q * w.K * w.R * w.S * w.C
+    n0 = 1
+    t0 = time.perf_counter()
+    oracle.conv2d_nhwc_f64(x, wt, n0, w.H, w.W, w.C, w.K, w.R, w.S, w.pad, w.stride, w.dil)
+    dt0 = time.perf_counter() - t0
+    n = int(min(w.N, max(n0, n0 * target_s / max(dt0, 1e-6))))
+    t0 = time.perf_counter()
+    oracle.conv2d_nhwc_f64(x, wt, n, w.H, w.W, w.C, w.K, w.R, w.S, w.pad, w.stride, w.dil)
+    dt = time.perf_counter() - t0
+    return {"value": per_image * n / dt / 1e12, "unit": "TFLOP/s",
+            "cores": int(oracle.max_threads()), "kind": "oracle",
+            "sample": "images 0..%d of %s (%.3g GFLOP) in %.2f s, FP64 accumulation, OpenMP "
+                      "over outputs" % (n - 1, w.name, per_image * n / 1e9, dt),
+            "seconds": dt}
+
+
+def bench_conv(args) -> int:
+    """2-D convolution (implicit GEMM): TFLOP/s of the definition's
+    multiply-adds against the FP32 matrix peak."""
+    import torch
+    from workloads import CONV_WORKLOADS, conv_operands
+    import tiled_fp32_gemm_sgemm_amd as sg
+
+    w = CONV_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    x_cpu, wt_cpu = conv_operands(w)
+    x = x_cpu.to(dev).view(w.N, w.H, w.W, w.C)
+    wt = wt_cpu.to(dev).view(w.K, w.R, w.S, w.C)
+    P, Q = sg.conv2d_output_size(w.H, w.W, w.R, w.S, w.pad, w.stride, w.dil)
+    y = torch.empty((w.N, P, Q, w.K), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream
+
+    def step(config=args.config):
+        st = sg.conv2d_nhwc_raw(w.N, w.H, w.W, w.C, w.K, w.R, w.S, x.data_ptr(), wt.data_ptr(),
+                                y.data_ptr(), w.pad, w.stride, w.dil, handle, config)
+        if st != 0:
+            raise sg.SgemmError(st, "conv2d_nhwc")
+
+    def timed(fn, n_steps, n_warm):
+        for _ in range(n_warm):
+            fn()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(n_steps):
+            fn()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n_steps
+
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ms = timed(step, args.steps, args.warmup)
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    cfg = args.config if args.config is not None else sg.conv2d_select_config(
+        w.N, w.H, w.W, w.C, w.K, w.R, w.S, w.pad, w.stride, w.dil)
+    comparators = {}
+    if not args.no_comparator:
+        # MIOpen through torch, FP32, on the same NHWC memory (channels_last).
+        torch.backends.cudnn.allow_tf32 = False
+        xt = x.permute(0, 3, 1, 2)
+        wtt = wt.permute(0, 3, 1, 2)
+        tms = timed(lambda: torch.nn.functional.conv2d(xt, wtt, stride=w.stride, padding=w.pad,
+                                                       dilation=w.dil),
+                    max(5, args.steps // 2), 3)
+        comparators["torch_conv2d_channels_last"] = {
+            "tflops": w.flops / (tms * 1e-3) / 1e12, "ms_per_step": tms}
+    out = {
+        "metric": "FP32 2-D convolution TFLOP/s (implicit GEMM, NHWC)",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_fp32_peak": 100.0 * tflops / PEAK_FP32_TFLOPS,
+        "config": {"workload": w.describe(), "N": w.N, "H": w.H, "W": w.W, "C": w.C, "K": w.K,
+                   "R": w.R, "S": w.S, "tile": sg.config_info(cfg)["name"]},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / PEAK_FP32_TFLOPS,
+                     "traffic": (read_traffic(CONV_TRAFFIC_FILE, GEMM_SOURCES,
+                                              sg.config_info(cfg)["name"])
+                                 if args.workload == "conv3x3_c256" and args.config is None
+                                 else None),
+                     "kernel": sg.config_info(cfg)["name"], "avg_kernel_ms": ms},
+        "cpu_baseline": None if args.no_cpu_baseline else conv_cpu_baseline(w, x_cpu, wt_cpu),
+        "comparators": comparators,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -361,9 +500,11 @@ def main(argv=None) -> int:
               "multi-GPU path (asked for --gpus %d)" % args.gpus, file=sys.stderr)
         return 2
 
-    from workloads import WINDOW_WORKLOADS
+    from workloads import CONV_WORKLOADS, WINDOW_WORKLOADS
     if args.workload in WINDOW_WORKLOADS:
         return bench_window(args)
+    if args.workload in CONV_WORKLOADS:
+        return bench_conv(args)
 
     if args.path == "window":
         print("--path window names the window kernel in counter summaries; run "
@@ -429,7 +570,7 @@ def main(argv=None) -> int:
     else:
         tile = "valu_128x128x8_t8x8"
 
-    traffic = (read_traffic(TRAFFIC_FILE)
+    traffic = (read_traffic(TRAFFIC_FILE, GEMM_SOURCES, tile)
                if args.path == "mfma" and args.workload == "square4096" and args.config is None
                else None)
     roofline = {"bound": "mfma" if args.path == "mfma" else "alu",
