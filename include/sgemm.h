@@ -185,12 +185,22 @@ int sgemm_select_config(int64_t M, int64_t N, int64_t K, int64_t batch);
 int sgemm_config_selectable(int config);
 
 /*
+ * Workgroups of configuration `config` one compute unit can hold at once:
+ * the HIP runtime's occupancy answer for the kernel (registers as compiled,
+ * LDS), or, when no device is available, the floor the tile's launch bound
+ * and LDS footprint guarantee.  Host only; SGEMM_STATUS_INVALID_CONFIG for an
+ * unknown index.
+ */
+int sgemm_config_workgroups_per_cu(int config);
+
+/*
  * Predicted microseconds of one launch of configuration `config` on this
  * shape, from a per-configuration time model fitted to measurements (the
  * tile-size trade-off of "Tiling Strategies" section 4, in numbers): whole
- * rounds of 256 (or, where two workgroups fit on a CU, 512) tiles, each
- * costing BM*BN*(a + b*K).  A negative value is a status code (unknown or
- * control configuration, bad sizes).  Host only.
+ * rounds of 256 * w tiles, where w workgroups overlap on a CU, each costing
+ * BM*BN*(a + b*K), and a partial last round in proportion.  A negative value
+ * is a status code (unknown or control configuration, bad sizes).  Host
+ * only.
  */
 double sgemm_config_predict_us(int config, int64_t M, int64_t N, int64_t K, int64_t batch);
 

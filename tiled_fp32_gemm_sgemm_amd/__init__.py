@@ -12,7 +12,7 @@ from .api import (autotune, autotune_raw, config_has_general_form, config_info,
                   config_selectable, num_configs, predict_us, select_config,
                   select_general_config, sgemm, sgemm_ex, sgemm_ex_raw, sgemm_raw,
                   sgemm_strided_batched, sgemm_strided_batched_raw, window_sum,
-                  window_sum_raw)
+                  window_sum_raw, workgroups_per_cu)
 from ._native import SgemmError, status_string
 
 __all__ = ["sgemm", "sgemm_strided_batched", "sgemm_raw", "sgemm_strided_batched_raw",
@@ -20,5 +20,5 @@ __all__ = ["sgemm", "sgemm_strided_batched", "sgemm_raw", "sgemm_strided_batched
            "autotune", "autotune_raw", "sgemm_ex", "sgemm_ex_raw", "config_has_general_form",
            "select_general_config", "window_sum", "window_sum_raw", "conv2d_nhwc",
            "conv2d_nhwc_raw", "conv2d_output_size", "conv2d_config_available",
-           "conv2d_select_config", "SgemmError",
+           "conv2d_select_config", "workgroups_per_cu", "SgemmError",
            "status_string"]

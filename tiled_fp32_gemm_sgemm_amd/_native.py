@@ -57,6 +57,7 @@ _SIGS = {
                            ctypes.POINTER(ctypes.c_int)], ctypes.c_int),
     "sgemm_select_config": ([_i64, _i64, _i64, _i64], ctypes.c_int),
     "sgemm_config_selectable": ([ctypes.c_int], ctypes.c_int),
+    "sgemm_config_workgroups_per_cu": ([ctypes.c_int], ctypes.c_int),
     "sgemm_ex": ([ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, ctypes.c_float, _p, _i64, _p,
                   _i64, ctypes.c_float, _p, _i64, _p], ctypes.c_int),
     "sgemm_ex_strided_batched": (

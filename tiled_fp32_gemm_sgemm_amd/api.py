@@ -143,6 +143,14 @@ def config_selectable(config: int) -> bool:
     return bool(st)
 
 
+def workgroups_per_cu(config: int) -> int:
+    """Workgroups of this configuration one CU holds at once."""
+    st = _native.lib().sgemm_config_workgroups_per_cu(int(config))
+    if st < 0:
+        raise _native.SgemmError(st, "sgemm_config_workgroups_per_cu")
+    return st
+
+
 def predict_us(config: int, M: int, N: int, K: int, batch: int = 1) -> float:
     """Predicted microseconds of one launch of `config` on this shape."""
     t = _native.lib().sgemm_config_predict_us(int(config), M, N, K, batch)

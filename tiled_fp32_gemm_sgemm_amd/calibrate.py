@@ -3,15 +3,18 @@
     python -m tiled_fp32_gemm_sgemm_amd.calibrate [--out calib.json]
     python -m tiled_fp32_gemm_sgemm_amd.calibrate --fit calib.json
 
-For every selectable configuration it times shapes whose tile count fills
-the GPU exactly once (256 tiles: one workgroup per CU) and twice (512 tiles),
-each at K = 256, 1024 and 4096, and fits, per unit of tile area,
+For every configuration it times shapes whose tile count fills the GPU with
+one workgroup per CU (256 tiles) and with as many as a CU holds (256 * w
+tiles, w from the configuration's waves and LDS footprint, at least 2), each
+at K = 128, 256, 1024 and 4096, and fits, per unit of tile area,
 
-    one round of 256 tiles:  BM*BN * (one_a + one_b * K)  microseconds
-    one round of 512 tiles:  BM*BN * (two_a + two_b * K)  microseconds
+    one round of 256 tiles:      BM*BN * (one_a + one_b * K)  microseconds
+    one round of 256 * w tiles:  BM*BN * (two_a + two_b * K)  microseconds
 
-A configuration holds two workgroups per CU when 512 tiles run clearly faster
-per tile than 256 (the second round overlaps the first).  The fitted rows are
+A configuration counts as holding w workgroups per CU when the full round runs
+clearly faster per tile than 256 tiles do (the workgroups overlap).
+`--configs` restricts the run to some configurations (control and
+experimental builds included).  The fitted rows are
 printed in the form the configuration table in csrc/sgemm.hip takes.  Tile
 size is a per-shape trade-off that libraries tune per GPU ("Tiling
 Strategies", section 4; "CMU DLSys Lecture 12", section 6); this is that
@@ -24,11 +27,15 @@ import json
 import sys
 import time
 
-K_POINTS = (256, 1024, 4096)
+K_POINTS = (128, 256, 1024, 4096)
 CUS = 256
 
 
-def measure(out_path: str | None) -> dict:
+def _slots(w: int):
+    return (CUS, min(4, max(2, w)) * CUS)
+
+
+def measure(out_path: str | None, configs=None) -> dict:
     import torch
     from . import api
     dev = torch.device("cuda:0")
@@ -36,9 +43,13 @@ def measure(out_path: str | None) -> dict:
     data = {}
     for c in range(api.num_configs()):
         info = api.config_info(c)
-        if not api.config_selectable(c):
+        if configs is None and not api.config_selectable(c):
             continue
-        for slots in (CUS, 2 * CUS):
+        if configs is not None and c not in configs:
+            continue
+        w = api.workgroups_per_cu(c)
+        data["_w_" + info["name"]] = w
+        for slots in _slots(w):
             M = info["bm"] * 16
             N = info["bn"] * slots // 16
             for K in K_POINTS:
@@ -84,9 +95,12 @@ def fit(data: dict) -> dict:
     import numpy as np
     rows = {}
     for name, pts in data.items():
+        if name.startswith("_w_"):
+            continue
+        w = min(4, max(2, int(data.get("_w_" + name, 2))))
         coef = []
         top = {}
-        for slots in (CUS, 2 * CUS):
+        for slots in _slots(w):
             K = np.array([k for s, k, _ in pts if s == slots], float)
             tf = np.array([t for s, _, t in pts if s == slots], float)
             t_us = 2.0 * slots * K / (tf * 1e12) * 1e6
@@ -94,7 +108,7 @@ def fit(data: dict) -> dict:
             (a, b), *_ = np.linalg.lstsq(A, t_us, rcond=None)
             coef += [max(float(a), 0.0), float(b)]  # a fixed cost is never negative
             top[slots] = tf[np.argmax(K)]
-        per_cu = 2 if top[2 * CUS] > 1.06 * top[CUS] else 1
+        per_cu = w if top[w * CUS] > 1.06 * top[CUS] else 1
         rows[name] = (per_cu, *coef)
     return rows
 
@@ -103,8 +117,10 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--out", help="write the measurements here (JSON)")
     ap.add_argument("--fit", help="fit measurements read from this JSON instead of measuring")
+    ap.add_argument("--configs", help="comma-separated configuration indices to measure")
     args = ap.parse_args(argv)
-    data = json.load(open(args.fit)) if args.fit else measure(args.out)
+    configs = [int(c) for c in args.configs.split(",")] if args.configs else None
+    data = json.load(open(args.fit)) if args.fit else measure(args.out, configs)
     for name, (per_cu, a1, b1, a2, b2) in fit(data).items():
         print('    "%s": %d, %.4e, %.4e, %.4e, %.4e' % (name, per_cu, a1, b1, a2, b2))
     return 0

@@ -135,6 +135,10 @@ struct DlTile {
     static constexpr int B_VEC = BK * BN / 4 / NT;
     static constexpr int LDS_BYTES = STAGES * BUF_FLOATS * 4;
     static constexpr int LPS = A_CHW + B_CHW;            // copy instructions per wave per slice
+    // Workgroups one CU can hold: by waves per SIMD (OCC, the launch bound)
+    // and by the 160 KB of LDS.
+    static constexpr int WG_PER_CU = (4 * OCC * 64 / NT) < (160 * 1024 / LDS_BYTES)
+                                         ? (4 * OCC * 64 / NT) : (160 * 1024 / LDS_BYTES);
 
     static_assert(MI == 16 || MI == 32, "MFMA tile edge");
     static_assert(BK == 16 || BK == 32 || BK == 64, "BK must be 16, 32 or 64");

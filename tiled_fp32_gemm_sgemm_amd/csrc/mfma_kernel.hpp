@@ -103,6 +103,10 @@ struct MfmaTile {
     static constexpr int NKG = KPL / KG;                 // operand groups per slice
     static constexpr int HOLD = 2;                       // k steps issued after the barrier
     static constexpr int LDS_BYTES = 2 * (A_FLOATS + B_FLOATS) * 4;
+    // Workgroups one CU can hold: by waves per SIMD (OCC, the launch bound)
+    // and by the 160 KB of LDS.
+    static constexpr int WG_PER_CU = (4 * OCC * 64 / NT) < (160 * 1024 / LDS_BYTES)
+                                         ? (4 * OCC * 64 / NT) : (160 * 1024 / LDS_BYTES);
 
     static_assert(MI == 16 || MI == 32, "MFMA tile edge");
     static_assert(BK == 8 || BK == 16 || BK == 32, "BK must be 8, 16 or 32");

@@ -88,19 +88,25 @@ using Dl128x128k64m32s2 = DlTile<128, 128, 64, 2, 2, 32, 1, 8, 2>;  // 4 waves o
 using Dl64x64k64m32s4x2 = DlTile<64, 64, 64, 2, 2, 32, 2, 8, 4, 2>;
 using Dl64x64k32m32s4x2 = DlTile<64, 64, 32, 2, 2, 32, 2, 8, 4, 2>;
 using Dl128x64k64m32s2x2 = DlTile<128, 64, 64, 2, 2, 32, 2, 8, 2, 2>;  // 8 waves of 64x32
+// Small LDS footprints, so that three or four workgroups share a CU and
+// their barriers fall at different times (4 waves of 64x64 or 32x32 each).
+using Dl128x128k16o4 = DlTile<128, 128, 16, 2, 2, 32, 4, 8, 2>;     // 32 KB LDS, 4 per CU
+using Dl128x128k16o3s3 = DlTile<128, 128, 16, 2, 2, 32, 3, 8, 3>;   // 48 KB LDS, 3 per CU
+using Dl64x64k32o4 = DlTile<64, 64, 32, 2, 2, 32, 4, 8, 2>;         // 32 KB LDS, 4 per CU
 // Control build: A stored unswizzled (bank conflicts on purpose); never chosen.
 using Dl256x256k32m32Plain = DlTile<256, 256, 32, 2, 4, 32, 2, 8, 2, 1, false>;
 
 struct ConfigEntry {
     const char* name;
     int bm, bn, bk, threads;
+    int wg_per_cu;  // workgroups a CU can hold (waves and LDS)
     const void* kernel;
     // Time model for the choice of a configuration, fitted to measurements on
     // MI355X (python -m tiled_fp32_gemm_sgemm_amd.calibrate), per unit of tile
     // area in microseconds: a round of 256 tiles (one workgroup per CU) takes
-    // BM*BN*(one_a + one_b*K); when two workgroups fit on a CU (per_cu = 2) a
-    // round of 512 tiles takes BM*BN*(two_a + two_b*K).  per_cu = 0 marks a
-    // control build that is never chosen.
+    // BM*BN*(one_a + one_b*K); when w = per_cu > 1 workgroups overlap on a CU,
+    // a full round of 256*w tiles takes BM*BN*(two_a + two_b*K).  per_cu = 0
+    // marks a control or experimental build that is never chosen.
     int per_cu;
     double one_a, one_b, two_a, two_b;
     // General form C = alpha op(A) op(B) + beta C, by operand layout
@@ -122,13 +128,14 @@ using DlConv = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::OCC
                       T::STAGES, T::KSPLIT, T::SWIZZLE, false, true, false, T::BIL, true>;
 
 #define SGEMM_CFG(T, name, per_cu, a1, b1, a2, b2) \
-    { name, T::BM, T::BN, T::BK, T::NT, (const void*)&sgemm_mfma_kernel<T>, per_cu, a1, b1, a2, b2 }
+    { name, T::BM, T::BN, T::BK, T::NT, T::WG_PER_CU, (const void*)&sgemm_mfma_kernel<T>, per_cu, \
+      a1, b1, a2, b2 }
 #define SGEMM_DL_CFG(T, name, per_cu, a1, b1, a2, b2)                                        \
-    { name, T::BM, T::BN, T::BK, T::NT, (const void*)&sgemm_mfma_dl_kernel<T>, per_cu, a1, b1, \
-      a2, b2 }
+    { name, T::BM, T::BN, T::BK, T::NT, T::WG_PER_CU, (const void*)&sgemm_mfma_dl_kernel<T>, \
+      per_cu, a1, b1, a2, b2 }
 #define SGEMM_DLX_CFG(T, name, per_cu, a1, b1, a2, b2)                                       \
-    { name, T::BM, T::BN, T::BK, T::NT, (const void*)&sgemm_mfma_dl_kernel<T>, per_cu, a1, b1, \
-      a2, b2,                                                                                 \
+    { name, T::BM, T::BN, T::BK, T::NT, T::WG_PER_CU, (const void*)&sgemm_mfma_dl_kernel<T>, \
+      per_cu, a1, b1, a2, b2,                                                                 \
       { (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, false, false>>,                       \
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, false>>,                        \
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, false, true>>,                        \
@@ -136,32 +143,35 @@ using DlConv = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::OCC
       (const void*)&sgemm_mfma_dl_kernel<DlConv<T>> }
 
 const ConfigEntry kConfigs[] = {
-    SGEMM_CFG(Cfg256x128, "mfma32_256x128x16_w2x2", 1, 3.8386e-04, 4.2165e-06, 3.9847e-04, 8.1269e-06),
-    SGEMM_CFG(Cfg128x128, "mfma32_128x128x16_w2x2", 2, 4.3762e-04, 4.5313e-06, 4.8419e-04, 8.3435e-06),
-    SGEMM_CFG(Cfg64x64, "mfma32_64x64x16_w2x2", 2, 0.0000e+00, 9.0826e-06, 9.5395e-04, 9.8877e-06),
-    SGEMM_CFG(Cfg256x256, "mfma32_256x256x16_w2x4", 1, 1.9301e-04, 3.7992e-06, 3.4525e-04, 7.5872e-06),
-    SGEMM_CFG(Cfg256x256k32, "mfma32_256x256x32_w2x4", 1, 1.9927e-04, 3.7600e-06, 3.6440e-04, 7.5142e-06),
-    SGEMM_CFG(Cfg128x128k32, "mfma32_128x128x32_w2x2", 2, 3.9461e-04, 4.5436e-06, 5.7746e-04, 7.8146e-06),
-    SGEMM_CFG(Cfg128x128k32m16, "mfma16_128x128x32_w2x2", 2, 3.7491e-04, 4.7511e-06, 5.8424e-04, 8.1157e-06),
-    SGEMM_CFG(Cfg64x64k32m16, "mfma16_64x64x32_w2x2", 2, 6.9501e-04, 6.4427e-06, 1.0260e-03, 9.8135e-06),
-    SGEMM_CFG(Cfg256x256m32w1, "mfma32_256x256x16_w2x2", 1, 2.0224e-04, 3.9503e-06, 3.9565e-04, 7.8758e-06),
-    SGEMM_CFG(Cfg256x256k32m32w1, "mfma32_256x256x32_w2x2", 1, 2.2312e-04, 3.9043e-06, 4.1389e-04, 7.8000e-06),
-    SGEMM_DLX_CFG(Dl256x256k32m32, "dl32_256x256x32_w2x4", 1, 2.1036e-04, 3.4720e-06, 3.7595e-04, 6.9415e-06),
-    SGEMM_DL_CFG(Dl256x256k16m32, "dl32_256x256x16_w2x4", 1, 2.0071e-04, 3.4849e-06, 3.6338e-04, 6.9601e-06),
-    SGEMM_DL_CFG(Dl256x128k32m32, "dl32_256x128x32_w2x2", 1, 3.5631e-04, 3.7684e-06, 5.3476e-04, 7.5500e-06),
-    SGEMM_DLX_CFG(Dl128x128k32m32, "dl32_128x128x32_w2x2", 2, 4.3123e-04, 3.9272e-06, 5.4574e-04, 6.9695e-06),
+    SGEMM_CFG(Cfg256x128, "mfma32_256x128x16_w2x2", 1, 3.6505e-04, 4.2029e-06, 4.1134e-04, 8.0806e-06),
+    SGEMM_CFG(Cfg128x128, "mfma32_128x128x16_w2x2", 3, 4.3004e-04, 4.5225e-06, 6.6566e-04, 1.2010e-05),
+    SGEMM_CFG(Cfg64x64, "mfma32_64x64x16_w2x2", 4, 0.0000e+00, 8.9392e-06, 1.5698e-03, 1.7660e-05),
+    SGEMM_CFG(Cfg256x256, "mfma32_256x256x16_w2x4", 1, 1.9697e-04, 3.7832e-06, 3.4747e-04, 7.5724e-06),
+    SGEMM_CFG(Cfg256x256k32, "mfma32_256x256x32_w2x4", 1, 2.0272e-04, 3.7449e-06, 3.6204e-04, 7.4854e-06),
+    SGEMM_CFG(Cfg128x128k32, "mfma32_128x128x32_w2x2", 2, 4.0454e-04, 4.5185e-06, 5.8699e-04, 7.7883e-06),
+    SGEMM_CFG(Cfg128x128k32m16, "mfma16_128x128x32_w2x2", 2, 3.8094e-04, 4.7398e-06, 5.6840e-04, 8.1136e-06),
+    SGEMM_CFG(Cfg64x64k32m16, "mfma16_64x64x32_w2x2", 4, 6.8628e-04, 6.4584e-06, 1.5598e-03, 1.8572e-05),
+    SGEMM_CFG(Cfg256x256m32w1, "mfma32_256x256x16_w2x2", 1, 2.1097e-04, 3.9263e-06, 3.9320e-04, 7.8470e-06),
+    SGEMM_CFG(Cfg256x256k32m32w1, "mfma32_256x256x32_w2x2", 1, 2.2194e-04, 3.8922e-06, 4.1654e-04, 7.7681e-06),
+    SGEMM_DLX_CFG(Dl256x256k32m32, "dl32_256x256x32_w2x4", 1, 2.2637e-04, 3.4025e-06, 3.9250e-04, 6.8025e-06),
+    SGEMM_DL_CFG(Dl256x256k16m32, "dl32_256x256x16_w2x4", 1, 2.1670e-04, 3.4090e-06, 3.7145e-04, 6.8345e-06),
+    SGEMM_DL_CFG(Dl256x128k32m32, "dl32_256x128x32_w2x2", 1, 3.1727e-04, 3.7384e-06, 4.3118e-04, 7.4863e-06),
+    SGEMM_DLX_CFG(Dl128x128k32m32, "dl32_128x128x32_w2x2", 2, 3.9928e-04, 3.8776e-06, 4.8043e-04, 7.0650e-06),
     SGEMM_DL_CFG(Dl256x256k32m32Plain, "dl32_256x256x32_w2x4_unswizzled", 0, 0, 0, 0, 0),
-    SGEMM_DL_CFG(Dl128x128k32m32s4, "dl32_128x128x32_w2x2_s4", 1, 4.5364e-04, 4.1307e-06, 6.7966e-04, 8.2867e-06),
-    SGEMM_DLX_CFG(Dl64x64k32m32s4, "dl32_64x64x32_w2x2_s4", 2, 8.8462e-04, 5.0915e-06, 1.1556e-03, 7.6853e-06),
-    SGEMM_DLX_CFG(Dl256x192k32m32, "dl32_256x192x32_w4x2", 1, 2.1452e-04, 3.5334e-06, 3.5426e-04, 7.0652e-06),
-    SGEMM_DLX_CFG(Dl192x256k32m32, "dl32_192x256x32_w2x4", 1, 2.1940e-04, 3.4913e-06, 3.5898e-04, 6.9860e-06),
-    SGEMM_DL_CFG(Dl64x64k64m32s4, "dl32_64x64x64_w2x2_s4", 1, 9.1894e-04, 4.9619e-06, 1.4383e-03, 9.9365e-06),
-    SGEMM_DL_CFG(Dl64x64k32m32s8, "dl32_64x64x32_w2x2_s8", 1, 1.0063e-03, 5.0706e-06, 1.6064e-03, 1.0141e-05),
-    SGEMM_DL_CFG(Dl128x64k32m32s4, "dl32_128x64x32_w2x2_s4", 1, 6.1517e-04, 4.5946e-06, 9.0588e-04, 9.2191e-06),
-    SGEMM_DL_CFG(Dl128x128k64m32s2, "dl32_128x128x64_w2x2", 1, 4.9542e-04, 3.9598e-06, 7.7019e-04, 7.9307e-06),
-    SGEMM_DLX_CFG(Dl64x64k64m32s4x2, "dl32_64x64x64_w2x2_s4_k2", 1, 1.0666e-03, 4.1455e-06, 1.7638e-03, 8.2600e-06),
-    SGEMM_DL_CFG(Dl64x64k32m32s4x2, "dl32_64x64x32_w2x2_s4_k2", 2, 9.7944e-04, 5.1438e-06, 1.4432e-03, 8.2780e-06),
-    SGEMM_DLX_CFG(Dl128x64k64m32s2x2, "dl32_128x64x64_w2x2_s2_k2", 1, 6.7196e-04, 3.8131e-06, 1.0361e-03, 7.6395e-06),
+    SGEMM_DL_CFG(Dl128x128k32m32s4, "dl32_128x128x32_w2x2_s4", 1, 4.0428e-04, 4.0995e-06, 5.6909e-04, 8.2213e-06),
+    SGEMM_DLX_CFG(Dl64x64k32m32s4, "dl32_64x64x32_w2x2_s4", 2, 7.2952e-04, 5.2118e-06, 1.0443e-03, 7.7747e-06),
+    SGEMM_DLX_CFG(Dl256x192k32m32, "dl32_256x192x32_w4x2", 1, 2.1701e-04, 3.5203e-06, 3.5759e-04, 7.0372e-06),
+    SGEMM_DLX_CFG(Dl192x256k32m32, "dl32_192x256x32_w2x4", 1, 2.1944e-04, 3.4698e-06, 3.6160e-04, 6.9358e-06),
+    SGEMM_DL_CFG(Dl64x64k64m32s4, "dl32_64x64x64_w2x2_s4", 1, 7.8433e-04, 5.0220e-06, 1.2553e-03, 1.0008e-05),
+    SGEMM_DL_CFG(Dl64x64k32m32s8, "dl32_64x64x32_w2x2_s8", 1, 8.0675e-04, 5.3391e-06, 1.2985e-03, 1.0657e-05),
+    SGEMM_DL_CFG(Dl128x64k32m32s4, "dl32_128x64x32_w2x2_s4", 1, 5.0258e-04, 4.5911e-06, 8.2285e-04, 9.1651e-06),
+    SGEMM_DL_CFG(Dl128x128k64m32s2, "dl32_128x128x64_w2x2", 1, 4.4821e-04, 3.8893e-06, 6.4915e-04, 7.8117e-06),
+    SGEMM_DLX_CFG(Dl64x64k64m32s4x2, "dl32_64x64x64_w2x2_s4_k2", 1, 9.3095e-04, 4.2275e-06, 1.5347e-03, 8.4092e-06),
+    SGEMM_DL_CFG(Dl64x64k32m32s4x2, "dl32_64x64x32_w2x2_s4_k2", 2, 8.4221e-04, 5.1424e-06, 1.2486e-03, 8.5543e-06),
+    SGEMM_DLX_CFG(Dl128x64k64m32s2x2, "dl32_128x64x64_w2x2_s2_k2", 1, 5.7721e-04, 3.8502e-06, 9.6700e-04, 7.6880e-06),
+    SGEMM_DLX_CFG(Dl128x128k16o4, "dl32_128x128x16_w2x2_o4", 4, 3.8746e-04, 3.7646e-06, 9.6869e-04, 1.3744e-05),
+    SGEMM_DL_CFG(Dl128x128k16o3s3, "dl32_128x128x16_w2x2_s3_o3", 3, 3.6668e-04, 4.2300e-06, 5.9514e-04, 1.0602e-05),
+    SGEMM_DLX_CFG(Dl64x64k32o4, "dl32_64x64x32_w2x2_o4", 4, 7.5377e-04, 4.5803e-06, 1.6470e-03, 1.4589e-05),
 };
 #undef SGEMM_CFG
 #undef SGEMM_DL_CFG
@@ -233,18 +243,25 @@ int validate(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, int64
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Predicted time of one launch: whole rounds of tiles at the fitted round
-// times; a last round of at most 256 tiles on a two-per-CU configuration runs
-// at the one-per-CU time.
+// Predicted time of one launch: whole rounds of 256 * per_cu tiles at the
+// fitted full-round time; a last, partial round that puts j of the w
+// workgroups on the busiest CU takes the one-per-CU time plus (j - 1) / (w - 1)
+// of the difference to a full round.
 double predict_us(const ConfigEntry& c, int64_t M, int64_t N, int64_t K, int64_t batch) {
     const double tiles = (double)(ceil_div(M, c.bm) * ceil_div(N, c.bn)) * (double)batch;
     const double area = (double)c.bm * c.bn;
     const double one = area * (c.one_a + c.one_b * (double)K);
-    const double two = area * (c.two_a + c.two_b * (double)K);
-    if (c.per_cu < 2) return std::ceil(tiles / kNumCu) * one;
-    const double full = std::floor(tiles / (2.0 * kNumCu));
-    const double rest = tiles - full * 2.0 * kNumCu;
-    return full * two + (rest == 0.0 ? 0.0 : rest <= kNumCu ? one : two);
+    const double full_t = area * (c.two_a + c.two_b * (double)K);
+    const int w = c.per_cu;
+    if (w < 2) return std::ceil(tiles / kNumCu) * one;
+    const double full = std::floor(tiles / ((double)w * kNumCu));
+    const double rest = tiles - full * (double)w * kNumCu;
+    double last = 0.0;
+    if (rest > 0.0) {
+        const double j = std::ceil(rest / kNumCu);
+        last = one + (full_t - one) * (j - 1.0) / (double)(w - 1);
+    }
+    return full * full_t + last;
 }
 
 // Shape -> configuration: the smallest predicted time; control builds are
@@ -267,24 +284,18 @@ int choose_config(int64_t M, int64_t N, int64_t K, int64_t batch, bool general =
 
 // Convolution tiles: the smallest predicted time for the implicit GEMM
 // (M = N*P*Q, N = output channels, K = R*S*C); a tile whose BK does not divide
-// C gathers through registers and is counted four times slower.  Predictions
-// within 3 % of the best (the model's accuracy on these kernels) go to the
-// larger tile, which rebuilds fewer gather offsets per multiply-add.
+// C gathers through registers and is counted four times slower.
 int choose_conv_config(int64_t M, int64_t N, int64_t K, int64_t C) {
-    double best_us = -1.0;
-    for (int idx = 0; idx < kNumConfigs; ++idx) {
-        const ConfigEntry& c = kConfigs[idx];
-        if (c.per_cu == 0 || c.conv == nullptr) continue;
-        const double t = predict_us(c, M, N, K, 1) * (C % c.bk == 0 ? 1.0 : 4.0);
-        if (best_us < 0.0 || t < best_us) best_us = t;
-    }
     int best = -1;
+    double best_us = 0.0;
     for (int idx = 0; idx < kNumConfigs; ++idx) {
         const ConfigEntry& c = kConfigs[idx];
         if (c.per_cu == 0 || c.conv == nullptr) continue;
         const double t = predict_us(c, M, N, K, 1) * (C % c.bk == 0 ? 1.0 : 4.0);
-        if (t > best_us * 1.03) continue;
-        if (best < 0 || c.bm * c.bn > kConfigs[best].bm * kConfigs[best].bn) best = idx;
+        if (best < 0 || t < best_us * (1.0 - 1e-9)) {
+            best_us = t;
+            best = idx;
+        }
     }
     return best;
 }
@@ -572,6 +583,20 @@ int sgemm_select_general_config(int64_t M, int64_t N, int64_t K, int64_t batch) 
     if (M > kMaxDim || N > kMaxDim || K > kMaxDim || batch > kMaxDim)
         return SGEMM_STATUS_SIZE_OVERFLOW;
     return choose_config(M, N, K, batch, true);
+}
+
+int sgemm_config_workgroups_per_cu(int config) {
+    if (config < 0 || config >= kNumConfigs) return SGEMM_STATUS_INVALID_CONFIG;
+    const ConfigEntry& c = kConfigs[config];
+    // The runtime's answer counts the registers the compiler actually used;
+    // the launch bound in the table is only the floor it guarantees.
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, c.kernel, c.threads, 0) ==
+            hipSuccess &&
+        blocks > 0)
+        return blocks;
+    (void)hipGetLastError();
+    return c.wg_per_cu;
 }
 
 int sgemm_config_selectable(int config) {
