@@ -461,8 +461,11 @@ def bench_conv(args) -> int:
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default: 50 for GEMMs, 200 for the window and convolution)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed steps first (default: 30 for GEMMs, 200 for the window and "
+                         "convolution, about 30 ms of work either way, so clocks have settled)")
     ap.add_argument("--path", choices=["mfma", "valu", "window"], default="mfma",
                     help="GEMM path (window: counter summaries of the window kernel only)")
     ap.add_argument("--workload", default="square4096")
@@ -501,6 +504,11 @@ def main(argv=None) -> int:
         return 2
 
     from workloads import CONV_WORKLOADS, WINDOW_WORKLOADS
+    short = args.workload in WINDOW_WORKLOADS or args.workload in CONV_WORKLOADS
+    if args.steps is None:
+        args.steps = 200 if short else 50
+    if args.warmup is None:
+        args.warmup = 200 if short else 30
     if args.workload in WINDOW_WORKLOADS:
         return bench_window(args)
     if args.workload in CONV_WORKLOADS:
