@@ -499,8 +499,8 @@ def main(argv=None) -> int:
         return 0
 
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build runs on a single MI355X and has no "
-              "multi-GPU path (asked for --gpus %d)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU: the library runs each call on a single MI355X and "
+              "has no multi-GPU path (asked for --gpus %d)" % args.gpus, file=sys.stderr)
         return 2
 
     from workloads import CONV_WORKLOADS, WINDOW_WORKLOADS

@@ -1,5 +1,6 @@
 """CPU oracle for C = A x B in FP32 inputs with an FP64 result (and for the
-sliding window sum and the 2-D convolution built on the same staging idea).
+sliding window sum, the 2-D convolution and blockwise attention built on the
+same staging idea).
 
 TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
 benchmark's CPU-baseline leg may import this package.  The GPU library never
@@ -61,6 +62,12 @@ def _load():
     lib.oracle_conv2d_nhwc_f64.restype = ctypes.c_int
     lib.oracle_conv2d_nhwc_entries_f64.argtypes = [i64] * 13 + [p, p, i64, p, p, p]
     lib.oracle_conv2d_nhwc_entries_f64.restype = ctypes.c_int
+    lib.oracle_attention_f64.argtypes = [i64, i64, i64, i64, p, p, p, ctypes.c_float,
+                                         ctypes.c_int, p, p, p]
+    lib.oracle_attention_f64.restype = ctypes.c_int
+    lib.oracle_attention_rows_f64.argtypes = [i64, i64, i64, i64, p, p, p, ctypes.c_float,
+                                              ctypes.c_int, i64, p, p, p, p]
+    lib.oracle_attention_rows_f64.restype = ctypes.c_int
     lib.oracle_sgemm_ex_f64.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64,
                                         ctypes.c_float, p, i64, p, i64, ctypes.c_float, p, i64,
                                         p, p, i64, ctypes.c_int]
@@ -304,3 +311,44 @@ def conv2d_nhwc_entries_f64(x, wt, N: int, H: int, W: int, C: int, K: int, R: in
         if st != 0:
             raise ValueError("invalid convolution arguments")
     return y, yabs
+
+
+def attention_f64(Q, K, V, H: int, Sq: int, Skv: int, D: int, scale: float, causal: bool = False):
+    """Scaled dot-product attention per head (see oracle.c): Q (H*Sq*D floats),
+    K and V (H*Skv*D floats), row-major per head.  Returns FP64 (O, mag, smax):
+    O and mag shaped (H, Sq, D), smax shaped (H, Sq)."""
+    lib = _load()
+    q, k, v = _f32_flat(Q), _f32_flat(K), _f32_flat(V)
+    if min(H, Sq, Skv, D) < 0:
+        raise ValueError("negative size")
+    if q.size < H * Sq * D or k.size < H * Skv * D or v.size < H * Skv * D:
+        raise ValueError("operand buffer too small")
+    O = np.empty((H, Sq, D), dtype=np.float64)
+    mag = np.empty((H, Sq, D), dtype=np.float64)
+    smax = np.empty((H, Sq), dtype=np.float64)
+    st = lib.oracle_attention_f64(H, Sq, Skv, D, _ptr(q), _ptr(k), _ptr(v), float(scale),
+                                  int(bool(causal)), _ptr(O), _ptr(mag), _ptr(smax))
+    if st != 0:
+        raise ValueError("invalid attention arguments")
+    return O, mag, smax
+
+
+def attention_rows_f64(Q, K, V, H: int, Sq: int, Skv: int, D: int, scale: float, rows,
+                       causal: bool = False):
+    """Selected rows (flat index h * Sq + i) of the attention above; returns
+    FP64 (O, mag, smax) shaped (len(rows), D), (len(rows), D), (len(rows),)."""
+    lib = _load()
+    q, k, v = _f32_flat(Q), _f32_flat(K), _f32_flat(V)
+    rr = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).ravel())
+    if rr.size and (rr.min() < 0 or rr.max() >= H * Sq):
+        raise ValueError("row index out of range")
+    O = np.empty((rr.size, D), dtype=np.float64)
+    mag = np.empty((rr.size, D), dtype=np.float64)
+    smax = np.empty(rr.size, dtype=np.float64)
+    if rr.size:
+        st = lib.oracle_attention_rows_f64(H, Sq, Skv, D, _ptr(q), _ptr(k), _ptr(v),
+                                           float(scale), int(bool(causal)), rr.size, _ptr(rr),
+                                           _ptr(O), _ptr(mag), _ptr(smax))
+        if st != 0:
+            raise ValueError("invalid attention arguments")
+    return O, mag, smax

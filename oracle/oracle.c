@@ -354,6 +354,107 @@ int oracle_conv2d_nhwc_entries_f64(int64_t N, int64_t H, int64_t W, int64_t C, i
     return 0;
 }
 
+/*
+ * Attention, the "FlashAttention" row of the tiled-kernel table in "Tiling
+ * Strategies", section 5 (tiled: Q, K and V blocks along the sequence;
+ * reused: K and V blocks across query rows).  The pages give the tiling, not
+ * the formula; this is scaled dot-product attention, one head at a time:
+ *   Q[h][i][d] (Sq x D), K[h][j][d], V[h][j][d] (Skv x D), O[h][i][d] (Sq x D),
+ *   s_ij = scale * sum_d Q[h][i][d] K[h][j][d],   j allowed when j < Skv and,
+ *          if causal, j <= i,
+ *   p_ij = exp(s_ij - max_j s_ij) over the allowed j,
+ *   O[h][i][d] = sum_j p_ij V[h][j][d] / sum_j p_ij,
+ * all in FP64 (the tiled, online-softmax form computes the same quantity).
+ * A row with no allowed key (Skv = 0) is all zeros.  Also returned, per
+ * output, mag = sum_j p_ij |V[h][j][d]| / sum_j p_ij (the scale of the
+ * acceptance bound), and per row smax = max over allowed j of
+ * scale * sum_d |Q[h][i][d]| |K[h][j][d]| (the size of the scores' rounding).
+ * O and mag hold H*Sq*D doubles, smax H*Sq (mag and smax may be NULL).
+ * Returns 0, or -1 for negative sizes.
+ */
+static void attention_row(int64_t Skv, int64_t D, double scale, int causal, int64_t i,
+                          const float *q, const float *K, const float *V, double *s,
+                          double *o, double *mag, double *smax) {
+    const int64_t nj = causal ? (i + 1 < Skv ? i + 1 : Skv) : Skv;
+    double m = -INFINITY, sm = 0.0;
+    for (int64_t j = 0; j < nj; ++j) {
+        double dot = 0.0, dabs = 0.0;
+        for (int64_t d = 0; d < D; ++d) {
+            dot += (double)q[d] * (double)K[j * D + d];
+            dabs += fabs((double)q[d] * (double)K[j * D + d]);
+        }
+        s[j] = scale * dot;
+        if (s[j] > m) m = s[j];
+        if (fabs(scale) * dabs > sm) sm = fabs(scale) * dabs;
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < nj; ++j) {
+        s[j] = exp(s[j] - m);  /* p_ij */
+        l += s[j];
+    }
+    for (int64_t d = 0; d < D; ++d) {
+        double acc = 0.0, accabs = 0.0;
+        for (int64_t j = 0; j < nj; ++j) {
+            acc += s[j] * (double)V[j * D + d];
+            accabs += s[j] * fabs((double)V[j * D + d]);
+        }
+        o[d] = nj > 0 ? acc / l : 0.0;
+        if (mag) mag[d] = nj > 0 ? accabs / l : 0.0;
+    }
+    if (smax) *smax = sm;
+}
+
+int oracle_attention_f64(int64_t H, int64_t Sq, int64_t Skv, int64_t D, const float *Q,
+                         const float *K, const float *V, float scale, int causal, double *O,
+                         double *mag, double *smax) {
+    if (H < 0 || Sq < 0 || Skv < 0 || D < 0) return -1;
+#ifdef _OPENMP
+#pragma omp parallel
+#endif
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Skv > 0 ? Skv : 1));
+#ifdef _OPENMP
+#pragma omp for collapse(2) schedule(static)
+#endif
+        for (int64_t h = 0; h < H; ++h) {
+            for (int64_t i = 0; i < Sq; ++i) {
+                const int64_t row = h * Sq + i;
+                attention_row(Skv, D, (double)scale, causal, i, Q + row * D, K + h * Skv * D,
+                              V + h * Skv * D, s, O + row * D, mag ? mag + row * D : NULL,
+                              smax ? smax + row : NULL);
+            }
+        }
+        free(s);
+    }
+    return 0;
+}
+
+/* Selected rows (h, i) of the attention above: rows[e] = h * Sq + i; O, mag
+ * hold count * D doubles, smax count.  Returns 0 or -1. */
+int oracle_attention_rows_f64(int64_t H, int64_t Sq, int64_t Skv, int64_t D, const float *Q,
+                              const float *K, const float *V, float scale, int causal,
+                              int64_t count, const int64_t *rows, double *O, double *mag,
+                              double *smax) {
+    if (H < 0 || Sq < 0 || Skv < 0 || D < 0) return -1;
+#ifdef _OPENMP
+#pragma omp parallel
+#endif
+    {
+        double *s = (double *)malloc(sizeof(double) * (size_t)(Skv > 0 ? Skv : 1));
+#ifdef _OPENMP
+#pragma omp for schedule(static)
+#endif
+        for (int64_t e = 0; e < count; ++e) {
+            const int64_t h = rows[e] / (Sq > 0 ? Sq : 1);
+            const int64_t i = rows[e] - h * Sq;
+            attention_row(Skv, D, (double)scale, causal, i, Q + rows[e] * D, K + h * Skv * D,
+                          V + h * Skv * D, s, O + e * D, mag + e * D, smax + e);
+        }
+        free(s);
+    }
+    return 0;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
     return omp_get_max_threads();
