@@ -215,3 +215,17 @@ def test_conv2d_host_logic_and_argument_errors():
     assert call(1, 2, 2, 16, 16, 5, 5, None, None, None) == 0         # P = Q = 0
     assert call(1, 8, 8, 16, 0, 3, 3, None, None, None) == 0          # no output channels
     assert lib.conv2d_config_available(-1) == -7
+
+
+def test_attention_argument_errors():
+    lib = _native.lib()
+    F = FAKE
+    assert lib.attention_fwd(-1, 4, 4, 64, F, F, F, F, 1.0, 0, 0) == -1
+    assert lib.attention_fwd(1, 4, 4, 96, F, F, F, F, 1.0, 0, 0) == -1       # head dim 64 or 128
+    assert lib.attention_fwd(1, 4, 4, 64, F, F, F, F, float("inf"), 0, 0) == -1
+    assert lib.attention_fwd(1, 4, 4, 64, F, F, F, F, 1.0, 2, 0) == -8
+    assert lib.attention_fwd(1, 2 ** 31, 4, 64, F, F, F, F, 1.0, 0, 0) == -4
+    assert lib.attention_fwd(1, 4, 4, 64, None, F, F, F, 1.0, 0, 0) == -3
+    assert lib.attention_fwd(1, 4, 4, 64, F, F, F, None, 1.0, 0, 0) == -3
+    assert lib.attention_fwd(0, 4, 4, 64, None, None, None, None, 1.0, 0, 0) == 0
+    assert lib.attention_fwd(3, 0, 4, 128, None, None, None, None, 1.0, 1, 0) == 0

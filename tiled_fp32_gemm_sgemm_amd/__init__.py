@@ -1,12 +1,13 @@
 """FP32 matrix multiply C = A x B for the AMD Instinct MI355X (gfx950), plus the
-sliding window sum that the same pages use to introduce cooperative staging and
-the 2-D convolution (tiling beyond GEMM) run as an implicit product.
+sliding window sum that the same pages use to introduce cooperative staging,
+and two cases of tiling beyond GEMM: the 2-D convolution run as an implicit
+product and blockwise attention.
 
 The product runs in libsgemm.so (hand-written HIP kernels behind the C ABI
 in include/sgemm.h); this package only passes tensors' device addresses,
 leading dimensions and the current stream to it.
 """
-from .api import (autotune, autotune_raw, config_has_general_form, config_info,
+from .api import (attention, attention_raw, autotune, autotune_raw, config_has_general_form, config_info,
                   conv2d_config_available, conv2d_nhwc, conv2d_nhwc_raw, conv2d_output_size,
                   conv2d_select_config,
                   config_selectable, num_configs, predict_us, select_config,
@@ -20,5 +21,6 @@ __all__ = ["sgemm", "sgemm_strided_batched", "sgemm_raw", "sgemm_strided_batched
            "autotune", "autotune_raw", "sgemm_ex", "sgemm_ex_raw", "config_has_general_form",
            "select_general_config", "window_sum", "window_sum_raw", "conv2d_nhwc",
            "conv2d_nhwc_raw", "conv2d_output_size", "conv2d_config_available",
-           "conv2d_select_config", "workgroups_per_cu", "SgemmError",
+           "conv2d_select_config", "workgroups_per_cu", "attention", "attention_raw",
+           "SgemmError",
            "status_string"]

@@ -1,5 +1,5 @@
-"""ctypes view of libsgemm.so (the C ABI in include/sgemm.h, window_sum.h and
-conv2d.h).
+"""ctypes view of libsgemm.so (the C ABI in include/sgemm.h, window_sum.h,
+conv2d.h and attention.h).
 
 Argument marshalling only: every operation runs in the HIP library.  If the
 library has not been built, loading fails with an error that says so; there is
@@ -81,6 +81,8 @@ _SIGS = {
                                 ctypes.c_int),
     "conv2d_config_available": ([ctypes.c_int], ctypes.c_int),
     "conv2d_select_config": ([_i64] * 13, ctypes.c_int),
+    "attention_fwd": ([_i64, _i64, _i64, _i64, _p, _p, _p, _p, ctypes.c_float, ctypes.c_int, _p],
+                      ctypes.c_int),
 }
 
 

@@ -371,3 +371,41 @@ def conv2d_select_config(N, H, W, C, K, R, S, pad=0, stride=1, dil=1) -> int:
     if st < 0:
         raise _native.SgemmError(st, "conv2d_select_config")
     return st
+
+
+def attention_raw(BH, Sq, Skv, D, q_ptr, k_ptr, v_ptr, o_ptr, scale, causal=False,
+                  stream=0) -> int:
+    """Blockwise attention on device addresses (include/attention.h); returns
+    the status."""
+    return _native.lib().attention_fwd(BH, Sq, Skv, D, q_ptr, k_ptr, v_ptr, o_ptr, float(scale),
+                                       int(bool(causal)), stream)
+
+
+def attention(q, k, v, scale=None, causal=False, out=None, stream=None):
+    """softmax(scale q k^T) v per head for contiguous float32 CUDA tensors
+    shaped (..., S, D) (leading dimensions are heads); scale defaults to
+    1/sqrt(D).  Returns a tensor shaped like q."""
+    import math
+    import torch
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.device.type != "cuda":
+            raise TypeError("%s must be a float32 CUDA tensor" % name)
+        if t.dim() < 2 or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous tensor of at least 2 dimensions" % name)
+    if q.shape[:-2] != k.shape[:-2] or k.shape != v.shape or q.shape[-1] != k.shape[-1]:
+        raise ValueError("shapes do not match: q %s, k %s, v %s"
+                         % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    Sq, D = q.shape[-2], q.shape[-1]
+    Skv = k.shape[-2]
+    BH = math.prod(q.shape[:-2])
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape or not out.is_contiguous():
+        raise ValueError("out must be a contiguous tensor shaped like q")
+    with torch.cuda.device(q.device):
+        st = attention_raw(BH, Sq, Skv, D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                           out.data_ptr(), scale, causal, _stream_handle(stream, q.device))
+    _check(st, "attention_fwd")
+    return out

@@ -171,6 +171,51 @@ def conv_operands(w: ConvWorkload):
     return x, wt
 
 
+@dataclass(frozen=True)
+class AttnWorkload:
+    """Attention per head: Q (BH, Sq, D), K and V (BH, Skv, D)."""
+    name: str
+    BH: int
+    Sq: int
+    Skv: int
+    D: int
+    causal: bool
+    seed: int
+    about: str = field(default="", compare=False)
+
+    @property
+    def flops(self) -> int:
+        # two products (scores, values) over the allowed query/key pairs
+        if self.causal:
+            pairs = sum(min(i + 1, self.Skv) for i in range(self.Sq))
+        else:
+            pairs = self.Sq * self.Skv
+        return 4 * self.BH * pairs * self.D
+
+    def describe(self) -> str:
+        return ("attention BH=%d Sq=%d Skv=%d D=%d causal=%d q,k,v~normal(0,1) seed=%d"
+                % (self.BH, self.Sq, self.Skv, self.D, int(self.causal), self.seed))
+
+
+# Batch 4 x 16 heads of 2048 tokens, head dimension 128 (137 GFLOP without the
+# mask), the same with the causal mask, and 32 heads of 4096 tokens at D = 64.
+ATTN_WORKLOADS = {
+    "attn_s2048_d128": AttnWorkload("attn_s2048_d128", 64, 2048, 2048, 128, False, 11),
+    "attn_s2048_d128_causal": AttnWorkload("attn_s2048_d128_causal", 64, 2048, 2048, 128, True,
+                                           12),
+    "attn_s4096_d64": AttnWorkload("attn_s4096_d64", 32, 4096, 4096, 64, False, 13),
+}
+
+
+def attn_operands(w: AttnWorkload):
+    """Flat float32 CPU buffers (Q, K, V), drawn in that order, normal(0, 1)."""
+    gen = torch.Generator("cpu").manual_seed(w.seed)
+    q = draw(gen, w.BH * w.Sq * w.D, "normal")
+    k = draw(gen, w.BH * w.Skv * w.D, "normal")
+    v = draw(gen, w.BH * w.Skv * w.D, "normal")
+    return q, k, v
+
+
 def draw(gen: torch.Generator, n: int, dist: str, scale: float = 1.0) -> torch.Tensor:
     """n float32 values from one of the recipes, using ``gen``."""
     if dist == "uniform":
