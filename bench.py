@@ -4,6 +4,7 @@
                     [--workload square4096] [--no-cpu-baseline]
     python bench.py --workload window5      (sliding window sums, GB/s)
     python bench.py --workload conv3x3_c256 (2-D convolution, TFLOP/s)
+    python bench.py --workload attn_s2048_d128 (blockwise attention, TFLOP/s)
 
 One step is one call of the library on the named workload (default: the
 4096^3 product, A and B ~ normal(0,1)/sqrt(K), seed 1), inputs resident in
@@ -46,6 +47,8 @@ GEMM_SOURCES = ("tile_common.hpp", "mfma_dl_kernel.hpp", "mfma_kernel.hpp", "val
 WINDOW_SOURCES = ("window.hip", "window_kernel.hpp", "tile_common.hpp")
 WINDOW_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "window_sum_window5_counters.txt")
 CONV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv2d_conv3x3_c256_counters.txt")
+ATTN_SOURCES = ("attention_kernel.hpp", "mfma_dl_kernel.hpp", "mfma_kernel.hpp", "tile_common.hpp")
+ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_attn_s2048_d128_counters.txt")
 
 
 def kernel_source_hash(names=GEMM_SOURCES) -> str:
@@ -146,16 +149,20 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
     from workloads import WINDOW_WORKLOADS, WORKLOADS
     from tiled_fp32_gemm_sgemm_amd import model
     import tiled_fp32_gemm_sgemm_amd as sg
-    from workloads import CONV_WORKLOADS
+    from workloads import ATTN_WORKLOADS, CONV_WORKLOADS
     window = workload in WINDOW_WORKLOADS
     conv = workload in CONV_WORKLOADS
+    attn = workload in ATTN_WORKLOADS
     w = (WINDOW_WORKLOADS[workload] if window else
-         CONV_WORKLOADS[workload] if conv else WORKLOADS[workload])
+         CONV_WORKLOADS[workload] if conv else
+         ATTN_WORKLOADS[workload] if attn else WORKLOADS[workload])
     L = ["# rocprofv3 hardware counters, %s path, workload %s" % (path, w.describe()),
          "# commands (one counter pass each, run from the repository root):"]
     L += ["#   " + c for c in commands]
     L.append("kernel_source_sha256_16: %s" % kernel_source_hash(
-        WINDOW_SOURCES if window else GEMM_SOURCES))
+        WINDOW_SOURCES if window else ATTN_SOURCES if attn else GEMM_SOURCES))
+    if attn:
+        L.append("flops_per_launch: %d" % w.flops)
     if conv:
         L.append("flops_per_launch: %d" % w.flops)
     copy_part = "MulFunctor"
@@ -181,6 +188,7 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
               "hbm_bytes_per_launch: %.0f" % hbm,
               "compulsory_bytes: %d" % (w.bytes if window else
                                         conv_compulsory_bytes(w) if conv else
+                                        4 * w.BH * w.D * (2 * w.Sq + 2 * w.Skv) if attn else
                                         model.compulsory_bytes(w.M, w.N, w.K, w.batch))]
     merged = {}
     for c in sq_csvs:
@@ -209,7 +217,17 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
         want = model.mfma_instructions(w.N * P * Q, w.K, w.R * w.S * w.C, info["bm"], info["bn"],
                                        info["bk"], 32, 1)
         L.append("mfma_instructions_closed_form: %d (tile %s)" % (want, info["name"]))
-    if path == "mfma" and not window and not conv:
+    if attn:
+        # Each of the 8 waves issues 2 D v_mfma_f32_32x32x2_f32 per visited
+        # (256-query, 64-key) block pair: D for the scores, D for P V.
+        import math
+        qb = math.ceil(w.Sq / 256)
+        nkv = math.ceil(w.Skv / 64)
+        pairs = sum(min(nkv, (min(w.Sq, 256 * b + 256) - 1) // 64 + 1) if w.causal else nkv
+                    for b in range(qb))
+        L.append("mfma_instructions_closed_form: %d (attention, 256 x 64 blocks)"
+                 % (w.BH * pairs * 8 * 2 * w.D))
+    if path == "mfma" and not window and not conv and not attn:
         cfg = sg.select_config(w.M, w.N, w.K, w.batch) if config is None else config
         info = sg.config_info(cfg)
         mi = 16 if info["name"].startswith("mfma16") else 32
@@ -458,6 +476,122 @@ def bench_conv(args) -> int:
     return 0
 
 
+def attn_cpu_baseline(w, q, k, v, scale, target_s: float = 10.0):
+    """The oracle, untouched, on the first query rows of head 0 (then of the
+    following heads) of the attention workload."""
+    import numpy as np
+    import oracle
+    qn, kn, vn = q.numpy(), k.numpy(), v.numpy()
+
+    def rows_flops(n):
+        rows = np.arange(n, dtype=np.int64)
+        pairs = sum(min(int(r % w.Sq) + 1, w.Skv) if w.causal else w.Skv for r in rows)
+        return rows, 4.0 * pairs * w.D
+
+    n0 = 64
+    rows, _ = rows_flops(n0)
+    t0 = time.perf_counter()
+    oracle.attention_rows_f64(qn, kn, vn, w.BH, w.Sq, w.Skv, w.D, scale, rows, w.causal)
+    dt0 = time.perf_counter() - t0
+    n = int(min(w.BH * w.Sq, max(n0, n0 * target_s / max(dt0, 1e-6))))
+    rows, flops = rows_flops(n)
+    t0 = time.perf_counter()
+    oracle.attention_rows_f64(qn, kn, vn, w.BH, w.Sq, w.Skv, w.D, scale, rows, w.causal)
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(oracle.max_threads()),
+            "kind": "oracle",
+            "sample": "query rows 0..%d (head-major) of %s (%.3g GFLOP) in %.2f s, FP64, OpenMP "
+                      "over rows" % (n - 1, w.name, flops / 1e9, dt),
+            "seconds": dt}
+
+
+def bench_attention(args) -> int:
+    """Blockwise attention: TFLOP/s of the two products over the allowed
+    query/key pairs, against the FP32 matrix peak."""
+    import math
+    import torch
+    from workloads import ATTN_WORKLOADS, attn_operands
+    import tiled_fp32_gemm_sgemm_amd as sg
+
+    w = ATTN_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q_cpu, k_cpu, v_cpu = attn_operands(w)
+    q = q_cpu.to(dev).view(w.BH, w.Sq, w.D)
+    k = k_cpu.to(dev).view(w.BH, w.Skv, w.D)
+    v = v_cpu.to(dev).view(w.BH, w.Skv, w.D)
+    o = torch.empty_like(q)
+    scale = float(torch.tensor(1.0 / math.sqrt(w.D), dtype=torch.float32))
+    stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream
+
+    def step():
+        st = sg.attention_raw(w.BH, w.Sq, w.Skv, w.D, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                              o.data_ptr(), scale, w.causal, handle)
+        if st != 0:
+            raise sg.SgemmError(st, "attention_fwd")
+
+    def timed(fn, n_steps, n_warm):
+        for _ in range(n_warm):
+            fn()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(n_steps):
+            fn()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n_steps
+
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ms = timed(step, args.steps, args.warmup)
+    tflops = w.flops / (ms * 1e-3) / 1e12
+    comparators = {}
+    if not args.no_comparator:
+        q4, k4, v4 = (t.unsqueeze(0) for t in (q, k, v))
+        tms = timed(lambda: torch.nn.functional.scaled_dot_product_attention(
+            q4, k4, v4, is_causal=w.causal, scale=scale), max(3, args.steps // 5), 2)
+        comparators["torch_sdpa_fp32"] = {"tflops": w.flops / (tms * 1e-3) / 1e12,
+                                          "ms_per_step": tms}
+    kernel = "attention_d%d%s" % (w.D, "_causal" if w.causal else "")
+    out = {
+        "metric": "FP32 blockwise attention TFLOP/s (4 D flops per allowed query/key pair)",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_fp32_peak": 100.0 * tflops / PEAK_FP32_TFLOPS,
+        "config": {"workload": w.describe(), "BH": w.BH, "Sq": w.Sq, "Skv": w.Skv, "D": w.D,
+                   "causal": w.causal},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / PEAK_FP32_TFLOPS,
+                     "traffic": (read_traffic(ATTN_TRAFFIC_FILE, ATTN_SOURCES)
+                                 if args.workload == "attn_s2048_d128" else None),
+                     "kernel": kernel, "avg_kernel_ms": ms},
+        "cpu_baseline": (None if args.no_cpu_baseline
+                         else attn_cpu_baseline(w, q_cpu, k_cpu, v_cpu, scale)),
+        "comparators": comparators,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -503,12 +637,14 @@ def main(argv=None) -> int:
               "has no multi-GPU path (asked for --gpus %d)" % args.gpus, file=sys.stderr)
         return 2
 
-    from workloads import CONV_WORKLOADS, WINDOW_WORKLOADS
+    from workloads import ATTN_WORKLOADS, CONV_WORKLOADS, WINDOW_WORKLOADS
     short = args.workload in WINDOW_WORKLOADS or args.workload in CONV_WORKLOADS
     if args.steps is None:
         args.steps = 200 if short else 50
     if args.warmup is None:
         args.warmup = 200 if short else 30
+    if args.workload in ATTN_WORKLOADS:
+        return bench_attention(args)
     if args.workload in WINDOW_WORKLOADS:
         return bench_window(args)
     if args.workload in CONV_WORKLOADS:
