@@ -225,6 +225,7 @@ def test_attention_argument_errors():
     assert lib.attention_fwd(1, 4, 4, 64, F, F, F, F, float("inf"), 0, 0) == -1
     assert lib.attention_fwd(1, 4, 4, 64, F, F, F, F, 1.0, 2, 0) == -8
     assert lib.attention_fwd(1, 2 ** 31, 4, 64, F, F, F, F, 1.0, 0, 0) == -4
+    assert lib.attention_fwd(1, 2 ** 31 - 300, 4, 64, F, F, F, F, 1.0, 0, 0) == -4
     assert lib.attention_fwd(1, 4, 4, 64, None, F, F, F, 1.0, 0, 0) == -3
     assert lib.attention_fwd(1, 4, 4, 64, F, F, F, None, 1.0, 0, 0) == -3
     assert lib.attention_fwd(0, 4, 4, 64, None, None, None, None, 1.0, 0, 0) == 0

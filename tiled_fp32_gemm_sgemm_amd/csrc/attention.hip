@@ -48,7 +48,10 @@ extern "C" int attention_fwd(int64_t BH, int64_t Sq, int64_t Skv, int64_t D, con
                              hipStream_t stream) {
     if (BH < 0 || Sq < 0 || Skv < 0 || (D != 64 && D != 128)) return SGEMM_STATUS_INVALID_SIZE;
     if (causal != 0 && causal != 1) return SGEMM_STATUS_INVALID_OP;
-    if (Sq > INT32_MAX || Skv > INT32_MAX || BH > INT32_MAX) return SGEMM_STATUS_SIZE_OVERFLOW;
+    // Query and key indices are 32-bit in the kernel, one block past the end
+    // included.
+    if (Sq > INT32_MAX - 512 || Skv > INT32_MAX - 512 || BH > INT32_MAX)
+        return SGEMM_STATUS_SIZE_OVERFLOW;
     int64_t t, q_elems, kv_elems;
     if (__builtin_mul_overflow(BH, Sq, &t) || __builtin_mul_overflow(t, D, &q_elems) ||
         __builtin_mul_overflow(BH, Skv, &t) || __builtin_mul_overflow(t, D, &kv_elems))
