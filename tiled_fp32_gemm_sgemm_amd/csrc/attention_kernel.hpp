@@ -27,9 +27,10 @@
 // interleaved (d = DT * i + t for tile t, lane row i) so that one ds_read of DT
 // floats serves all DT tiles.
 //
-// Online softmax, in base 2: scores are scaled by scale * log2(e); per block,
-// m_new = max(m, block max), alpha = 2^(m - m_new), p = 2^(s - m_new),
-// l = alpha l + sum p, O = alpha O + P V; at the end O / l.
+// Online softmax, in base 2: Q is scaled by scale * log2(e) as it is loaded,
+// so the products are base-2 scores; per block, m_new = max(m, block max),
+// alpha = 2^(m - m_new), p = 2^(s - m_new), l = alpha l + sum p,
+// O = alpha O + P V; at the end O / l.
 //
 // LDS layouts.  K block [key][d] with quad q of row R stored at q ^ (R % 16):
 // the 16 lanes of a ds_read_b128 pass read one logical quad of 16 consecutive
@@ -114,8 +115,9 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
         nb = min(nkv, last_q / T::BKV + 1);
     }
 
-    // Q in registers: lane (j, g) holds Q[qi][HALF*g + kk], kk < HALF; zeros
-    // past Sq (those rows are computed and never stored).
+    // Q in registers: lane (j, g) holds Q[qi][HALF*g + kk] * scale * log2(e),
+    // kk < HALF, so the products come out as base-2 scores; zeros past Sq
+    // (those rows are computed and never stored).
     float qreg[T::HALF];
     {
         const float* src = a.Q + q_org + (int64_t)qi * T::D + T::HALF * g;
@@ -124,7 +126,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
             f32x4 v = {0.f, 0.f, 0.f, 0.f};
             if (qi < a.Sq) v = ldg4(src + 4 * c);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) qreg[4 * c + e] = v[e];
+            for (int e = 0; e < 4; ++e) qreg[4 * c + e] = v[e] * a.scale_log2;
         }
     }
 
@@ -203,42 +205,54 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
                     s_acc[n][s & 1] = Op::mma(ka[n][s], qreg[4 * kq + s], s_acc[n][s & 1]);
         }
 
-        // Scale, mask, online softmax.
+        // Mask (only blocks that reach past Skv or, causal, past the wave's
+        // first query can hold a disallowed key), then the online softmax.
+        // Exponentials are v_exp_f32: 2^-inf = 0, and a result below the
+        // normal range flushes to 0, which changes O by less than 2^-126 of
+        // the weighted |V|.
         const int kbase = b * T::BKV;
+        const bool edge = kbase + T::BKV > a.Skv ||
+                          (T::CAUSAL && kbase + T::BKV - 1 > qb * T::BQ + 32 * wave);
         float sv[2][16];
         float mloc = -__builtin_huge_valf();
 #pragma unroll
         for (int n = 0; n < 2; ++n)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int key = kbase + 32 * n + Op::row(r, g);
-                const bool ok = key < a.Skv && (!T::CAUSAL || key <= qi);
-                const float x = (s_acc[n][0][r] + s_acc[n][1][r]) * a.scale_log2;
-                sv[n][r] = ok ? x : -__builtin_huge_valf();
+                sv[n][r] = s_acc[n][0][r] + s_acc[n][1][r];
+                if (edge) {
+                    const int key = kbase + 32 * n + Op::row(r, g);
+                    const bool ok = key < a.Skv && (!T::CAUSAL || key <= qi);
+                    sv[n][r] = ok ? sv[n][r] : -__builtin_huge_valf();
+                }
                 mloc = fmaxf(mloc, sv[n][r]);
             }
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
         const float m_new = fmaxf(m_run, mloc);
-        const bool none = m_new == -__builtin_huge_valf();  // no allowed key yet
-        const float alpha = none ? 1.0f : exp2f(m_run - m_new);
+        // No allowed key yet: shift by 0, every weight is 2^-inf = 0.
+        const float m_use = m_new == -__builtin_huge_valf() ? 0.0f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
         float lsum = 0.0f;
 #pragma unroll
         for (int n = 0; n < 2; ++n)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = sv[n][r] == -__builtin_huge_valf() ? 0.0f : exp2f(sv[n][r] - m_new);
-                sv[n][r] = p;
-                lsum += p;
+                sv[n][r] = __builtin_amdgcn_exp2f(sv[n][r] - m_use);
+                lsum += sv[n][r];
             }
         lsum += __shfl_xor(lsum, 32);
         l_run = l_run * alpha + lsum;
         m_run = m_new;
+        // alpha is exactly 1 where the maximum did not move; skip the rescale
+        // when that holds for the whole wave.
+        if (__any(alpha != 1.0f)) {
 #pragma unroll
-        for (int t = 0; t < T::DT; ++t)
+            for (int t = 0; t < T::DT; ++t)
 #pragma unroll
-            for (int u = 0; u < T::OP; ++u)
+                for (int u = 0; u < T::OP; ++u)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) o_acc[t][u][r] *= alpha;
+                    for (int r = 0; r < 16; ++r) o_acc[t][u][r] *= alpha;
+        }
 
         // O^T += V^T P^T over the block's 64 keys, in register order.
 #pragma unroll
