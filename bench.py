@@ -12,7 +12,10 @@ device memory before timing starts.  W untimed calls, then K calls timed with
 HIP events recorded on the stream the kernel is launched on, bracketed by
 device synchronisation.  Prints one JSON line:
 
-  value      whole-job TFLOP/s = 2MNK / (time per step)
+  value      whole-job TFLOP/s = 2MNK / (time per step); with --cold, the mean
+             of single launches each preceded by a 512 MiB write that evicts the
+             operands from the caches
+  single_launch  median and best of launches timed one by one
   roofline   achieved TFLOP/s of the GEMM kernel against the FP32 matrix peak
              (157.3 TFLOP/s), and HBM traffic measured with rocprofv3 counters
              when the committed counter summary matches the current kernel source
@@ -604,6 +607,10 @@ def main(argv=None) -> int:
                     help="GEMM path (window: counter summaries of the window kernel only)")
     ap.add_argument("--workload", default="square4096")
     ap.add_argument("--config", type=int, default=None, help="force a matrix-core tile config")
+    ap.add_argument("--cold", action="store_true",
+                    help="GEMM: before every timed launch, write a 512 MiB buffer (more than the "
+                         "256 MB last-level cache) so the operands come from HBM; each launch is "
+                         "timed by its own event pair")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparator", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -643,6 +650,10 @@ def main(argv=None) -> int:
         args.steps = 200 if short else 50
     if args.warmup is None:
         args.warmup = 200 if short else 30
+    if args.cold and (args.workload in ATTN_WORKLOADS or args.workload in WINDOW_WORKLOADS
+                      or args.workload in CONV_WORKLOADS):
+        print("--cold applies to the GEMM workloads", file=sys.stderr)
+        return 2
     if args.workload in ATTN_WORKLOADS:
         return bench_attention(args)
     if args.workload in WINDOW_WORKLOADS:
@@ -703,7 +714,31 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    ms = timed(args.steps, args.warmup)
+    def per_launch(n_steps, cold):
+        """Each launch between its own event pair (the scrub, if any, outside
+        it): the spread of single-launch times."""
+        scrub = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev) if cold else None
+        pairs = []
+        for i in range(n_steps):
+            if scrub is not None:
+                scrub.fill_(float(i))
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            step()
+            e1.record(stream)
+            pairs.append((e0, e1))
+        torch.cuda.synchronize()
+        return sorted(e0.elapsed_time(e1) for e0, e1 in pairs)
+
+    if args.cold:
+        for _ in range(args.warmup):
+            step()
+        single = per_launch(args.steps, True)
+        ms = sum(single) / len(single)
+    else:
+        ms = timed(args.steps, args.warmup)
+        single = per_launch(min(args.steps, 50), False)
     flops = float(w.flops)
     tflops = flops / (ms * 1e-3) / 1e12
 
@@ -714,9 +749,10 @@ def main(argv=None) -> int:
     else:
         tile = "valu_128x128x8_t8x8"
 
+    # The counter summary was taken with warm caches.
     traffic = (read_traffic(TRAFFIC_FILE, GEMM_SOURCES, tile)
                if args.path == "mfma" and args.workload == "square4096" and args.config is None
-               else None)
+               and not args.cold else None)
     roofline = {"bound": "mfma" if args.path == "mfma" else "alu",
                 "achieved": tflops,
                 "peak": PEAK_FP32_TFLOPS,
@@ -751,6 +787,12 @@ def main(argv=None) -> int:
         "dtype": "f32",
         "data": "synthetic",
         "pct_of_fp32_peak": 100.0 * tflops / PEAK_FP32_TFLOPS,
+        "cache": "cold" if args.cold else "warm",
+        "single_launch": {"n": len(single),
+                          "median_ms": single[len(single) // 2],
+                          "min_ms": single[0],
+                          "median_tflops": flops / (single[len(single) // 2] * 1e-3) / 1e12,
+                          "max_tflops": flops / (single[0] * 1e-3) / 1e12},
         "config": {"workload": w.describe(), "M": w.M, "N": w.N, "K": w.K, "batch": w.batch,
                    "path": args.path, "tile": tile},
         "roofline": roofline,
