@@ -103,16 +103,25 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
     const int j = lane % 32;
     const int g = lane / 32;
-    const int qi = qb * T::BQ + 32 * wave + j;  // this lane's query
+    // Wave w takes the 32-query row group w for w < NW/2 and NW-1-(w-NW/2)
+    // above: waves w and w + NW/2 usually share a SIMD, and under the causal
+    // mask each such pair then holds one early and one late row group, so the
+    // SIMDs carry equal work on the diagonal blocks.
+    const int wrow = wave < T::NW / 2 ? wave : 3 * T::NW / 2 - 1 - wave;
+    const int q_first = qb * T::BQ + 32 * wrow;  // the wave's first query
+    const int qi = q_first + j;                  // this lane's query
     const int64_t q_org = uniform_i64(h * (int64_t)a.Sq * T::D);
     const int64_t kv_org = uniform_i64(h * (int64_t)a.Skv * T::D);
 
-    // Key blocks this workgroup needs (causal: none past its last query).
+    // Key blocks this workgroup needs (causal: none past its last query), and
+    // the ones this wave computes (causal: none past the wave's last query;
+    // it still copies its share of the later ones and meets the barriers).
     const int nkv = (a.Skv + T::BKV - 1) / T::BKV;
-    int nb = nkv;
+    int nb = nkv, nb_wave = nkv;
     if constexpr (T::CAUSAL) {
         const int last_q = min(a.Sq, qb * T::BQ + T::BQ) - 1;
         nb = min(nkv, last_q / T::BKV + 1);
+        nb_wave = min(nb, (q_first + 31) / T::BKV + 1);
     }
 
     // Q in registers: lane (j, g) holds Q[qi][HALF*g + kk] * scale * log2(e),
@@ -174,7 +183,7 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
     if (nb > 0) load_block(0, 0);
     wait_vmcnt<0>();
     lds_barrier();
-    for (int b = 0; b < nb; ++b) {
+    for (int b = 0; b < nb_wave; ++b) {
         const int st = b & 1;
         if (b + 1 < nb) load_block(b + 1, st ^ 1);
         const float* const Ks = smem + st * T::STAGE;
@@ -208,11 +217,11 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
         // Mask (only blocks that reach past Skv or, causal, past the wave's
         // first query can hold a disallowed key), then the online softmax.
         // Exponentials are v_exp_f32: 2^-inf = 0, and a result below the
-        // normal range flushes to 0, which changes O by less than 2^-126 of
-        // the weighted |V|.
+        // normal range may come out as 0, which changes O by less than 2^-126
+        // of the weighted |V|.
         const int kbase = b * T::BKV;
-        const bool edge = kbase + T::BKV > a.Skv ||
-                          (T::CAUSAL && kbase + T::BKV - 1 > qb * T::BQ + 32 * wave);
+        const bool edge =
+            kbase + T::BKV > a.Skv || (T::CAUSAL && kbase + T::BKV - 1 > q_first);
         float sv[2][16];
         float mloc = -__builtin_huge_valf();
 #pragma unroll
@@ -269,6 +278,12 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
 
         // Block b + 1 has landed (this wave's copies), and every wave is done
         // with stage st before the next iteration refills it.
+        wait_vmcnt<0>();
+        lds_barrier();
+    }
+    // Causal: the blocks past this wave's queries, copies and barriers only.
+    for (int b = nb_wave; b < nb; ++b) {
+        if (b + 1 < nb) load_block(b + 1, (b & 1) ^ 1);
         wait_vmcnt<0>();
         lds_barrier();
     }
