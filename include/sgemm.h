@@ -51,7 +51,9 @@ typedef enum sgemm_status {
     SGEMM_STATUS_INVALID_LD = -2,
     /* A, B or C is NULL although the call would read or write it. */
     SGEMM_STATUS_NULL_POINTER = -3,
-    /* M, N, K or batch is 2^31 or more, or an element offset overflows 64 bits. */
+    /* M, N, K or batch is 2^31 or more, an element offset overflows 64 bits, or
+       one product's tile grid needs more than 2^32 - 1 work-items (a single
+       launch's limit; a batch is split over as many launches as it needs). */
     SGEMM_STATUS_SIZE_OVERFLOW = -4,
     /* A batch stride is negative, or strideC lets two C matrices overlap. */
     SGEMM_STATUS_INVALID_STRIDE = -5,

@@ -1,0 +1,149 @@
+"""GPU parity at the size limits, through the C ABI of include/sgemm.h.
+
+* An operand of more than 2^31 elements: row offsets past 32 bits.
+* Leading dimensions so large that one tile's rows span more than 2^31 bytes:
+  the direct copies' 32-bit buffer offsets cannot reach, so every slice goes
+  through the register-staged loads, on every tile configuration; C's rows are
+  as far apart, so the stores' offsets pass 32 bits too.
+* Batch strides past 2^31 elements.
+* A strided batch with more workgroups than one launch holds (2^32 - 1
+  work-items): the library splits it over several launches.
+
+Operands are drawn on the device (workloads.device_operand, integers -4..4,
+NaN padding) and only the rows the oracle needs are copied back, so the
+products are exact: every checked entry must match the oracle bit for bit.
+Everything outside C's windows starts as a sentinel and must come back
+unchanged.  These need tens of GB of device memory (a 288 GB MI355X holds them).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+from workloads import device_operand
+
+import tiled_fp32_gemm_sgemm_amd as sg
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = -7.25  # not an integer: no exact product of integer inputs equals it
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True)
+def _release_memory():
+    yield
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def _call(M, N, K, A, lda, sA, B, ldb, sB, C, ldc, sC, batch, path="mfma", config=None):
+    stream = torch.cuda.current_stream().cuda_stream
+    st = sg.sgemm_strided_batched_raw(M, N, K, A.data_ptr(), lda, sA, B.data_ptr(), ldb, sB,
+                                      C.data_ptr(), ldc, sC, batch, stream, path, config)
+    assert st == 0, sg.status_string(st)
+    torch.cuda.synchronize()
+
+
+def _untouched_outside(C, M, N, ldc, stride, batch):
+    """Every float of C outside the batch's M x N windows still holds the
+    sentinel (counted on the device)."""
+    inside = batch * M * N
+    return int((C != SENTINEL).sum().item()) == inside and bool(
+        torch.all(torch.stack([(C[b * stride: b * stride + M * ldc].view(M, ldc)[:, :N]
+                                != SENTINEL).all() for b in range(batch)])).item())
+
+
+@pytest.mark.parametrize("path", ["mfma", "valu"])
+def test_operand_beyond_2_31_elements(path):
+    dev = _dev()
+    M, N, K = 131075, 40, 16411  # A holds 2,151,071,825 > 2^31 elements
+    assert M * K > 2 ** 31
+    A = device_operand(1, M, K, K, 0, seed=21, device=dev)
+    B = device_operand(1, K, N, N, 0, seed=22, device=dev)
+    C = torch.full((M * N + 64,), SENTINEL, device=dev)
+    _call(M, N, K, A, K, 0, B, N, 0, C, N, 0, 1, path)
+    assert bool((C[M * N:] == SENTINEL).all().item())
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 1, M // 2, M - 3, M - 2, M - 1],
+                                     rng.integers(0, M, 60)]))
+    A_rows = A.view(M, K)[torch.as_tensor(rows, device=dev)].cpu().numpy()
+    B_h = B.cpu().numpy()
+    ref, _, _ = oracle.sgemm_f64(len(rows), N, K, A_rows, K, B_h, N)
+    got = C[: M * N].view(M, N)[torch.as_tensor(rows, device=dev)].cpu().numpy()
+    parity.assert_bitwise(got, ref, "%s M*K > 2^31 rows %s" % (path, rows[:6]))
+
+
+PATHS = [("mfma", c) for c in range(sg.num_configs())] + [("valu", None)]
+
+
+@pytest.fixture(scope="module")
+def wide_operands():
+    """A (70 x 100, lda = 2^25 + 3), B (100 x 50, ldb = 2^26 + 5), C (70 x 50,
+    ldc = 2^25 + 1): a 64-row tile of A spans 8.5 GB, a 16-row slice of B
+    4.0 GB, more than a 32-bit buffer offset reaches, so no tile can use the
+    direct copies."""
+    dev = _dev()
+    M, N, K = 70, 50, 100
+    lda, ldb, ldc = 2 ** 25 + 3, 2 ** 26 + 5, 2 ** 25 + 1
+    A = device_operand(1, M, K, lda, 0, seed=23, device=dev)
+    B = device_operand(1, K, N, ldb, 0, seed=24, device=dev)
+    A_h = A.view(M, lda)[:, :K].cpu().numpy()
+    B_h = B.view(K, ldb)[:, :N].cpu().numpy()
+    ref, _, _ = oracle.sgemm_f64(M, N, K, np.ascontiguousarray(A_h), K,
+                                 np.ascontiguousarray(B_h), N)
+    C = torch.empty((M * ldc,), dtype=torch.float32, device=dev)
+    yield M, N, K, A, lda, B, ldb, C, ldc, ref
+    del A, B, C
+
+
+@pytest.mark.parametrize("path,config", PATHS,
+                         ids=["%s%s" % (p, "" if c is None else c) for p, c in PATHS])
+def test_leading_dimensions_beyond_32_bit_offsets(wide_operands, path, config):
+    M, N, K, A, lda, B, ldb, C, ldc, ref = wide_operands
+    C.fill_(SENTINEL)
+    _call(M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, 1, path, config)
+    got = C.view(M, ldc)[:, :N].cpu().numpy()
+    parity.assert_bitwise(got, ref,
+                          "%s cfg %s lda %d ldb %d ldc %d" % (path, config, lda, ldb, ldc))
+    assert _untouched_outside(C, M, N, ldc, 0, 1)
+
+
+@pytest.mark.parametrize("path", ["mfma", "valu"])
+def test_batch_strides_beyond_2_31_elements(path):
+    dev = _dev()
+    M, N, K, batch = 50, 60, 70, 3
+    sA, sB, sC = 2 ** 31 + 5, 2 ** 31 + 7, 2 ** 31 + 9
+    A = device_operand(batch, M, K, K, sA, seed=25, device=dev)
+    B = device_operand(batch, K, N, N, sB, seed=26, device=dev)
+    C = torch.full(((batch - 1) * sC + M * N,), SENTINEL, device=dev)
+    _call(M, N, K, A, K, sA, B, N, sB, C, N, sC, batch, path)
+    for b in range(batch):
+        A_h = A[b * sA: b * sA + M * K].cpu().numpy()
+        B_h = B[b * sB: b * sB + K * N].cpu().numpy()
+        ref, _, _ = oracle.sgemm_f64(M, N, K, A_h, K, B_h, N)
+        got = C[b * sC: b * sC + M * N].view(M, N).cpu().numpy()
+        parity.assert_bitwise(got, ref, "%s batch member %d" % (path, b))
+    assert _untouched_outside(C, M, N, N, sC, batch)
+
+
+@pytest.mark.parametrize("path", ["mfma", "valu"])
+def test_batch_split_over_launches(path):
+    """2^24 + 3 products of 1 x 1 x 2 (one workgroup each): more than
+    (2^32 - 1) / 256 workgroups, so at least two launches."""
+    dev = _dev()
+    M, N, K, batch = 1, 1, 2, 2 ** 24 + 3
+    A = device_operand(1, batch, K, K, 0, seed=27, device=dev)  # member b = row b
+    B = device_operand(1, batch, K, K, 0, seed=28, device=dev)  # stored K x 1, stride K
+    C = torch.full((batch + 16,), SENTINEL, device=dev)
+    _call(M, N, K, A, K, K, B, N, K, C, N, 1, batch, path)
+    ref, _ = oracle.sgemm_strided_batched_f64(M, N, K, A.cpu().numpy(), K, K, B.cpu().numpy(),
+                                              N, K, batch)
+    parity.assert_bitwise(C[:batch].cpu().numpy(), ref.reshape(batch),
+                          "%s batch %d" % (path, batch))
+    assert bool((C[batch:] == SENTINEL).all().item())

@@ -180,7 +180,9 @@ constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 constexpr int kNumCu = 256;  // MI355X compute units
 
 constexpr int64_t kMaxDim = INT32_MAX;
-constexpr int64_t kMaxGridX = INT32_MAX;
+// A dispatch counts its work-items in 32 bits: one launch holds at most
+// UINT32_MAX / threads workgroups.
+constexpr int64_t kMaxWorkItems = UINT32_MAX;
 
 bool mul_add_overflows(int64_t a, int64_t b, int64_t c, int64_t* out) {
     int64_t t;
@@ -323,8 +325,9 @@ int launch_gemm(const void* kernel, int bm, int bn, int threads, int64_t M, int6
     const int64_t tiles_m = ceil_div(M, bm);
     const int64_t tiles_n = ceil_div(N, bn);
     const int64_t per_matrix = tiles_m * tiles_n;
-    if (per_matrix > kMaxGridX) return SGEMM_STATUS_SIZE_OVERFLOW;
-    const int64_t per_launch = kMaxGridX / per_matrix;  // batch members per launch
+    const int64_t max_blocks = kMaxWorkItems / threads;
+    if (per_matrix > max_blocks) return SGEMM_STATUS_SIZE_OVERFLOW;
+    const int64_t per_launch = max_blocks / per_matrix;  // batch members per launch
     for (int64_t b0 = 0; b0 < batch; b0 += per_launch) {
         const int64_t nb = (batch - b0) < per_launch ? (batch - b0) : per_launch;
         GemmArgs p = {};

@@ -3,7 +3,10 @@
 This module holds input recipes only (shapes, layouts, value distributions,
 seeds); none of the product's arithmetic.  Both sides of every parity check,
 the HIP library and the CPU oracle, receive the very same float32 bits built
-here on the CPU with ``torch.Generator`` (A is drawn first, then B).
+here on the CPU with ``torch.Generator`` (A is drawn first, then B).  Operands
+too large for the host (the size-limit tests) are drawn on the device by
+``device_operand``; the oracle then gets the rows it needs copied back, bit for
+bit.
 
 Layouts are row-major with leading dimensions; when a leading dimension
 exceeds the row length the padding is filled with ``pad`` (NaN by default, so
@@ -303,3 +306,26 @@ def matrix(rows: int, cols: int, ld: int, seed: int, dist: str = "uniform",
     initial values for beta != 0)."""
     gen = torch.Generator("cpu").manual_seed(seed)
     return place(draw(gen, rows * cols, dist), rows, cols, ld, pad)
+
+
+def device_operand(batch: int, rows: int, cols: int, ld: int, stride: int, seed: int, device,
+                   dist: str = "int4", pad: float = float("nan"), extra: int = 0) -> torch.Tensor:
+    """A flat float32 buffer on ``device`` of (batch - 1) * stride + rows * ld
+    + extra floats holding ``batch`` rows x cols matrices (matrix b at b *
+    stride, leading dimension ld), drawn in place, matrix by matrix, from a
+    seeded generator on that device: "int4" = integers -4..4, "uniform" =
+    [-1, 1).  Everything else holds ``pad``."""
+    if ld < cols or (batch > 1 and stride < rows * ld):
+        raise ValueError("leading dimension or stride too small")
+    gen = torch.Generator(device).manual_seed(seed)
+    size = (batch - 1) * stride + rows * ld + extra if batch > 0 else extra
+    buf = torch.full((size,), pad, dtype=torch.float32, device=device)
+    for b in range(batch):
+        view = buf[b * stride: b * stride + rows * ld].view(rows, ld)[:, :cols]
+        if dist == "int4":
+            view.random_(-4, 5, generator=gen)
+        elif dist == "uniform":
+            view.uniform_(-1.0, 1.0, generator=gen)
+        else:
+            raise ValueError("unknown distribution %r" % dist)
+    return buf
