@@ -26,8 +26,8 @@
  * negative size, a head dimension other than 64 or 128, or a scale that is not
  * finite; SGEMM_STATUS_INVALID_OP for causal other than 0 or 1;
  * SGEMM_STATUS_SIZE_OVERFLOW when BH reaches 2^31, Sq or Skv exceeds
- * 2^31 - 513, an element count overflows 64 bits or the grid exceeds 2^31
- * workgroups;
+ * 2^31 - 513 or an element count overflows 64 bits (heads that need more
+ * workgroups than one launch holds go over several launches);
  * SGEMM_STATUS_NULL_POINTER for a NULL O with outputs to write or a NULL Q, K
  * or V when Skv > 0; SGEMM_STATUS_LAUNCH_FAILED if HIP rejects the launch.
  * BH == 0 or Sq == 0 enqueues nothing; Skv == 0 sets O to +0.0.

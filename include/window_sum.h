@@ -23,7 +23,8 @@ extern "C" {
  * and must not overlap; y[n..] is never written and x past n + W - 1 is never
  * read.  Enqueued on `stream`, asynchronous.
  * Returns 0; SGEMM_STATUS_INVALID_SIZE for n < 0, W < 1 or W > 1024;
- * SGEMM_STATUS_SIZE_OVERFLOW when n + W - 1 or the block count overflows;
+ * SGEMM_STATUS_SIZE_OVERFLOW when n + W - 1 overflows or the launch would need
+ * more than 2^32 - 1 work-items (n above 2^32 / 256 * 4096, about 6.9e10);
  * SGEMM_STATUS_NULL_POINTER for a NULL x or y with n > 0;
  * SGEMM_STATUS_LAUNCH_FAILED if HIP rejects the launch.  n == 0 enqueues
  * nothing.

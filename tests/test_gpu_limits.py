@@ -147,3 +147,55 @@ def test_batch_split_over_launches(path):
     parity.assert_bitwise(C[:batch].cpu().numpy(), ref.reshape(batch),
                           "%s batch %d" % (path, batch))
     assert bool((C[batch:] == SENTINEL).all().item())
+
+
+def test_window_sum_beyond_2_31_elements():
+    """n = 2^31 + 4101 window sums of integers: exact.  Output ranges at the
+    start, across element 2^31 and at the end, against the oracle on the same
+    stretch of x."""
+    dev = _dev()
+    n, W = 2 ** 31 + 4101, 5
+    x = device_operand(1, 1, n + W - 1, n + W - 1, 0, seed=29, device=dev)
+    y = torch.full((n + 64,), SENTINEL, device=dev)
+    st = sg.window_sum_raw(n, W, x.data_ptr(), y.data_ptr(),
+                           torch.cuda.current_stream().cuda_stream)
+    assert st == 0, sg.status_string(st)
+    torch.cuda.synchronize()
+    assert bool((y[n:] == SENTINEL).all().item())
+    for a, b in ((0, 5000), (2 ** 31 - 3000, 2 ** 31 + 3000), (n - 5000, n)):
+        ref, _ = oracle.window_sum_f64(b - a, W, x[a:b + W - 1].cpu().numpy())
+        parity.assert_bitwise(y[a:b].cpu().numpy(), ref, "window outputs %d..%d" % (a, b))
+
+
+def _attention_heads(q, k, v, o, heads, Sq, Skv, D, scale, what):
+    from test_gpu_attention import assert_attention_close
+    for h in heads:
+        qs = q[h * Sq * D:(h + 1) * Sq * D].cpu().numpy()
+        ks = k[h * Skv * D:(h + 1) * Skv * D].cpu().numpy()
+        vs = v[h * Skv * D:(h + 1) * Skv * D].cpu().numpy()
+        ref, mag, smax = oracle.attention_f64(qs, ks, vs, 1, Sq, Skv, D, scale, False)
+        got = o[h * Sq * D:(h + 1) * Sq * D].cpu().numpy().reshape(1, Sq, D)
+        assert_attention_close(got, ref, mag, smax, D, "%s head %d" % (what, h))
+
+
+@pytest.mark.parametrize("BH,Sq,Skv,D", [
+    (65600, 256, 64, 128),   # Q and O hold 2,149,580,800 > 2^31 elements
+    (2 ** 23 + 24, 1, 3, 64),  # more workgroups than one launch holds: two launches
+], ids=["q_beyond_2_31", "heads_over_two_launches"])
+def test_attention_at_the_size_limits(BH, Sq, Skv, D):
+    dev = _dev()
+    scale = float(np.float32(1.0 / np.sqrt(D)))
+    q = device_operand(1, BH * Sq, D, D, 0, seed=30, device=dev, dist="uniform")
+    k = device_operand(1, BH * Skv, D, D, 0, seed=31, device=dev, dist="uniform")
+    v = device_operand(1, BH * Skv, D, D, 0, seed=32, device=dev, dist="uniform")
+    o = torch.full((BH * Sq * D + 64,), SENTINEL, device=dev)
+    st = sg.attention_raw(BH, Sq, Skv, D, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                          scale, False, torch.cuda.current_stream().cuda_stream)
+    assert st == 0, sg.status_string(st)
+    torch.cuda.synchronize()
+    assert bool((o[BH * Sq * D:] == SENTINEL).all().item())
+    assert not bool((o[:BH * Sq * D] == SENTINEL).any().item())
+    per_launch = (2 ** 32 - 1) // 512 // ((Sq + 255) // 256)
+    heads = sorted({0, 1, BH // 2, BH - 2, BH - 1} |
+                   ({per_launch - 1, per_launch, per_launch + 1} if per_launch < BH else set()))
+    _attention_heads(q, k, v, o, heads, Sq, Skv, D, scale, "BH %d Sq %d" % (BH, Sq))

@@ -1,5 +1,6 @@
 // Host side of attention_fwd (include/attention.h): argument checks and the
-// launch of one workgroup per (head, block of queries).
+// launch of one workgroup per (head, block of queries), split over several
+// launches when one dispatch cannot hold them all.
 #include "attention.h"
 
 #include <hip/hip_runtime.h>
@@ -24,21 +25,28 @@ template <class T>
 int launch(int64_t BH, int64_t Sq, int64_t Skv, const float* Q, const float* K, const float* V,
            float* O, float scale, hipStream_t stream) {
     AttnArgs a;
-    a.Q = Q;
-    a.K = K;
-    a.V = V;
-    a.O = O;
-    a.BH = BH;
     a.Sq = (int)Sq;
     a.Skv = (int)Skv;
     a.q_blocks = (int)((Sq + T::BQ - 1) / T::BQ);
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);  // log2(e)
-    const int64_t blocks = (int64_t)a.q_blocks * BH;
-    if (blocks > INT32_MAX) return SGEMM_STATUS_SIZE_OVERFLOW;
-    void* args[] = {&a};
-    const hipError_t e = hipLaunchKernel((const void*)&attention_kernel<T>, dim3((unsigned)blocks),
-                                         dim3(T::NT), args, 0, stream);
-    return e == hipSuccess ? SGEMM_STATUS_SUCCESS : SGEMM_STATUS_LAUNCH_FAILED;
+    // A dispatch counts its work-items in 32 bits: the heads go over as many
+    // launches as that needs (Sq < 2^31 - 512 keeps one head's query blocks
+    // within one launch).
+    const int64_t per_launch = (int64_t)UINT32_MAX / T::NT / a.q_blocks;
+    for (int64_t h0 = 0; h0 < BH; h0 += per_launch) {
+        const int64_t nh = BH - h0 < per_launch ? BH - h0 : per_launch;
+        a.Q = Q + h0 * Sq * T::D;
+        a.K = K + h0 * Skv * T::D;
+        a.V = V + h0 * Skv * T::D;
+        a.O = O + h0 * Sq * T::D;
+        a.BH = nh;
+        void* args[] = {&a};
+        const hipError_t e =
+            hipLaunchKernel((const void*)&attention_kernel<T>, dim3((unsigned)(a.q_blocks * nh)),
+                            dim3(T::NT), args, 0, stream);
+        if (e != hipSuccess) return SGEMM_STATUS_LAUNCH_FAILED;
+    }
+    return SGEMM_STATUS_SUCCESS;
 }
 
 }  // namespace

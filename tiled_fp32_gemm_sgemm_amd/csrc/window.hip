@@ -14,7 +14,8 @@ extern "C" int window_sum(int64_t n, int64_t W, const float* x, float* y, hipStr
     if (n == 0) return SGEMM_STATUS_SUCCESS;
     if (n > INT64_MAX - W) return SGEMM_STATUS_SIZE_OVERFLOW;
     const int64_t blocks = (n + WindowTile::T - 1) / WindowTile::T;
-    if (blocks > INT32_MAX) return SGEMM_STATUS_SIZE_OVERFLOW;
+    // A dispatch counts its work-items in 32 bits.
+    if (blocks > (int64_t)UINT32_MAX / WindowTile::NT) return SGEMM_STATUS_SIZE_OVERFLOW;
     if (x == nullptr || y == nullptr) return SGEMM_STATUS_NULL_POINTER;
     int w = (int)W;
     void* args[] = {&x, &y, &n, &w};
