@@ -199,3 +199,78 @@ def test_attention_at_the_size_limits(BH, Sq, Skv, D):
     heads = sorted({0, 1, BH // 2, BH - 2, BH - 1} |
                    ({per_launch - 1, per_launch, per_launch + 1} if per_launch < BH else set()))
     _attention_heads(q, k, v, o, heads, Sq, Skv, D, scale, "BH %d Sq %d" % (BH, Sq))
+
+
+def _conv_images_check(x, wt, y, H, W, C, K, R, S, pad, images, what, n_samples=3000):
+    """Sampled outputs of the given images (every border position, all
+    channels at the centre, random ones) against the oracle run on that image
+    alone."""
+    P, Q = sg.conv2d_output_size(H, W, R, S, pad, (1, 1), (1, 1))
+    wt_h = wt.cpu().numpy()
+    rng = np.random.default_rng(13)
+    per_img = P * Q * K
+    for n in images:
+        x_h = x[n * H * W * C:(n + 1) * H * W * C].cpu().numpy()
+        pos = [(p, q) for p in (0, P - 1) for q in range(Q)] + \
+              [(p, q) for p in range(P) for q in (0, Q - 1)]
+        idx = [(p * Q + q) * K + k for (p, q) in pos for k in (0, K - 1)]
+        idx += [((P // 2) * Q + Q // 2) * K + k for k in range(K)]
+        idx = np.concatenate([np.asarray(idx, np.int64), rng.integers(0, per_img, n_samples)])
+        ref, _ = oracle.conv2d_nhwc_entries_f64(x_h, wt_h, 1, H, W, C, K, R, S, idx, pad)
+        got = y[n * per_img:(n + 1) * per_img].cpu().numpy()[idx]
+        parity.assert_bitwise(got, ref, "%s image %d" % (what, n))
+
+
+@pytest.fixture(scope="module")
+def conv_large_input():
+    """180 images of 112 x 112 x 1024 (2,311,061,504 elements, 9.2 GB),
+    3 x 3 filters to 64 channels, padding 1."""
+    dev = _dev()
+    N, H, W, C, K, R, S = 180, 112, 112, 1024, 64, 3, 3
+    x = device_operand(1, N * H * W, C, C, 0, seed=33, device=dev)
+    wt = device_operand(1, K * R * S, C, C, 0, seed=34, device=dev)
+    y = torch.empty((N * H * W * K + 64,), dtype=torch.float32, device=dev)
+    yield N, H, W, C, K, R, S, x, wt, y
+    del x, wt, y
+
+
+CONV_LIMIT_CONFIGS = [None] + [c for c in range(sg.num_configs())
+                               if sg.conv2d_config_available(c)]
+
+
+@pytest.mark.parametrize("config", CONV_LIMIT_CONFIGS,
+                         ids=["auto" if c is None else "cfg%d" % c for c in CONV_LIMIT_CONFIGS])
+def test_conv_input_beyond_2_31_elements(conv_large_input, config):
+    """Each tile addresses its images from the first one, so the direct copies
+    serve an input of any total size."""
+    N, H, W, C, K, R, S, x, wt, y = conv_large_input
+    assert N * H * W * C > 2 ** 31
+    y.fill_(SENTINEL)
+    st = sg.conv2d_nhwc_raw(N, H, W, C, K, R, S, x.data_ptr(), wt.data_ptr(), y.data_ptr(),
+                            (1, 1), (1, 1), (1, 1), torch.cuda.current_stream().cuda_stream,
+                            config)
+    assert st == 0, sg.status_string(st)
+    torch.cuda.synchronize()
+    n_out = N * H * W * K
+    assert bool((y[n_out:] == SENTINEL).all().item())
+    assert not bool((y[:n_out] == SENTINEL).any().item())
+    _conv_images_check(x, wt, y, H, W, C, K, R, S, (1, 1), (0, N // 2, N - 1),
+                       "conv cfg %s" % config, n_samples=1000)
+
+
+def test_conv_image_beyond_31_bit_offsets():
+    """Two images of 1040 x 1040 x 1024 (4.4 GB each): one image is more than
+    31-bit offsets reach, so the input is gathered through registers, with
+    offsets past 2^31 elements in the second image."""
+    dev = _dev()
+    N, H, W, C, K, R, S = 2, 1040, 1040, 1024, 8, 1, 1
+    x = device_operand(1, N * H * W, C, C, 0, seed=35, device=dev)
+    wt = device_operand(1, K * R * S, C, C, 0, seed=36, device=dev)
+    n_out = N * H * W * K
+    y = torch.full((n_out + 64,), SENTINEL, device=dev)
+    st = sg.conv2d_nhwc_raw(N, H, W, C, K, R, S, x.data_ptr(), wt.data_ptr(), y.data_ptr(),
+                            (0, 0), (1, 1), (1, 1), torch.cuda.current_stream().cuda_stream)
+    assert st == 0, sg.status_string(st)
+    torch.cuda.synchronize()
+    assert bool((y[n_out:] == SENTINEL).all().item())
+    _conv_images_check(x, wt, y, H, W, C, K, R, S, (0, 0), (0, 1), "conv 1040x1040x1024")

@@ -301,24 +301,33 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     // pixel (p sh - ph + r dh, q sw - pw + s dw): per-lane offsets for c0 = 0
     // are rebuilt when a slice starts a new tap, and c0 goes into the
     // descriptor base.  Pixels outside the image get an out-of-range offset
-    // and load as zeros (the zero padding).
+    // and load as zeros (the zero padding).  The descriptor starts at the
+    // first image the tile's rows fall in and ends after the last one, so the
+    // byte offsets only have to span those images, not the whole input.
     const ConvGeom& cg = p.conv;
-    int64_t cv_base[T::A_CHW];  // n * H * W * C + 4 kq
+    int64_t cv_base[T::A_CHW];  // (n - first image) * H * W * C + 4 kq
     int cv_ih0[T::A_CHW], cv_iw0[T::A_CHW];
     bool cv_row[T::A_CHW];
+    int64_t cv_org = 0, cv_span = 0;  // first element and element count of the tile's images
     if constexpr (T::CONV) {
+        const int64_t hwc = (int64_t)cg.H * cg.W * cg.C;
+        const int pq = cg.P * cg.Q;
+        const int img0 = m0 / pq;
+        const int img1 = (min(p.M, m0 + T::BM) - 1) / pq;
+        cv_org = uniform_i64((int64_t)img0 * hwc);
+        cv_span = uniform_i64((int64_t)(img1 - img0 + 1) * hwc);
 #pragma unroll
         for (int j = 0; j < T::A_CHW; ++j) {
             const int q = 64 * (wave * T::A_CHW + j) + lane;
             const int r = q / T::A_QPR;
             const int kq = (q % T::A_QPR) ^ T::swz(r);
             cv_row[j] = r < rows_left;
-            const int m = cv_row[j] ? m0 + r : 0;
+            const int m = cv_row[j] ? m0 + r : m0;
             const int oq = m % cg.Q;
             const int t = m / cg.Q;
             const int op = t % cg.P;
             const int n = t / cg.P;
-            cv_base[j] = (int64_t)n * cg.H * cg.W * cg.C + 4 * kq;
+            cv_base[j] = (int64_t)(n - img0) * hwc + 4 * kq;
             cv_ih0[j] = op * cg.stride_h - cg.pad_h;
             cv_iw0[j] = oq * cg.stride_w - cg.pad_w;
         }
@@ -345,8 +354,8 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
             const int tap = __builtin_amdgcn_readfirstlane(k0 / cg.C);
             const int c0 = k0 - tap * cg.C;
             if (c0 == 0) conv_offsets(tap);
-            a_step = c0;
-            a_range = (int)((cg.x_elems - c0) * 4);
+            a_step = cv_org + c0;
+            a_range = (int)((cv_span - c0) * 4);
         }
         const float* const a_base = p.A + uniform_i64(a_org + a_step);
         const float* const b_base =
@@ -435,8 +444,9 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     // one when BK does not divide K) goes through registers, so the offsets
     // stay fixed for the whole loop.
     // A convolution stages directly when every slice lies inside one filter
-    // tap (C a multiple of BK) and the image's byte offsets fit 31 bits.
-    const bool direct_ok = (T::CONV ? (cg.C % T::BK == 0 && cg.x_elems * 4 < (int64_t)kOutOfRange)
+    // tap (C a multiple of BK) and the byte offsets into the tile's images fit
+    // 31 bits.
+    const bool direct_ok = (T::CONV ? (cg.C % T::BK == 0 && cv_span * 4 < (int64_t)kOutOfRange)
                                     : a_span64 * 4 < (int64_t)kOutOfRange) &&
                            b_span64 * 4 < (int64_t)kOutOfRange &&
                            (T::A_KC || rows_left >= T::BM || p.M % 4 == 0) &&

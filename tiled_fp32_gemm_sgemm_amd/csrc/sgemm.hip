@@ -476,7 +476,6 @@ int run_conv(int config, int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, 
     g.stride_w = (int)stride_w;
     g.dil_h = (int)dil_h;
     g.dil_w = (int)dil_w;
-    g.x_elems = pl.x_elems;
     return launch_gemm(c.conv, c.bm, c.bn, c.threads, pl.Mg, K, pl.Kg, x, pl.Kg, 0, w, pl.Kg, 0, y,
                        K, 0, 1, stream, 1.0f, 0.0f, &g);
 }

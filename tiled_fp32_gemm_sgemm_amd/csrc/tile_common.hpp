@@ -22,7 +22,6 @@ struct ConvGeom {
     int H, W, C;          // input image
     int P, Q, S;          // output image, filter width (R = K / (S * C))
     int pad_h, pad_w, stride_h, stride_w, dil_h, dil_w;
-    int64_t x_elems;      // N * H * W * C
 };
 
 // Kernel arguments.  Sizes are validated on the host: M, N, K < 2^31, all
