@@ -274,3 +274,49 @@ def test_conv_image_beyond_31_bit_offsets():
     torch.cuda.synchronize()
     assert bool((y[n_out:] == SENTINEL).all().item())
     _conv_images_check(x, wt, y, H, W, C, K, R, S, (0, 0), (0, 1), "conv 1040x1040x1024")
+
+
+GENERAL_CONFIGS = [None] + [c for c in range(sg.num_configs()) if sg.config_has_general_form(c)]
+
+
+@pytest.fixture(scope="module")
+def wide_general():
+    """Stored A (70 x 100, or 100 x 70 transposed) with lda = 2^25 + 3, stored
+    B (100 x 50, or 50 x 100) with ldb = 2^26 + 5, C (70 x 50) with ldc =
+    2^25 + 1, all integers; one buffer per operand, as large as either layout
+    needs."""
+    dev = _dev()
+    M, N, K = 70, 50, 100
+    lda, ldb, ldc = 2 ** 25 + 3, 2 ** 26 + 5, 2 ** 25 + 1
+    A = device_operand(1, max(M, K), max(M, K), lda, 0, seed=37, device=dev)
+    B = device_operand(1, max(K, N), max(K, N), ldb, 0, seed=38, device=dev)
+    C0 = device_operand(1, M, N, ldc, 0, seed=39, device=dev, pad=SENTINEL)
+    C = torch.empty_like(C0)
+    yield M, N, K, A, lda, B, ldb, C0, C, ldc
+    del A, B, C0, C
+
+
+@pytest.mark.parametrize("config", GENERAL_CONFIGS,
+                         ids=["auto" if c is None else "cfg%d" % c for c in GENERAL_CONFIGS])
+@pytest.mark.parametrize("transA,transB", [(0, 0), (1, 0), (0, 1), (1, 1)],
+                         ids=["NN", "TN", "NT", "TT"])
+def test_general_form_beyond_32_bit_offsets(wide_general, transA, transB, config):
+    """C = 2 op(A) op(B) + 0.5 C with every leading dimension past 32-bit
+    offsets: staged loads in all four layouts and an epilogue that reads C."""
+    M, N, K, A, lda, B, ldb, C0, C, ldc = wide_general
+    ra, ca = (K, M) if transA else (M, K)
+    rb, cb = (N, K) if transB else (K, N)
+    C.copy_(C0)
+    st = sg.sgemm_ex_raw(transA, transB, M, N, K, 2.0, A.data_ptr(), lda, B.data_ptr(), ldb,
+                         0.5, C.data_ptr(), ldc, torch.cuda.current_stream().cuda_stream, config)
+    assert st == 0, sg.status_string(st)
+    torch.cuda.synchronize()
+    A_h = np.ascontiguousarray(A[: ra * lda].view(ra, lda)[:, :ca].cpu().numpy())
+    B_h = np.ascontiguousarray(B[: rb * ldb].view(rb, ldb)[:, :cb].cpu().numpy())
+    C_h = np.ascontiguousarray(C0[: M * ldc].view(M, ldc)[:, :N].cpu().numpy())
+    ref, _, _ = oracle.sgemm_ex_f64(bool(transA), bool(transB), M, N, K, 2.0, A_h, ca, B_h, cb,
+                                    0.5, C_h, N)
+    got = C[: M * ldc].view(M, ldc)[:, :N].cpu().numpy()
+    parity.assert_bitwise(got, ref, "general %d%d cfg %s" % (transA, transB, config))
+    assert int((C != C0).sum().item()) <= M * N  # nothing outside the window changed
+    assert torch.equal(C[M * ldc - ldc + N:], C0[M * ldc - ldc + N:])
