@@ -242,9 +242,17 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
         L.append("global_to_lds_values_model: %d" % staged)
         # one 64-lane dwordx4 instruction moves 256 values
         L.append("global_dwordx4_wave_instructions_closed_form: %d" % (staged // 256))
+        if "TCP_TCC_READ_REQ_sum" in merged:
+            # L1 -> L2 read requests, taken as one 128-byte line each
+            req = _mean(merged["TCP_TCC_READ_REQ_sum"])
+            L.append("l2_read_request_bytes_at_128B: %.0f (%.4f x the global-to-LDS model)"
+                     % (req * 128, req * 128 / (4.0 * staged)))
     if path == "valu" and "SQ_INSTS_VALU_FMA_F32" in merged:
         L.append("valu_fma_instructions_closed_form: %d" % model.valu_fma_instructions(
             w.M, w.N, w.K, batch=w.batch))
+    if "SQ_WAIT_ANY" in merged and "SQ_WAVE_CYCLES" in merged:
+        L.append("wave_cycles_waiting_fraction: %.4f"
+                 % (_mean(merged["SQ_WAIT_ANY"]) / _mean(merged["SQ_WAVE_CYCLES"])))
     if "SQ_LDS_BANK_CONFLICT" in merged and "SQ_LDS_IDX_ACTIVE" in merged:
         c = _mean(merged["SQ_LDS_BANK_CONFLICT"])
         a = _mean(merged["SQ_LDS_IDX_ACTIVE"])
