@@ -110,7 +110,7 @@ def _mean(vals):
 
 
 def summarize_trace(stats_csv: str, out: str, command: str, trace_csv: str = None,
-                    timed: int = 0) -> None:
+                    timed: int = 0, made_by: str = None) -> None:
     """Text summary of a rocprofv3 --kernel-trace --stats kernel_stats.csv.
     With the kernel_trace.csv and the bench's timed step count, also the
     average over the last `timed` dispatches of each kernel (the launches the
@@ -122,7 +122,10 @@ def summarize_trace(stats_csv: str, out: str, command: str, trace_csv: str = Non
             per_kernel.setdefault(r["Kernel_Name"], []).append(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     lines = ["# rocprofv3 kernel statistics (durations in microseconds)",
-             "# command: " + command, ""]
+             "# command: " + command]
+    if made_by:
+        lines.append("# summary: " + made_by)
+    lines.append("")
     for r in rows:
         name = r.get("Name") or r.get("KernelName") or r.get("Kernel_Name")
         calls = int(float(r.get("Calls", 0)))
@@ -638,13 +641,28 @@ def main(argv=None) -> int:
     ap.add_argument("--out")
     args = ap.parse_args(argv)
 
+    if args.summarize_trace or args.summarize_counters:
+        # The summary's own invocation, without the --command annotations
+        # (they name the profiler runs and change no figure).
+        import shlex
+        raw = list(sys.argv[1:] if argv is None else argv)
+        own = []
+        i = 0
+        while i < len(raw):
+            if raw[i] == "--command":
+                i += 2
+                continue
+            if not raw[i].startswith("--command="):
+                own.append(raw[i])
+            i += 1
+        own_cmd = "python3 bench.py " + " ".join(shlex.quote(a) for a in own)
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.out, " ".join(args.command), args.trace_csv,
-                        args.timed)
+                        args.timed, own_cmd)
         return 0
     if args.summarize_counters:
         summarize_counters(args.out, args.workload, args.path, args.kernel_part, args.fetch_csv,
-                           args.write_csv, args.sq_csv, args.command, args.config)
+                           args.write_csv, args.sq_csv, args.command + [own_cmd], args.config)
         return 0
 
     if args.gpus != 1:
