@@ -10,7 +10,8 @@ One step is one call of the library on the named workload (default: the
 4096^3 product, A and B ~ normal(0,1)/sqrt(K), seed 1), inputs resident in
 device memory before timing starts.  W untimed calls, then K calls timed with
 HIP events recorded on the stream the kernel is launched on, bracketed by
-device synchronisation.  Prints one JSON line:
+device synchronisation (GEMM defaults: W and K each fill about 0.1 s).
+Prints one JSON line:
 
   value      whole-job TFLOP/s = 2MNK / (time per step); with --cold, the mean
              of single launches each preceded by a 512 MiB write that evicts the
@@ -21,6 +22,8 @@ device synchronisation.  Prints one JSON line:
              when the committed counter summary matches the current kernel source
   cpu_baseline  the CPU oracle on a bounded sample (leading rows of C) of the
              same workload, on all host threads
+  comparators   the vector-ALU path and torch.mm / torch.bmm (hipBLASLt) on the
+             same operands with the same timing
 """
 from __future__ import annotations
 
@@ -41,6 +44,7 @@ PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "tiled_fp32_gemm_sgemm_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sgemm_mfma_square4096_counters.txt")
 COPY_BYTES = 512 * 1024 * 1024   # larger than the 256 MB last-level cache
+GEMM_WORK_S = 0.1                # default warm-up and timed work per GEMM phase (s)
 
 
 # Device sources each kernel family is compiled from.  A counter summary is
@@ -610,10 +614,12 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None,
-                    help="timed steps (default: 50 for GEMMs, 200 for the window and convolution)")
+                    help="timed steps (default: GEMMs as many as fill 0.1 s, at least 50; "
+                         "200 for the window and convolution; 50 for attention)")
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed steps first (default: 30 for GEMMs, 200 for the window and "
-                         "convolution, about 30 ms of work either way, so clocks have settled)")
+                    help="untimed steps first (default: GEMMs as many as fill 0.1 s, at least "
+                         "30, so clocks have settled; 200 for the window and convolution; 30 "
+                         "for attention)")
     ap.add_argument("--path", choices=["mfma", "valu", "window"], default="mfma",
                     help="GEMM path (window: counter summaries of the window kernel only)")
     ap.add_argument("--workload", default="square4096")
@@ -672,9 +678,12 @@ def main(argv=None) -> int:
 
     from workloads import ATTN_WORKLOADS, CONV_WORKLOADS, WINDOW_WORKLOADS
     short = args.workload in WINDOW_WORKLOADS or args.workload in CONV_WORKLOADS
-    if args.steps is None:
+    gemm = not (short or args.workload in ATTN_WORKLOADS)
+    # GEMM defaults are set from the measured time of one step (at least
+    # GEMM_WORK_S of launches for each phase, and 30 / 50 launches).
+    if args.steps is None and not gemm:
         args.steps = 200 if short else 50
-    if args.warmup is None:
+    if args.warmup is None and not gemm:
         args.warmup = 200 if short else 30
     if args.cold and (args.workload in ATTN_WORKLOADS or args.workload in WINDOW_WORKLOADS
                       or args.workload in CONV_WORKLOADS):
@@ -708,6 +717,16 @@ def main(argv=None) -> int:
     handle = stream.cuda_stream
 
     def step(path=args.path, config=args.config):
+        if path == "torch":
+            # hipBLASLt / rocBLAS through torch on the same operands (the
+            # result goes to a fresh output; C is not touched).
+            if w.batch == 1:
+                torch.mm(A.as_strided((w.M, w.K), (w.lda, 1)),
+                         B.as_strided((w.K, w.N), (w.ldb, 1)))
+            else:
+                torch.bmm(A.as_strided((w.batch, w.M, w.K), (w.strideA, w.lda, 1)),
+                          B.as_strided((w.batch, w.K, w.N), (w.strideB, w.ldb, 1)))
+            return
         if w.batch == 1 and config is None:
             st = sg.sgemm_raw(w.M, w.N, w.K, A.data_ptr(), w.lda, B.data_ptr(), w.ldb,
                               C.data_ptr(), w.ldc, handle, path)
@@ -757,6 +776,23 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         return sorted(e0.elapsed_time(e1) for e0, e1 in pairs)
 
+    # Time-based defaults: short launches need many more of them before the
+    # clocks settle (at 30 warm-up launches a 45 us batch ran 20 % slow).
+    def counts(path=args.path, config=args.config):
+        for _ in range(3):
+            step(path, config)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            step(path, config)
+        torch.cuda.synchronize()
+        est = (time.perf_counter() - t0) / 5
+        n = max(1, int(GEMM_WORK_S / max(est, 1e-6)))
+        warm = args.warmup if args.warmup is not None else max(30, n)
+        steps = args.steps if args.steps is not None else max(50, n)
+        return warm, steps
+
+    args.warmup, args.steps = counts()
     if args.cold:
         for _ in range(args.warmup):
             step()
@@ -794,6 +830,12 @@ def main(argv=None) -> int:
         other = "valu" if args.path == "mfma" else "mfma"
         oms = timed(max(5, args.steps // 5), 3, other, None)
         comparators[other] = {"tflops": flops / (oms * 1e-3) / 1e12, "ms_per_step": oms}
+    if not args.no_comparator and not args.cold:
+        t_warm, t_steps = counts("torch", None)
+        tms = timed(t_steps, t_warm, "torch", None)
+        comparators["torch_matmul"] = {"tflops": flops / (tms * 1e-3) / 1e12, "ms_per_step": tms,
+                                       "note": "torch.mm / torch.bmm (hipBLASLt) on the same "
+                                               "operands, same timing"}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -69,7 +69,8 @@ struct F4 {
 
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MI_, int OCC_, int GROUP_M_,
           int STAGES_ = 2, int KSPLIT_ = 1, bool SWIZZLE_ = true, bool TA_ = false,
-          bool TB_ = false, bool EX_ = false, bool BIL_ = true, bool CONV_ = false>
+          bool TB_ = false, bool EX_ = false, bool BIL_ = true, bool CONV_ = false,
+          bool ILV_ = true>
 struct DlTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -124,6 +125,10 @@ struct DlTile {
     // all 64 banks once.  With MI = 16 only BV = 4 keeps a pass inside one k
     // row; other widths keep BV = 1 and the row flip below.
     static constexpr bool BIL = BIL_;
+    // ILV: the next operand group's LDS reads are issued a quarter at a time,
+    // one part after each k step of the current group's MFMAs, instead of all
+    // at once before them (see the slice schedule in the kernel body).
+    static constexpr bool ILV = ILV_;
     static constexpr int BV = (B_KC || !BIL) ? 1
                               : MI == 16 ? (TN % 4 == 0 ? 4 : 1)
                                          : (TN % 4 == 0 ? 4 : TN % 2 == 0 ? 2 : 1);
@@ -509,46 +514,55 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
 
     // One operand group = KG consecutive k steps: one 16-byte quad of A per
     // row tile and KG values of B per column tile.  The operands of group g+1
-    // are read before the MFMAs of group g are issued ("Tiling Hierarchy on
-    // GPUs", "Register prefetching").
+    // are read while the MFMAs of group g are issued ("Tiling Hierarchy on
+    // GPUs", "Register prefetching").  A group is a list of LDS reads: the A
+    // items first (one quad per row tile, or one float per k step and row
+    // tile for A staged [k][m]), then the B items (one quad per column tile,
+    // one float per k step and column tile, or one BV-vector per k step and
+    // run of column tiles); read_items issues those with index in [lo, hi).
     using AReg = typename T::AReg;
     using BReg = typename T::BReg;
-    auto read_group = [&](int buf, int g, AReg (&a)[T::TM], BReg (&b)[T::TN]) {
+    constexpr int NA_ITEMS = T::A_KC ? T::TM : T::KG * T::TM;
+    constexpr int NB_ITEMS = T::B_KC ? T::TN : T::KG * NBV;
+    constexpr int N_ITEMS = NA_ITEMS + NB_ITEMS;
+    auto read_items = [&](int buf, int g, int lo, int hi, AReg (&a)[T::TM], BReg (&b)[T::TN]) {
         const float* const As = smem + buf * T::BUF_FLOATS;
         const float* const Bs = As + T::A_FLOATS;
         const int krow = kgrp * T::KSUB + lg * T::KPL + g * T::KG;  // first k of the group
         const int quad = krow / 4;
-        if constexpr (T::A_KC) {
 #pragma unroll
-            for (int mi = 0; mi < T::TM; ++mi)
-                a[mi] = *(const f32x4*)(As + (a_row + T::MI * mi) * T::BK + ((quad ^ a_swz) << 2));
-        } else {
-#pragma unroll
-            for (int s = 0; s < T::KG; ++s)
-#pragma unroll
-                for (int mi = 0; mi < T::TM; ++mi)
-                    a[mi][s] = As[(krow + s) * T::LDA_S + a_col[mi]];
-        }
-        if constexpr (T::B_KC) {
-#pragma unroll
-            for (int ni = 0; ni < T::TN; ++ni)
-                b[ni] = *(const f32x4*)(Bs + (b_row + T::MI * ni) * T::BK + ((quad ^ b_swz) << 2));
-        } else if constexpr (T::BV == 1) {
-#pragma unroll
-            for (int s = 0; s < T::KG; ++s)
-#pragma unroll
-                for (int ni = 0; ni < T::TN; ++ni) b[ni][s] = Bs[(krow + s) * T::LDB + b_col[ni]];
-        } else {
-            typedef float bvec_t __attribute__((ext_vector_type(T::BV)));
-#pragma unroll
-            for (int s = 0; s < T::KG; ++s)
-#pragma unroll
-                for (int h = 0; h < NBV; ++h) {
-                    const bvec_t v = *(const bvec_t*)(Bs + (krow + s) * T::LDB + b_col[h]);
-#pragma unroll
-                    for (int u = 0; u < T::BV; ++u) b[h * T::BV + u][s] = v[u];
+        for (int i = 0; i < N_ITEMS; ++i) {
+            if (i < lo || i >= hi) continue;
+            if (i < NA_ITEMS) {
+                if constexpr (T::A_KC) {
+                    a[i] = *(const f32x4*)(As + (a_row + T::MI * i) * T::BK + ((quad ^ a_swz) << 2));
+                } else {
+                    const int st = i / T::TM, mi = i % T::TM;
+                    a[mi][st] = As[(krow + st) * T::LDA_S + a_col[mi]];
                 }
+            } else {
+                const int j = i - NA_ITEMS;
+                if constexpr (T::B_KC) {
+                    b[j] = *(const f32x4*)(Bs + (b_row + T::MI * j) * T::BK + ((quad ^ b_swz) << 2));
+                } else if constexpr (T::BV == 1) {
+                    const int st = j / T::TN, ni = j % T::TN;
+                    b[ni][st] = Bs[(krow + st) * T::LDB + b_col[ni]];
+                } else {
+                    typedef float bvec_t __attribute__((ext_vector_type(T::BV)));
+                    const int st = j / NBV, h = j % NBV;
+                    const bvec_t v = *(const bvec_t*)(Bs + (krow + st) * T::LDB + b_col[h]);
+#pragma unroll
+                    for (int u = 0; u < T::BV; ++u) b[h * T::BV + u][st] = v[u];
+                }
+            }
         }
+    };
+    auto read_group = [&](int buf, int g, AReg (&a)[T::TM], BReg (&b)[T::TN]) {
+        read_items(buf, g, 0, N_ITEMS, a, b);
+    };
+    // Part `part` of KG: the items [part, part + 1) * N_ITEMS / KG.
+    auto read_part = [&](int buf, int g, int part, AReg (&a)[T::TM], BReg (&b)[T::TN]) {
+        read_items(buf, g, part * N_ITEMS / T::KG, (part + 1) * N_ITEMS / T::KG, a, b);
     };
 
     auto mfma_steps = [&](const AReg (&a)[T::TM], const BReg (&b)[T::TN], int s0, int s1) {
@@ -571,6 +585,14 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     // HOLD k steps of MFMAs run after the barrier, behind the reads of the next
     // slice's first operand group, so the matrix core keeps working while the
     // waves synchronise.
+    // Inside a slice (ILV) the reads of group g+1 go out in KG parts, one
+    // after each k step of group g's MFMAs, fenced by scheduling barriers so
+    // the compiler keeps the MFMAs in k-step order (left free, it pairs MFMAs
+    // on the same accumulator, which then wait on each other).  Spread out,
+    // the reads of the eight waves do not reach the LDS in one burst; the
+    // copies stay in one burst at the start of the slice (spreading them, or
+    // issuing them right after the barrier ahead of the held MFMAs, measured
+    // slower).  Without ILV all reads of group g+1 go out before group g.
     // `more` is a compile-time flag: the last slice is peeled off the loop so
     // that no control-flow join sits in front of the held MFMAs (at a join the
     // compiler's LDS wait would also cover the next slice's fresh reads).
@@ -580,19 +602,37 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
         if (more && ahead < nslices) load_slice(ahead);
 #pragma unroll
         for (int g = 0; g < T::NKG; ++g) {
-            if (g + 1 < T::NKG) {
-                if (g & 1)
-                    read_group(buf, g + 1, opa[0], opb[0]);
-                else
-                    read_group(buf, g + 1, opa[1], opb[1]);
-            }
-            __builtin_amdgcn_sched_barrier(0);
             const int s1 = g + 1 < T::NKG ? T::KG : T::KG - T::HOLD;
-            if (g & 1)
-                mfma_steps(opa[1], opb[1], 0, s1);
-            else
-                mfma_steps(opa[0], opb[0], 0, s1);
-            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (T::ILV) {
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int st = 0; st < s1; ++st) {
+                    if (g & 1)
+                        mfma_steps(opa[1], opb[1], st, st + 1);
+                    else
+                        mfma_steps(opa[0], opb[0], st, st + 1);
+                    if (g + 1 < T::NKG) {
+                        if (g & 1)
+                            read_part(buf, g + 1, st, opa[0], opb[0]);
+                        else
+                            read_part(buf, g + 1, st, opa[1], opb[1]);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            } else {
+                if (g + 1 < T::NKG) {
+                    if (g & 1)
+                        read_group(buf, g + 1, opa[0], opb[0]);
+                    else
+                        read_group(buf, g + 1, opa[1], opb[1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                if (g & 1)
+                    mfma_steps(opa[1], opb[1], 0, s1);
+                else
+                    mfma_steps(opa[0], opb[0], 0, s1);
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         if constexpr (more) {
             // The direct copies count on vmcnt: wait for this wave's, then the
