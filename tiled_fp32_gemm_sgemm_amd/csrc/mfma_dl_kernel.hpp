@@ -70,7 +70,7 @@ struct F4 {
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MI_, int OCC_, int GROUP_M_,
           int STAGES_ = 2, int KSPLIT_ = 1, bool SWIZZLE_ = true, bool TA_ = false,
           bool TB_ = false, bool EX_ = false, bool BIL_ = true, bool CONV_ = false,
-          bool ILV_ = true>
+          int SCHED_ = 1>
 struct DlTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -125,10 +125,17 @@ struct DlTile {
     // all 64 banks once.  With MI = 16 only BV = 4 keeps a pass inside one k
     // row; other widths keep BV = 1 and the row flip below.
     static constexpr bool BIL = BIL_;
-    // ILV: the next operand group's LDS reads are issued a quarter at a time,
-    // one part after each k step of the current group's MFMAs, instead of all
-    // at once before them (see the slice schedule in the kernel body).
-    static constexpr bool ILV = ILV_;
+    // Slice schedule (see the kernel body):
+    //   SCHED = 0: the next operand group's LDS reads go out at once, before
+    //              the current group's MFMAs; the slice copies in one burst;
+    //   SCHED = 1: the reads go out a part at a time, one after each k step of
+    //              the current group's MFMAs; the copies in one burst;
+    //   SCHED = 2: as 1, and the copies one after each k step from the start
+    //              of the slice (a convolution keeps the burst: its copy
+    //              offsets are rebuilt per filter tap).
+    static constexpr int SCHED = SCHED_;
+    static constexpr bool ILV = SCHED >= 1;
+    static constexpr bool SPREAD_COPIES = SCHED >= 2 && !CONV_;
     static constexpr int BV = (B_KC || !BIL) ? 1
                               : MI == 16 ? (TN % 4 == 0 ? 4 : 1)
                                          : (TN % 4 == 0 ? 4 : TN % 2 == 0 ? 2 : 1);
@@ -157,6 +164,8 @@ struct DlTile {
     static_assert(TN % BV == 0, "whole vectors of column tiles");
     static_assert(!CONV || (A_KC && B_KC && !EX), "convolution: k-contiguous A and B, beta = 0");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+    static_assert(SCHED >= 0 && SCHED <= 2, "slice schedule");
+    static_assert(SCHED < 2 || LPS <= NKG * KG - HOLD, "one copy per k step fits in a slice");
     static_assert((KSPLIT - 1) * BM * BN <= STAGES * BUF_FLOATS, "k-group exchange fits in LDS");
 
     static __device__ __forceinline__ int swz(int r) { return SWIZZLE ? (r / RPB) % QPR : 0; }
@@ -379,6 +388,33 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
                 rb, (lds_void_t*)(dstB + 256 * (wave * T::B_CHW + j)), 16, b_off[j], 0, 0, 0);
     };
 
+    // The copies of a direct slice with index j in [lo, hi): this wave's A
+    // chunks are j < A_CHW, its B chunks the rest (SCHED = 2 issues them one
+    // per k step).
+    auto load_direct_part = [&](int k0, int buf, int lo, int hi) {
+        float* const dstA = smem + buf * T::BUF_FLOATS;
+        float* const dstB = dstA + T::A_FLOATS;
+        const float* const a_base =
+            p.A + uniform_i64(a_org + (T::A_KC ? (int64_t)k0 : (int64_t)k0 * p.lda));
+        const float* const b_base =
+            p.B + uniform_i64(b_org + (T::B_KC ? (int64_t)k0 : (int64_t)k0 * p.ldb));
+        const __amdgpu_buffer_rsrc_t ra =
+            __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, (int)a_span, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rb =
+            __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, (int)b_span, 0x00020000);
+#pragma unroll
+        for (int j = 0; j < T::LPS; ++j) {
+            if (j < lo || j >= hi) continue;
+            if (j < T::A_CHW)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    ra, (lds_void_t*)(dstA + 256 * (wave * T::A_CHW + j)), 16, a_off[j], 0, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rb, (lds_void_t*)(dstB + 256 * (wave * T::B_CHW + j - T::A_CHW)), 16,
+                    b_off[j - T::A_CHW], 0, 0, 0);
+        }
+    };
+
     // Fallback for slices with quads that straddle the matrix edge: masked
     // element loads through registers, written to the same layout.
     auto load_staged = [&](int k0, int buf) {
@@ -585,21 +621,29 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     // HOLD k steps of MFMAs run after the barrier, behind the reads of the next
     // slice's first operand group, so the matrix core keeps working while the
     // waves synchronise.
-    // Inside a slice (ILV) the reads of group g+1 go out in KG parts, one
-    // after each k step of group g's MFMAs, fenced by scheduling barriers so
-    // the compiler keeps the MFMAs in k-step order (left free, it pairs MFMAs
-    // on the same accumulator, which then wait on each other).  Spread out,
-    // the reads of the eight waves do not reach the LDS in one burst; the
-    // copies stay in one burst at the start of the slice (spreading them, or
-    // issuing them right after the barrier ahead of the held MFMAs, measured
-    // slower).  Without ILV all reads of group g+1 go out before group g.
+    // Inside a slice (SCHED >= 1) the reads of group g+1 go out in KG parts,
+    // one after each k step of group g's MFMAs, fenced by scheduling barriers
+    // so the compiler keeps the MFMAs in k-step order (left free, it pairs
+    // MFMAs on the same accumulator, which then wait on each other).  Spread
+    // out, the waves' reads do not reach the LDS in one burst.  A copy
+    // instruction holds its wave while the address unit takes it in: with
+    // SCHED = 2 one copy follows each k step, behind MFMAs already issued,
+    // which pays on small wave tiles (512 x 4096 x 4096 on 64 x 128 tiles:
+    // +7 %); on the 256 x 256 tile, where the other wave of the SIMD covers
+    // the burst, one burst at the start of the slice measured faster (as did
+    // that burst against issuing the copies right after the barrier, ahead of
+    // the held MFMAs).  With SCHED = 0 all reads of group g+1 go out before
+    // group g.
     // `more` is a compile-time flag: the last slice is peeled off the loop so
     // that no control-flow join sits in front of the held MFMAs (at a join the
     // compiler's LDS wait would also cover the next slice's fresh reads).
     auto slice = [&](auto more_tag, int buf, int s) {
         constexpr bool more = decltype(more_tag)::value;
         const int ahead = s + T::STAGES - 1;
-        if (more && ahead < nslices) load_slice(ahead);
+        // Copies of a direct slice spread over the k steps (SCHED = 2); a
+        // register-staged slice is copied whole at the start.
+        const bool spread = T::SPREAD_COPIES && more && direct_ok && ahead < full_slices;
+        if (more && ahead < nslices && !spread) load_slice(ahead);
 #pragma unroll
         for (int g = 0; g < T::NKG; ++g) {
             const int s1 = g + 1 < T::NKG ? T::KG : T::KG - T::HOLD;
@@ -616,6 +660,11 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
                             read_part(buf, g + 1, st, opa[0], opb[0]);
                         else
                             read_part(buf, g + 1, st, opa[1], opb[1]);
+                    }
+                    if constexpr (T::SPREAD_COPIES) {
+                        const int step = g * T::KG + st;
+                        if (spread && step < T::LPS)
+                            load_direct_part(ahead * T::BK, ahead % T::STAGES, step, step + 1);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }

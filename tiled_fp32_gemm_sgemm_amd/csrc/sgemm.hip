@@ -87,10 +87,11 @@ using Dl128x128k64m32s2 = DlTile<128, 128, 64, 2, 2, 32, 1, 8, 2>;  // 4 waves o
 // Two wave groups split every slice's k range (8 waves of 32x32, 2 per SIMD).
 using Dl64x64k64m32s4x2 = DlTile<64, 64, 64, 2, 2, 32, 2, 8, 4, 2>;
 using Dl64x64k32m32s4x2 = DlTile<64, 64, 32, 2, 2, 32, 2, 8, 4, 2>;
-// (reads of a group issued in one burst: the k-step interleave measured 0.9 %
-// slower on this tile at 512 x 4096 x 4096, and faster on every other tile)
+// Copies spread over the k steps (schedule 2): +6 % at 512 x 4096 x 4096.
 using Dl128x64k64m32s2x2 =
-    DlTile<128, 64, 64, 2, 2, 32, 2, 8, 2, 2, true, false, false, false, true, false, false>;  // 8 waves of 64x32
+    DlTile<128, 64, 64, 2, 2, 32, 2, 8, 2, 2, true, false, false, false, true, false, 2>;  // 8 waves of 64x32
+using Dl64x128k64m32s2x2 =
+    DlTile<64, 128, 64, 2, 2, 32, 2, 8, 2, 2, true, false, false, false, true, false, 2>;  // 8 waves of 32x64
 // Small LDS footprints, so that three or four workgroups share a CU and
 // their barriers fall at different times (4 waves of 64x64 or 32x32 each).
 using Dl128x128k16o4 = DlTile<128, 128, 16, 2, 2, 32, 4, 8, 2>;     // 32 KB LDS, 4 per CU
@@ -122,13 +123,13 @@ struct ConfigEntry {
 // The same tile with stored-operand layouts and the alpha/beta epilogue.
 template <class T, bool TA, bool TB>
 using DlGeneral = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::OCC, T::GROUP_M,
-                         T::STAGES, T::KSPLIT, T::SWIZZLE, TA, TB, true, T::BIL, false, T::ILV>;
+                         T::STAGES, T::KSPLIT, T::SWIZZLE, TA, TB, true, T::BIL, false, T::SCHED>;
 
 // The same tile as an implicit-GEMM convolution (A gathered from an NHWC
 // image, B = KRSC filters stored N x K).
 template <class T>
 using DlConv = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::OCC, T::GROUP_M,
-                      T::STAGES, T::KSPLIT, T::SWIZZLE, false, true, false, T::BIL, true, T::ILV>;
+                      T::STAGES, T::KSPLIT, T::SWIZZLE, false, true, false, T::BIL, true, T::SCHED>;
 
 #define SGEMM_CFG(T, name, per_cu, a1, b1, a2, b2) \
     { name, T::BM, T::BN, T::BK, T::NT, T::WG_PER_CU, (const void*)&sgemm_mfma_kernel<T>, per_cu, \
@@ -156,25 +157,26 @@ const ConfigEntry kConfigs[] = {
     SGEMM_CFG(Cfg64x64k32m16, "mfma16_64x64x32_w2x2", 4, 6.8628e-04, 6.4584e-06, 1.5598e-03, 1.8572e-05),
     SGEMM_CFG(Cfg256x256m32w1, "mfma32_256x256x16_w2x2", 1, 2.1097e-04, 3.9263e-06, 3.9320e-04, 7.8470e-06),
     SGEMM_CFG(Cfg256x256k32m32w1, "mfma32_256x256x32_w2x2", 1, 2.2194e-04, 3.8922e-06, 4.1654e-04, 7.7681e-06),
-    SGEMM_DLX_CFG(Dl256x256k32m32, "dl32_256x256x32_w2x4", 1, 2.2637e-04, 3.4025e-06, 3.9250e-04, 6.8025e-06),
-    SGEMM_DL_CFG(Dl256x256k16m32, "dl32_256x256x16_w2x4", 1, 2.1670e-04, 3.4090e-06, 3.7145e-04, 6.8345e-06),
-    SGEMM_DL_CFG(Dl256x128k32m32, "dl32_256x128x32_w2x2", 1, 3.1727e-04, 3.7384e-06, 4.3118e-04, 7.4863e-06),
-    SGEMM_DLX_CFG(Dl128x128k32m32, "dl32_128x128x32_w2x2", 2, 3.9928e-04, 3.8776e-06, 4.8043e-04, 7.0650e-06),
+    SGEMM_DLX_CFG(Dl256x256k32m32, "dl32_256x256x32_w2x4", 1, 2.7056e-04, 3.3635e-06, 3.9211e-04, 6.7493e-06),
+    SGEMM_DL_CFG(Dl256x256k16m32, "dl32_256x256x16_w2x4", 1, 2.2059e-04, 3.3829e-06, 3.7041e-04, 6.7868e-06),
+    SGEMM_DL_CFG(Dl256x128k32m32, "dl32_256x128x32_w2x2", 1, 3.2052e-04, 3.7135e-06, 4.3937e-04, 7.4384e-06),
+    SGEMM_DLX_CFG(Dl128x128k32m32, "dl32_128x128x32_w2x2", 2, 3.9893e-04, 3.8925e-06, 5.5372e-04, 6.8583e-06),
     SGEMM_DL_CFG(Dl256x256k32m32Plain, "dl32_256x256x32_w2x4_unswizzled", 0, 0, 0, 0, 0),
-    SGEMM_DL_CFG(Dl128x128k32m32s4, "dl32_128x128x32_w2x2_s4", 1, 4.0428e-04, 4.0995e-06, 5.6909e-04, 8.2213e-06),
-    SGEMM_DLX_CFG(Dl64x64k32m32s4, "dl32_64x64x32_w2x2_s4", 2, 7.2952e-04, 5.2118e-06, 1.0443e-03, 7.7747e-06),
-    SGEMM_DLX_CFG(Dl256x192k32m32, "dl32_256x192x32_w4x2", 1, 2.1701e-04, 3.5203e-06, 3.5759e-04, 7.0372e-06),
-    SGEMM_DLX_CFG(Dl192x256k32m32, "dl32_192x256x32_w2x4", 1, 2.1944e-04, 3.4698e-06, 3.6160e-04, 6.9358e-06),
-    SGEMM_DL_CFG(Dl64x64k64m32s4, "dl32_64x64x64_w2x2_s4", 1, 7.8433e-04, 5.0220e-06, 1.2553e-03, 1.0008e-05),
-    SGEMM_DL_CFG(Dl64x64k32m32s8, "dl32_64x64x32_w2x2_s8", 1, 8.0675e-04, 5.3391e-06, 1.2985e-03, 1.0657e-05),
-    SGEMM_DL_CFG(Dl128x64k32m32s4, "dl32_128x64x32_w2x2_s4", 1, 5.0258e-04, 4.5911e-06, 8.2285e-04, 9.1651e-06),
-    SGEMM_DL_CFG(Dl128x128k64m32s2, "dl32_128x128x64_w2x2", 1, 4.4821e-04, 3.8893e-06, 6.4915e-04, 7.8117e-06),
-    SGEMM_DLX_CFG(Dl64x64k64m32s4x2, "dl32_64x64x64_w2x2_s4_k2", 1, 9.3095e-04, 4.2275e-06, 1.5347e-03, 8.4092e-06),
-    SGEMM_DL_CFG(Dl64x64k32m32s4x2, "dl32_64x64x32_w2x2_s4_k2", 2, 8.4221e-04, 5.1424e-06, 1.2486e-03, 8.5543e-06),
-    SGEMM_DLX_CFG(Dl128x64k64m32s2x2, "dl32_128x64x64_w2x2_s2_k2", 1, 5.7721e-04, 3.8502e-06, 9.6700e-04, 7.6880e-06),
-    SGEMM_DLX_CFG(Dl128x128k16o4, "dl32_128x128x16_w2x2_o4", 4, 3.8746e-04, 3.7646e-06, 9.6869e-04, 1.3744e-05),
-    SGEMM_DL_CFG(Dl128x128k16o3s3, "dl32_128x128x16_w2x2_s3_o3", 3, 3.6668e-04, 4.2300e-06, 5.9514e-04, 1.0602e-05),
-    SGEMM_DLX_CFG(Dl64x64k32o4, "dl32_64x64x32_w2x2_o4", 4, 7.5377e-04, 4.5803e-06, 1.6470e-03, 1.4589e-05),
+    SGEMM_DL_CFG(Dl128x128k32m32s4, "dl32_128x128x32_w2x2_s4", 1, 4.1409e-04, 4.0347e-06, 5.8961e-04, 8.0769e-06),
+    SGEMM_DLX_CFG(Dl64x64k32m32s4, "dl32_64x64x32_w2x2_s4", 2, 7.5517e-04, 4.8253e-06, 1.0738e-03, 7.8416e-06),
+    SGEMM_DLX_CFG(Dl256x192k32m32, "dl32_256x192x32_w4x2", 1, 2.1273e-04, 3.4836e-06, 3.5937e-04, 6.9587e-06),
+    SGEMM_DLX_CFG(Dl192x256k32m32, "dl32_192x256x32_w2x4", 1, 2.1856e-04, 3.4304e-06, 3.6343e-04, 6.8644e-06),
+    SGEMM_DL_CFG(Dl64x64k64m32s4, "dl32_64x64x64_w2x2_s4", 1, 7.7140e-04, 4.8489e-06, 1.2493e-03, 9.6503e-06),
+    SGEMM_DL_CFG(Dl64x64k32m32s8, "dl32_64x64x32_w2x2_s8", 1, 8.4332e-04, 4.8843e-06, 1.3606e-03, 9.7563e-06),
+    SGEMM_DL_CFG(Dl128x64k32m32s4, "dl32_128x64x32_w2x2_s4", 1, 4.9721e-04, 4.5194e-06, 8.1195e-04, 9.0356e-06),
+    SGEMM_DL_CFG(Dl128x128k64m32s2, "dl32_128x128x64_w2x2", 1, 4.4267e-04, 3.9188e-06, 6.5237e-04, 7.8463e-06),
+    SGEMM_DLX_CFG(Dl64x64k64m32s4x2, "dl32_64x64x64_w2x2_s4_k2", 1, 8.9272e-04, 4.1196e-06, 1.5031e-03, 8.1286e-06),
+    SGEMM_DL_CFG(Dl64x64k32m32s4x2, "dl32_64x64x32_w2x2_s4_k2", 2, 8.4842e-04, 4.9353e-06, 1.1928e-03, 8.4095e-06),
+    SGEMM_DLX_CFG(Dl128x64k64m32s2x2, "dl32_128x64x64_w2x2_s2_k2", 1, 5.7303e-04, 3.7133e-06, 1.0005e-03, 7.3913e-06),
+    SGEMM_DLX_CFG(Dl128x128k16o4, "dl32_128x128x16_w2x2_o4", 4, 3.7798e-04, 3.8163e-06, 7.8534e-04, 1.3933e-05),
+    SGEMM_DL_CFG(Dl128x128k16o3s3, "dl32_128x128x16_w2x2_s3_o3", 3, 3.7375e-04, 4.0480e-06, 5.7368e-04, 1.0599e-05),
+    SGEMM_DLX_CFG(Dl64x64k32o4, "dl32_64x64x32_w2x2_o4", 4, 7.5602e-04, 4.4574e-06, 1.4899e-03, 1.4845e-05),
+    SGEMM_DLX_CFG(Dl64x128k64m32s2x2, "dl32_64x128x64_w2x2_s2_k2", 1, 5.6513e-04, 3.6309e-06, 9.9029e-04, 7.2336e-06),
 };
 #undef SGEMM_CFG
 #undef SGEMM_DL_CFG
