@@ -114,11 +114,12 @@ def _mean(vals):
 
 
 def summarize_trace(stats_csv: str, out: str, command: str, trace_csv: str = None,
-                    timed: int = 0, made_by: str = None) -> None:
+                    timed: int = 0, made_by: str = None, after: int = 0) -> None:
     """Text summary of a rocprofv3 --kernel-trace --stats kernel_stats.csv.
     With the kernel_trace.csv and the bench's timed step count, also the
-    average over the last `timed` dispatches of each kernel (the launches the
-    bench times; the others are its warm-up)."""
+    average over the `timed` dispatches of each kernel that precede its last
+    `after` ones (the launches the bench times in one event pair; before them
+    come the warm-up, after them the launches timed one by one)."""
     rows = _read_csv(stats_csv)
     per_kernel = {}
     if trace_csv:
@@ -139,9 +140,11 @@ def summarize_trace(stats_csv: str, out: str, command: str, trace_csv: str = Non
                      % (calls, avg_us, float(r.get("MinNs", 0)) / 1e3,
                         float(r.get("MaxNs", 0)) / 1e3, r.get("Percentage", "")))
         durs = per_kernel.get(name, [])
-        if timed and len(durs) >= timed:
-            lines.append("  timed_average_us (last %d dispatches): %.2f"
-                         % (timed, sum(durs[-timed:]) / timed))
+        if timed and len(durs) >= timed + after:
+            sel = durs[len(durs) - after - timed:len(durs) - after]
+            where = ("last %d dispatches" % timed if after == 0 else
+                     "%d dispatches before the last %d" % (timed, after))
+            lines.append("  timed_average_us (%s): %.2f" % (where, sum(sel) / timed))
     open(out, "w").write("\n".join(lines) + "\n")
 
 
@@ -635,6 +638,9 @@ def main(argv=None) -> int:
     ap.add_argument("--summarize-trace", metavar="KERNEL_STATS_CSV",
                     help="write a text summary of a rocprofv3 kernel-stats csv to --out")
     ap.add_argument("--trace-csv", help="kernel_trace.csv for --summarize-trace")
+    ap.add_argument("--after-timed", type=int, default=0,
+                    help="dispatches of the kernel after the timed ones (--summarize-trace; a "
+                         "GEMM run launches min(steps, 50) single timed launches after them)")
     ap.add_argument("--timed", type=int, default=0,
                     help="timed dispatches at the end of the trace (--summarize-trace)")
     ap.add_argument("--summarize-counters", action="store_true",
@@ -664,7 +670,7 @@ def main(argv=None) -> int:
         own_cmd = "python3 bench.py " + " ".join(shlex.quote(a) for a in own)
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.out, " ".join(args.command), args.trace_csv,
-                        args.timed, own_cmd)
+                        args.timed, own_cmd, args.after_timed)
         return 0
     if args.summarize_counters:
         summarize_counters(args.out, args.workload, args.path, args.kernel_part, args.fetch_csv,
