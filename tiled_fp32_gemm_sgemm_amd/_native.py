@@ -13,6 +13,9 @@ import re
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libsgemm.so")
+# Test library: the same C ABI built with SGEMM_RACECHECK=1 (LDS buffers
+# filled with NaN once consumed, tiles in reverse order).
+RACECHECK_LIB_PATH = os.path.join(PKG, "libsgemm_racecheck.so")
 INCLUDE = os.path.join(os.path.dirname(PKG), "include")
 HEADER = os.path.join(INCLUDE, "sgemm.h")
 
@@ -86,21 +89,37 @@ _SIGS = {
 }
 
 
+_racecheck_lib = None
+
+
+def _load(path: str):
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "%s is not built (%s); run `python -m tiled_fp32_gemm_sgemm_amd.build`"
+            % (os.path.basename(path), path))
+    handle = ctypes.CDLL(path)
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(handle, name)
+        fn.argtypes = args
+        fn.restype = res
+    return handle
+
+
 def lib():
     """The loaded library; raises if it has not been built."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(
-                "libsgemm.so is not built (%s); run `python -m tiled_fp32_gemm_sgemm_amd.build`"
-                % LIB_PATH)
-        handle = ctypes.CDLL(LIB_PATH)
-        for name, (args, res) in _SIGS.items():
-            fn = getattr(handle, name)
-            fn.argtypes = args
-            fn.restype = res
-        _lib = handle
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+def racecheck_lib():
+    """The race-check build of the same C ABI (tests only); raises if it has
+    not been built."""
+    global _racecheck_lib
+    if _racecheck_lib is None:
+        _racecheck_lib = _load(RACECHECK_LIB_PATH)
+    return _racecheck_lib
 
 
 def status_string(status: int) -> str:

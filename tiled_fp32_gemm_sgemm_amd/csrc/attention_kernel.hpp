@@ -90,7 +90,8 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
     // block's work grows with its index, and handing the longest jobs out
     // first (the longest-processing-time rule) keeps the CUs' finishing times
     // together.  Without the mask every block has the same work.
-    const uint32_t pid = xcd_contiguous_id(blockIdx.x, gridDim.x);
+    const uint32_t pid = xcd_contiguous_id(kRaceCheck ? gridDim.x - 1 - blockIdx.x : blockIdx.x,
+                                           gridDim.x);
     const uint32_t per_group = (uint32_t)(kHeadsPerGroup * a.q_blocks);
     const uint32_t hg = pid / per_group;
     const uint32_t l = pid - hg * per_group;
@@ -180,6 +181,10 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
     float m_run = -__builtin_huge_valf();
     float l_run = 0.0f;
 
+    if constexpr (kRaceCheck) {
+        poison_lds(smem, 2 * T::STAGE, tid, T::NT);
+        lds_barrier();
+    }
     if (nb > 0) load_block(0, 0);
     wait_vmcnt<0>();
     lds_barrier();
@@ -280,12 +285,21 @@ __device__ __forceinline__ void attention_body(const AttnArgs& a) {
         // with stage st before the next iteration refills it.
         wait_vmcnt<0>();
         lds_barrier();
+        if constexpr (kRaceCheck) {
+            poison_lds(smem + st * T::STAGE, T::STAGE, tid, T::NT);
+            lds_barrier();
+        }
     }
-    // Causal: the blocks past this wave's queries, copies and barriers only.
+    // Causal: the blocks past this wave's queries, copies and barriers only
+    // (every wave passes the same barriers as the compute loop's).
     for (int b = nb_wave; b < nb; ++b) {
         if (b + 1 < nb) load_block(b + 1, (b & 1) ^ 1);
         wait_vmcnt<0>();
         lds_barrier();
+        if constexpr (kRaceCheck) {
+            poison_lds(smem + (b & 1) * T::STAGE, T::STAGE, tid, T::NT);
+            lds_barrier();
+        }
     }
 
     // O[qi][DT * row(r, g) + t] = O^T / l.

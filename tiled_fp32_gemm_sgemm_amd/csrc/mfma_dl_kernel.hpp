@@ -688,6 +688,11 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
             // barrier makes every wave's part of the slice visible.
             wait_slice(s + 1, ahead < nslices ? ahead : nslices - 1);
             lds_barrier();
+            if constexpr (kRaceCheck) {
+                // Slice s is consumed: its buffer is refilled only after this.
+                poison_lds(smem + buf * T::BUF_FLOATS, T::BUF_FLOATS, tid, T::NT);
+                lds_barrier();
+            }
             read_group((s + 1) % T::STAGES, 0, opa[0], opb[0]);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -696,6 +701,10 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
+    if constexpr (kRaceCheck) {
+        poison_lds(smem, T::STAGES * T::BUF_FLOATS, tid, T::NT);
+        lds_barrier();
+    }
 #pragma unroll
     for (int t = 0; t < T::STAGES - 1; ++t)
         if (t < nslices) load_slice(t);

@@ -285,6 +285,12 @@ void sgemm_mfma_kernel(GemmArgs p) {
         if (more) {
             if (T::NKG == 1) store_slice(buf ^ 1);
             __syncthreads();
+            if constexpr (kRaceCheck) {
+                // Slice s is consumed: its buffers are refilled only after this.
+                poison_lds(As0 + buf * T::A_FLOATS, T::A_FLOATS, threadIdx.x, T::NT);
+                poison_lds(Bs0 + buf * T::B_FLOATS, T::B_FLOATS, threadIdx.x, T::NT);
+                __syncthreads();
+            }
             read_group(buf ^ 1, 0, opa[LAST ^ 1], opb[LAST ^ 1]);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -292,6 +298,10 @@ void sgemm_mfma_kernel(GemmArgs p) {
         __builtin_amdgcn_sched_barrier(0);
     };
 
+    if constexpr (kRaceCheck) {
+        poison_lds(smem, 2 * (T::A_FLOATS + T::B_FLOATS), threadIdx.x, T::NT);
+        __syncthreads();
+    }
     load_slice(0);
     store_slice(0);
     __syncthreads();

@@ -13,7 +13,26 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Race-check build (SGEMM_RACECHECK = 1, a separate test library): every
+// LDS buffer is filled with NaN at the start of a workgroup and again as soon
+// as the workgroup is done with it (after the barrier that ends its use, with
+// a barrier after the fill), and workgroups take their tiles in reverse order.
+// A wave that read a slice before its copy had landed, or after its buffer was
+// handed on, would read NaN, and NaN reaches the result.  The product library
+// is built with SGEMM_RACECHECK = 0, where none of this is compiled in.
+#ifndef SGEMM_RACECHECK
+#define SGEMM_RACECHECK 0
+#endif
+
 namespace sgemm_dev {
+
+constexpr bool kRaceCheck = SGEMM_RACECHECK != 0;
+
+// n floats of LDS from p set to NaN by the nt threads of a workgroup (the
+// caller adds the barrier).
+__device__ __forceinline__ void poison_lds(float* p, int n, int tid, int nt) {
+    for (int i = tid; i < n; i += nt) p[i] = __builtin_nanf("");
+}
 
 // Geometry of a 2-D convolution run as an implicit GEMM (NHWC input, KRSC
 // filters, NPQK output): GEMM row m = (n * P + p) * Q + q, column = output
@@ -83,7 +102,8 @@ struct TileCoord {
 
 __device__ __forceinline__ TileCoord map_block(const GemmArgs& p, int group_m) {
     const uint32_t nblocks = gridDim.x;
-    const uint32_t pid = xcd_contiguous_id(blockIdx.x, nblocks);
+    const uint32_t bid = kRaceCheck ? nblocks - 1 - blockIdx.x : blockIdx.x;
+    const uint32_t pid = xcd_contiguous_id(bid, nblocks);
     const uint32_t per_matrix = (uint32_t)p.tiles_m * (uint32_t)p.tiles_n;
     TileCoord t;
     t.b = (int)(pid / per_matrix);

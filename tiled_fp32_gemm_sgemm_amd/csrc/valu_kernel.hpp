@@ -122,6 +122,10 @@ __global__ __launch_bounds__(256) void sgemm_valu_kernel(GemmArgs p) {
     };
 
     const int nslices = (p.K + T::BK - 1) / T::BK;
+    if constexpr (kRaceCheck) {
+        poison_lds(smem, 2 * (T::A_FLOATS + T::B_FLOATS), threadIdx.x, T::NT);
+        __syncthreads();
+    }
     load_slice(0);
     store_slice(0);
     __syncthreads();
@@ -132,6 +136,12 @@ __global__ __launch_bounds__(256) void sgemm_valu_kernel(GemmArgs p) {
         compute_slice(cur);
         if (more) store_slice(cur ^ 1);
         __syncthreads();
+        if constexpr (kRaceCheck) {
+            // Slice s is consumed: its buffers are refilled only after this.
+            poison_lds(As0 + cur * T::A_FLOATS, T::A_FLOATS, threadIdx.x, T::NT);
+            poison_lds(Bs0 + cur * T::B_FLOATS, T::B_FLOATS, threadIdx.x, T::NT);
+            __syncthreads();
+        }
     }
 
 #pragma unroll
