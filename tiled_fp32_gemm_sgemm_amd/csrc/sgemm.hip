@@ -92,6 +92,9 @@ using Dl128x64k64m32s2x2 =
     DlTile<128, 64, 64, 2, 2, 32, 2, 8, 2, 2, true, false, false, false, true, false, 2>;  // 8 waves of 64x32
 using Dl64x128k64m32s2x2 =
     DlTile<64, 128, 64, 2, 2, 32, 2, 8, 2, 2, true, false, false, false, true, false, 2>;  // 8 waves of 32x64
+// 96 x 96: one tile per CU at 1536^2 (16 x 16 tiles), 4 waves of 48 x 48 on
+// 16x16x4 MFMAs (3 x 3 accumulator tiles each).
+using Dl96x96k32m16 = DlTile<96, 96, 32, 2, 2, 16, 2, 8>;
 // Small LDS footprints, so that three or four workgroups share a CU and
 // their barriers fall at different times (4 waves of 64x64 or 32x32 each).
 using Dl128x128k16o4 = DlTile<128, 128, 16, 2, 2, 32, 4, 8, 2>;     // 32 KB LDS, 4 per CU
@@ -177,6 +180,7 @@ const ConfigEntry kConfigs[] = {
     SGEMM_DL_CFG(Dl128x128k16o3s3, "dl32_128x128x16_w2x2_s3_o3", 3, 3.7375e-04, 4.0480e-06, 5.7368e-04, 1.0599e-05),
     SGEMM_DLX_CFG(Dl64x64k32o4, "dl32_64x64x32_w2x2_o4", 4, 7.5602e-04, 4.4574e-06, 1.4899e-03, 1.4845e-05),
     SGEMM_DLX_CFG(Dl64x128k64m32s2x2, "dl32_64x128x64_w2x2_s2_k2", 1, 5.6513e-04, 3.6309e-06, 9.9029e-04, 7.2336e-06),
+    SGEMM_DL_CFG(Dl96x96k32m16, "dl16_96x96x32_w2x2", 3, 5.7956e-04, 4.1848e-06, 8.6320e-04, 1.0753e-05),
 };
 #undef SGEMM_CFG
 #undef SGEMM_DL_CFG
