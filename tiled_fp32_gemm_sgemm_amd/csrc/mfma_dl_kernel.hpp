@@ -359,7 +359,11 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
         }
     };
 
-    auto load_direct = [&](int k0, int buf) {
+    // The copies of a direct slice with index j in [lo, hi): this wave's A
+    // chunks are j < A_CHW, its B chunks the rest.  Schedule 2 issues them
+    // one per k step; otherwise (and always for a convolution, whose offsets
+    // are rebuilt at a new filter tap) all at once.
+    auto load_direct_part = [&](int k0, int buf, int lo, int hi) {
         float* const dstA = smem + buf * T::BUF_FLOATS;
         float* const dstB = dstA + T::A_FLOATS;
         int a_range = (int)a_span;
@@ -379,30 +383,6 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
         const __amdgpu_buffer_rsrc_t rb =
             __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, (int)b_span, 0x00020000);
 #pragma unroll
-        for (int j = 0; j < T::A_CHW; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                ra, (lds_void_t*)(dstA + 256 * (wave * T::A_CHW + j)), 16, a_off[j], 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < T::B_CHW; ++j)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rb, (lds_void_t*)(dstB + 256 * (wave * T::B_CHW + j)), 16, b_off[j], 0, 0, 0);
-    };
-
-    // The copies of a direct slice with index j in [lo, hi): this wave's A
-    // chunks are j < A_CHW, its B chunks the rest (SCHED = 2 issues them one
-    // per k step).
-    auto load_direct_part = [&](int k0, int buf, int lo, int hi) {
-        float* const dstA = smem + buf * T::BUF_FLOATS;
-        float* const dstB = dstA + T::A_FLOATS;
-        const float* const a_base =
-            p.A + uniform_i64(a_org + (T::A_KC ? (int64_t)k0 : (int64_t)k0 * p.lda));
-        const float* const b_base =
-            p.B + uniform_i64(b_org + (T::B_KC ? (int64_t)k0 : (int64_t)k0 * p.ldb));
-        const __amdgpu_buffer_rsrc_t ra =
-            __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, (int)a_span, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rb =
-            __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, (int)b_span, 0x00020000);
-#pragma unroll
         for (int j = 0; j < T::LPS; ++j) {
             if (j < lo || j >= hi) continue;
             if (j < T::A_CHW)
@@ -414,6 +394,7 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
                     b_off[j - T::A_CHW], 0, 0, 0);
         }
     };
+    auto load_direct = [&](int k0, int buf) { load_direct_part(k0, buf, 0, T::LPS); };
 
     // Fallback for slices with quads that straddle the matrix edge: masked
     // element loads through registers, written to the same layout.
