@@ -67,8 +67,9 @@ typedef enum sgemm_status {
 } sgemm_status_t;
 
 /*
- * Single product on the matrix cores (v_mfma_f32_32x32x2_f32), block tile
- * chosen from the shape.  Arguments: sizes M, N, K (>= 0); A with leading
+ * Single product on the matrix cores (v_mfma_f32_32x32x2_f32, or
+ * v_mfma_f32_16x16x4_f32 on the 96 x 96 tile), block tile chosen from the
+ * shape.  Arguments: sizes M, N, K (>= 0); A with leading
  * dimension lda; B with ldb; C with ldc; stream.
  */
 int sgemm(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda, const float *B,

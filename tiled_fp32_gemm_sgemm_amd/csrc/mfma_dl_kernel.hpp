@@ -139,8 +139,17 @@ struct DlTile {
     static constexpr int BV = (B_KC || !BIL) ? 1
                               : MI == 16 ? (TN % 4 == 0 ? 4 : 1)
                                          : (TN % 4 == 0 ? 4 : TN % 2 == 0 ? 2 : 1);
+    // The same interleave for an A operand staged [k][m] (A^T stored): lane
+    // li of row tile mi supplies wave-tile row (mi / AV) * MI * AV + li * AV +
+    // mi % AV, so the AV values of A a lane needs at one k are adjacent and
+    // come in one ds_read_b64 / ds_read_b128 (a pass again reads one
+    // contiguous run of a k row), and the output rows of the AV tiles
+    // interleave the same way.
+    static constexpr int AV = (A_KC || !BIL) ? 1
+                              : MI == 16 ? (TM % 4 == 0 ? 4 : 1)
+                                         : (TM % 4 == 0 ? 4 : TM % 2 == 0 ? 2 : 1);
     // Quad flip on odd lane-group row blocks of an operand staged [k][mn].
-    static constexpr int AFLIP = MI == 16 ? 4 : 0;
+    static constexpr int AFLIP = (MI == 16 && AV == 1) ? 4 : 0;
     static constexpr int BFLIP = (MI == 16 && BV == 1) ? 4 : 0;
     // Register-staged fallback: quads per thread per slice.
     static constexpr int A_VEC = BM * BK / 4 / NT;
@@ -162,6 +171,7 @@ struct DlTile {
     static_assert((BM * BK / 4) % NT == 0 && (BK * BN / 4) % NT == 0, "fallback copy must split");
     static_assert(MI == 32 || (BN >= 32 && BM >= 32), "the flip needs 32-float rows");
     static_assert(TN % BV == 0, "whole vectors of column tiles");
+    static_assert(TM % AV == 0, "whole vectors of row tiles");
     static_assert(!CONV || (A_KC && B_KC && !EX), "convolution: k-contiguous A and B, beta = 0");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
     static_assert(SCHED >= 0 && SCHED <= 2, "slice schedule");
@@ -176,6 +186,10 @@ struct DlTile {
     // Wave-tile column of lane li in column tile ni (see BIL).
     static __device__ __forceinline__ int bcol(int ni, int li) {
         return (ni / BV) * MI * BV + li * BV + ni % BV;
+    }
+    // Wave-tile row of row i (the lane that supplies it) in row tile mi (see AV).
+    static __device__ __forceinline__ int arow(int mi, int i) {
+        return (mi / AV) * MI * AV + i * AV + mi % AV;
     }
     using AReg = std::conditional_t<A_KC, f32x4, F4>;
     using BReg = std::conditional_t<B_KC, f32x4, F4>;
@@ -520,9 +534,11 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     const int kfirst = kgrp * T::KSUB + lg * T::KPL;
     const int kflip_a = 4 * T::flipA(kfirst);
     const int kflip_b = 4 * T::flipB(kfirst);
-    int a_col[T::TM];
+    // First row of each AV-wide run of row tiles (AV = 1: every tile).
+    constexpr int NAV = T::TM / T::AV;
+    int a_col[NAV];
 #pragma unroll
-    for (int mi = 0; mi < T::TM; ++mi) a_col[mi] = (wy * T::WTM + T::MI * mi + li) ^ kflip_a;
+    for (int h = 0; h < NAV; ++h) a_col[h] = (wy * T::WTM + T::arow(h * T::AV, li)) ^ kflip_a;
     // First column of each BV-wide run of column tiles (BV = 1: every tile).
     constexpr int NBV = T::TN / T::BV;
     int b_col[NBV];
@@ -539,7 +555,7 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     // run of column tiles); read_items issues those with index in [lo, hi).
     using AReg = typename T::AReg;
     using BReg = typename T::BReg;
-    constexpr int NA_ITEMS = T::A_KC ? T::TM : T::KG * T::TM;
+    constexpr int NA_ITEMS = T::A_KC ? T::TM : T::KG * NAV;
     constexpr int NB_ITEMS = T::B_KC ? T::TN : T::KG * NBV;
     constexpr int N_ITEMS = NA_ITEMS + NB_ITEMS;
     auto read_items = [&](int buf, int g, int lo, int hi, AReg (&a)[T::TM], BReg (&b)[T::TN]) {
@@ -553,9 +569,15 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
             if (i < NA_ITEMS) {
                 if constexpr (T::A_KC) {
                     a[i] = *(const f32x4*)(As + (a_row + T::MI * i) * T::BK + ((quad ^ a_swz) << 2));
-                } else {
+                } else if constexpr (T::AV == 1) {
                     const int st = i / T::TM, mi = i % T::TM;
                     a[mi][st] = As[(krow + st) * T::LDA_S + a_col[mi]];
+                } else {
+                    typedef float avec_t __attribute__((ext_vector_type(T::AV)));
+                    const int st = i / NAV, h = i % NAV;
+                    const avec_t v = *(const avec_t*)(As + (krow + st) * T::LDA_S + a_col[h]);
+#pragma unroll
+                    for (int u = 0; u < T::AV; ++u) a[h * T::AV + u][st] = v[u];
                 }
             } else {
                 const int j = i - NA_ITEMS;
@@ -732,8 +754,8 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
         }
     }
 
-    // Epilogue: accumulator r of lane (li, lg) in MFMA tile (mi, ni) is row
-    // Op::row(r, lg) of that tile and wave-tile column bcol(ni, li).  The
+    // Epilogue: accumulator r of lane (li, lg) in MFMA tile (mi, ni) is
+    // wave-tile row arow(mi, Op::row(r, lg)) and column bcol(ni, li).  The
     // general form stores
     // alpha * acc, plus beta * C when beta != 0 (C is not read otherwise); the
     // choice is made once, outside the store loop.
@@ -752,7 +774,7 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
                 const int col = wx * T::WTN + T::bcol(h * T::BV, li);
 #pragma unroll
                 for (int r = 0; r < Op::ACC; ++r) {
-                    const int row = wy * T::WTM + T::MI * mi + Op::row(r, lg);
+                    const int row = wy * T::WTM + T::arow(mi, Op::row(r, lg));
                     float* const c = C + (int64_t)row * p.ldc + col;
                     cvec_t v;
 #pragma unroll
