@@ -95,6 +95,13 @@ using Dl64x128k64m32s2x2 =
 // 96 x 96: one tile per CU at 1536^2 (16 x 16 tiles), 4 waves of 48 x 48 on
 // 16x16x4 MFMAs (3 x 3 accumulator tiles each).
 using Dl96x96k32m16 = DlTile<96, 96, 32, 2, 2, 16, 2, 8>;
+// 128 x 128 with two k groups (8 waves of 64 x 64, two per SIMD) and copies
+// spread over the k steps: one tile per CU at 2048^2 without dropping to one
+// wave per SIMD (2048^3: 135.9 -> 138.0 TFLOP/s; 1024 x 4096 x 4096: 138.5 ->
+// 142.3).  No convolution variant: with the convolution's burst copies it ran
+// the 3x3 layers 1.5-2 % slower than the tile they use.
+using Dl128x128k64m32s2x2 =
+    DlTile<128, 128, 64, 2, 2, 32, 2, 8, 2, 2, true, false, false, false, true, false, 2>;
 // Small LDS footprints, so that three or four workgroups share a CU and
 // their barriers fall at different times (4 waves of 64x64 or 32x32 each).
 using Dl128x128k16o4 = DlTile<128, 128, 16, 2, 2, 32, 4, 8, 2>;     // 32 KB LDS, 4 per CU
@@ -148,6 +155,15 @@ using DlConv = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::OCC
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, false, true>>,                        \
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, true>> },                        \
       (const void*)&sgemm_mfma_dl_kernel<DlConv<T>> }
+// General form, no convolution variant.
+#define SGEMM_DLG_CFG(T, name, per_cu, a1, b1, a2, b2)                                       \
+    { name, T::BM, T::BN, T::BK, T::NT, T::WG_PER_CU, (const void*)&sgemm_mfma_dl_kernel<T>, \
+      per_cu, a1, b1, a2, b2,                                                                 \
+      { (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, false, false>>,                       \
+        (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, false>>,                        \
+        (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, false, true>>,                        \
+        (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, true>> },                        \
+      nullptr }
 
 const ConfigEntry kConfigs[] = {
     SGEMM_CFG(Cfg256x128, "mfma32_256x128x16_w2x2", 1, 3.6505e-04, 4.2029e-06, 4.1134e-04, 8.0806e-06),
@@ -181,10 +197,12 @@ const ConfigEntry kConfigs[] = {
     SGEMM_DLX_CFG(Dl64x64k32o4, "dl32_64x64x32_w2x2_o4", 4, 7.5602e-04, 4.4574e-06, 1.4899e-03, 1.4845e-05),
     SGEMM_DLX_CFG(Dl64x128k64m32s2x2, "dl32_64x128x64_w2x2_s2_k2", 1, 5.6513e-04, 3.6309e-06, 9.9029e-04, 7.2336e-06),
     SGEMM_DL_CFG(Dl96x96k32m16, "dl16_96x96x32_w2x2", 3, 5.7956e-04, 4.1848e-06, 8.6320e-04, 1.0753e-05),
+    SGEMM_DLG_CFG(Dl128x128k64m32s2x2, "dl32_128x128x64_w2x2_s2_k2", 1, 5.9521e-04, 3.4661e-06, 7.0309e-04, 6.9811e-06),
 };
 #undef SGEMM_CFG
 #undef SGEMM_DL_CFG
 #undef SGEMM_DLX_CFG
+#undef SGEMM_DLG_CFG
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 constexpr int kNumCu = 256;  // MI355X compute units
 
