@@ -1,0 +1,114 @@
+"""The library's calls inside a captured HIP graph (torch.cuda.CUDAGraph).
+
+Each entry point only enqueues kernels on the caller's stream (no memset, no
+allocation, no synchronisation), so it can be captured.  Each test captures
+calls into static output buffers, then replays the graph several times.
+Between replays it does eager work of its own: the outputs are overwritten
+with NaN and other library calls run on other operands.  Every replay must
+reproduce the eager result bit for bit, because the same kernels run on the
+same inputs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import tiled_fp32_gemm_sgemm_amd as sg
+
+pytestmark = pytest.mark.gpu
+
+REPLAYS = 3
+
+
+def _dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda:0")
+
+
+def _replays_match(capture, outputs, eager_between):
+    """capture() enqueues the calls; outputs are the tensors they write."""
+    # Eager reference, then the graph (warm-up on a side stream first, as
+    # torch's capture rules ask).
+    capture()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outputs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        capture()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        capture()
+    torch.cuda.synchronize()
+    for r in range(REPLAYS):
+        for o in outputs:
+            o.fill_(float("nan"))
+        eager_between()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, want in zip(outputs, ref):
+            assert torch.equal(o.view(torch.int32), want.view(torch.int32)), \
+                "replay %d differs from the eager result" % r
+
+
+def _other_work(dev):
+    a = torch.randn(300, 200, device=dev)
+    b = torch.randn(200, 100, device=dev)
+
+    def run():
+        sg.sgemm(a, b)
+    return run
+
+
+def test_graph_sgemm_and_batched():
+    dev = _dev()
+    gen = torch.Generator(device=dev).manual_seed(3)
+    A = torch.randn(1000, 900, device=dev, generator=gen)
+    B = torch.randn(900, 700, device=dev, generator=gen)
+    C = torch.empty(1000, 700, device=dev)
+    Ab = torch.randn(6, 130, 70, device=dev, generator=gen)
+    Bb = torch.randn(6, 70, 90, device=dev, generator=gen)
+    Cb = torch.empty(6, 130, 90, device=dev)
+
+    def capture():
+        sg.sgemm(A, B, C)
+        sg.sgemm_strided_batched(Ab, Bb, Cb)
+        sg.sgemm(A[:64, :64], B[:64, :64], C[:64, :64], path="valu")
+    _replays_match(capture, [C, Cb], _other_work(dev))
+
+
+def test_graph_general_form():
+    dev = _dev()
+    gen = torch.Generator(device=dev).manual_seed(5)
+    At = torch.randn(513, 257, device=dev, generator=gen)  # stored K x M
+    B = torch.randn(513, 300, device=dev, generator=gen)
+    C0 = torch.randn(257, 300, device=dev, generator=gen)
+    C = torch.empty_like(C0)
+
+    def capture():
+        torch.mul(C0, 1.0, out=C)  # the graph's own reset (a kernel), so beta reads the same C
+        sg.sgemm_ex(At, B, C, alpha=1.5, beta=-0.5, transA=True)
+    _replays_match(capture, [C], _other_work(dev))
+
+
+def test_graph_window_conv_attention():
+    dev = _dev()
+    gen = torch.Generator(device=dev).manual_seed(7)
+    x = torch.rand(100003 + 4, device=dev, generator=gen)
+    y = torch.empty(100003, device=dev)
+    xi = torch.randn(2, 9, 11, 64, device=dev, generator=gen)
+    wt = torch.randn(40, 3, 3, 64, device=dev, generator=gen)
+    yc = torch.empty(2, 9, 11, 40, device=dev)
+    q = torch.randn(2, 300, 64, device=dev, generator=gen)
+    k = torch.randn(2, 513, 64, device=dev, generator=gen)
+    v = torch.randn(2, 513, 64, device=dev, generator=gen)
+    o = torch.empty(2, 300, 64, device=dev)
+
+    def capture():
+        sg.window_sum(x, 5, out=y)
+        sg.conv2d_nhwc(xi, wt, pad=1, out=yc)
+        sg.attention(q, k, v, causal=True, out=o)
+    _replays_match(capture, [y, yc, o], _other_work(dev))
+    assert np.isfinite(o.cpu().numpy()).all()
