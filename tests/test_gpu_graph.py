@@ -112,3 +112,49 @@ def test_graph_window_conv_attention():
         sg.attention(q, k, v, causal=True, out=o)
     _replays_match(capture, [y, yc, o], _other_work(dev))
     assert np.isfinite(o.cpu().numpy()).all()
+
+
+def test_host_threads_on_their_own_streams():
+    """The library keeps no mutable global state: four host threads, each on
+    its own stream, calling different entry points at once, give the same
+    bits as the same calls made one after another."""
+    import threading
+    dev = _dev()
+    gen = torch.Generator(device=dev).manual_seed(11)
+    jobs = []
+    for t in range(4):
+        A = torch.randn(500 + 37 * t, 300 + 11 * t, device=dev, generator=gen)
+        B = torch.randn(300 + 11 * t, 400 - 13 * t, device=dev, generator=gen)
+        jobs.append((A, B, torch.empty(A.shape[0], B.shape[1], device=dev)))
+    xs = torch.rand(50000, device=dev, generator=gen)
+    ref = [sg.sgemm(A, B) for A, B, _ in jobs]
+    ref_w = sg.window_sum(xs, 7)
+    torch.cuda.synchronize()
+    out_w = torch.empty_like(ref_w)
+    errors = []
+
+    def work(t):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(20):
+                    A, B, C = jobs[t]
+                    sg.sgemm(A, B, C, path="valu" if t == 3 else "mfma")
+                    if t == 0:
+                        sg.window_sum(xs, 7, out=out_w)
+            s.synchronize()
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for t, (A, B, C) in enumerate(jobs):
+        want = ref[t] if t != 3 else sg.sgemm(A, B, path="valu")
+        torch.cuda.synchronize()
+        assert torch.equal(C, want), "thread %d" % t
+    assert torch.equal(out_w, ref_w)
