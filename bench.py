@@ -627,6 +627,9 @@ def main(argv=None) -> int:
                     help="GEMM path (window: counter summaries of the window kernel only)")
     ap.add_argument("--workload", default="square4096")
     ap.add_argument("--config", type=int, default=None, help="force a matrix-core tile config")
+    ap.add_argument("--graph", action="store_true",
+                    help="GEMM: capture the timed launches in one HIP graph (torch.cuda.CUDAGraph) and "
+                         "time its replay, so host-side launch cost drops out")
     ap.add_argument("--cold", action="store_true",
                     help="GEMM: before every timed launch, write a 512 MiB buffer (more than the "
                          "256 MB last-level cache) so the operands come from HBM; each launch is "
@@ -798,8 +801,49 @@ def main(argv=None) -> int:
         steps = args.steps if args.steps is not None else max(50, n)
         return warm, steps
 
+    def graph_timed(n_steps, n_warm):
+        """The n_steps launches captured once and replayed: GPU time per
+        launch without the host's launch cost."""
+        for _ in range(n_warm):
+            step()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            gh = torch.cuda.current_stream().cuda_stream
+            for _ in range(n_steps):
+                if w.batch == 1:
+                    st = sg.sgemm_raw(w.M, w.N, w.K, A.data_ptr(), w.lda, B.data_ptr(), w.ldb,
+                                      C.data_ptr(), w.ldc, gh, args.path)
+                else:
+                    st = sg.sgemm_strided_batched_raw(w.M, w.N, w.K, A.data_ptr(), w.lda,
+                                                      w.strideA, B.data_ptr(), w.ldb, w.strideB,
+                                                      C.data_ptr(), w.ldc, w.strideC, w.batch, gh,
+                                                      args.path, args.config)
+                if st != 0:
+                    raise sg.SgemmError(st, "sgemm (graph capture)")
+        g.replay()  # first replay uploads the graph
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        g.replay()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n_steps
+
     args.warmup, args.steps = counts()
-    if args.cold:
+    if args.graph and args.cold:
+        print("--graph and --cold exclude each other", file=sys.stderr)
+        return 2
+    if args.graph:
+        ms = graph_timed(args.steps, args.warmup)
+        single = per_launch(min(args.steps, 50), False)
+    elif args.cold:
         for _ in range(args.warmup):
             step()
         single = per_launch(args.steps, True)
@@ -862,6 +906,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "pct_of_fp32_peak": 100.0 * tflops / PEAK_FP32_TFLOPS,
         "cache": "cold" if args.cold else "warm",
+        "launch": "hip_graph" if args.graph else "stream",
         "single_launch": {"n": len(single),
                           "median_ms": single[len(single) // 2],
                           "min_ms": single[0],
