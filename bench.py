@@ -270,8 +270,10 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
     open(out, "w").write("\n".join(L) + "\n")
 
 
-def cpu_baseline(w, A, B, target_s: float = 12.0):
-    """The oracle, untouched, on the leading rows of C of the same workload."""
+def cpu_baseline(w, A, B, target_s: float = 12.0, keep=None):
+    """The oracle, untouched, on the leading rows of C of the same workload.
+    With a dict `keep`, the rows' reference values and magnitude sums are
+    left in it (for the parity check beside the timing)."""
     import oracle
     a = A.numpy()
     b = B.numpy()
@@ -281,14 +283,47 @@ def cpu_baseline(w, A, B, target_s: float = 12.0):
     dt0 = time.perf_counter() - t0
     rows = int(min(w.M, max(rows0, rows0 * target_s / max(dt0, 1e-6))))
     t0 = time.perf_counter()
-    _, _, used = oracle.sgemm_f64(rows, w.N, w.K, a, w.lda, b, w.ldb)
+    ref, mag, used = oracle.sgemm_f64(rows, w.N, w.K, a, w.lda, b, w.ldb)
     dt = time.perf_counter() - t0
+    if keep is not None:
+        keep.update(rows=rows, ref=ref, mag=mag)
     flops = 2.0 * rows * w.N * w.K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(used), "kind": "oracle",
             "sample": "rows 0..%d of C for %s (%dx%dx%d, %.3g GFLOP) in %.2f s, FP64 "
                       "accumulation, OpenMP over rows" % (rows - 1, w.name, rows, w.N, w.K,
                                                           flops / 1e9, dt),
             "seconds": dt}
+
+
+def gemm_parity(C_rows, keep, rel_tol: float = 2e-4):
+    """The timed kernel's output rows against the oracle's: the largest
+    |C - C_ref| / sum_k |A||B| (the acceptance bound is 2e-4)."""
+    import numpy as np
+    got = np.asarray(C_rows, dtype=np.float64)
+    ref, mag = keep["ref"], keep["mag"]
+    err = np.abs(got - ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(mag > 0, err / mag, np.where(err > 0, np.inf, 0.0))
+    worst = float(ratio.max())
+    return {"rows_checked": int(keep["rows"]), "max_err_over_abs_products": worst,
+            "bound": rel_tol, "within_bound": bool(worst <= rel_tol),
+            "bitwise_equal_to_rounded_oracle": bool(np.array_equal(
+                got.astype(np.float32).view(np.uint32),
+                ref.astype(np.float32).view(np.uint32)))}
+
+
+def host_info():
+    import torch
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "torch": torch.__version__, "hip": torch.version.hip}
 
 
 def window_cpu_baseline(w, x_cpu):
@@ -888,8 +923,17 @@ def main(argv=None) -> int:
                                                "operands, same timing"}
 
     cpu = None
+    parity = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, A_cpu, B_cpu)
+        keep = {}
+        cpu = cpu_baseline(w, A_cpu, B_cpu, keep=keep)
+        if w.batch == 1 and not args.graph:
+            # One more launch of the timed path (the comparators wrote C too).
+            step()
+            torch.cuda.synchronize()
+            rows = keep["rows"]
+            C_rows = C[:rows * w.ldc].view(rows, w.ldc)[:, :w.N].cpu().numpy()
+            parity = gemm_parity(C_rows, keep)
 
     out = {
         "metric": METRIC,
@@ -916,8 +960,10 @@ def main(argv=None) -> int:
                    "path": args.path, "tile": tile},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "parity": parity,
         "comparators": comparators,
         "device": torch.cuda.get_device_name(dev),
+        "host": host_info(),
     }
     print(json.dumps(out), flush=True)
     return 0

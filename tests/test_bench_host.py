@@ -71,3 +71,24 @@ def test_trace_summary_averages_the_timed_dispatches(tmp_path):
 def test_cold_is_for_gemms_only(capsys):
     assert bench.main(["--workload", "window5", "--cold"]) == 2
     assert "GEMM" in capsys.readouterr().err
+
+
+def test_gemm_parity_ratio():
+    """The bench's parity field: largest |C - C_ref| / sum |A||B|, the bound
+    check, and exact equality of the FP32-rounded oracle."""
+    import numpy as np
+    ref = np.array([[1.0, 2.0], [3.0, 0.0]])
+    mag = np.array([[4.0, 2.0], [6.0, 0.0]])
+    keep = {"rows": 2, "ref": ref, "mag": mag}
+    same = bench.gemm_parity(ref.astype(np.float32), keep)
+    assert same["max_err_over_abs_products"] == 0.0 and same["within_bound"]
+    assert same["bitwise_equal_to_rounded_oracle"]
+    off = ref.astype(np.float32).copy()
+    off[1, 0] += 6.0 * 1e-3
+    got = bench.gemm_parity(off, keep)
+    assert abs(got["max_err_over_abs_products"] - 1e-3) < 1e-6
+    assert not got["within_bound"] and not got["bitwise_equal_to_rounded_oracle"]
+    # A nonzero error where the magnitude sum is zero is unbounded.
+    bad = ref.astype(np.float32).copy()
+    bad[1, 1] = 1e-30
+    assert not bench.gemm_parity(bad, keep)["within_bound"]
