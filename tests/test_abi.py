@@ -23,6 +23,19 @@ def test_library_exports_every_header_function():
         ctypes.cast(getattr(lib, n), ctypes.c_void_p)
 
 
+def test_racecheck_library_exports_the_same_abi():
+    """The race-check build (used by the GPU race-sensitivity tests) exports
+    every function the headers declare, with the same tile table."""
+    lib = _native.lib()
+    rc = _native.racecheck_lib()
+    for n in _native.header_functions():
+        assert hasattr(rc, n), n
+    assert rc.sgemm_num_configs() == lib.sgemm_num_configs()
+    # Host-side argument checks behave alike (nothing is enqueued).
+    assert rc.sgemm(-1, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, None) == \
+        lib.sgemm(-1, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4, None)
+
+
 @pytest.mark.parametrize("path", ["mfma", "valu"])
 @pytest.mark.parametrize("args,code", [
     ((-1, 4, 4, FAKE, 4, FAKE, 4, FAKE, 4), -1),        # negative M
