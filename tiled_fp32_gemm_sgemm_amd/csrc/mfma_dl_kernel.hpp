@@ -124,6 +124,9 @@ struct DlTile {
     // read as one contiguous run: 32 lanes x 8 bytes or 16 lanes x 16 bytes,
     // all 64 banks once.  With MI = 16 only BV = 4 keeps a pass inside one k
     // row; other widths keep BV = 1 and the row flip below.
+    // A B operand staged [n][k] (stored N x K) takes the same interleave for
+    // its stores: its quad reads stay at rows MI * ni + li, and the copies
+    // place logical column bcol(ni, li) there (bkc_row).
     static constexpr bool BIL = BIL_;
     // Slice schedule (see the kernel body):
     //   SCHED = 0: the next operand group's LDS reads go out at once, before
@@ -136,7 +139,7 @@ struct DlTile {
     static constexpr int SCHED = SCHED_;
     static constexpr bool ILV = SCHED >= 1;
     static constexpr bool SPREAD_COPIES = SCHED >= 2 && !CONV_;
-    static constexpr int BV = (B_KC || !BIL) ? 1
+    static constexpr int BV = !BIL ? 1
                               : MI == 16 ? (TN % 4 == 0 ? 4 : 1)
                                          : (TN % 4 == 0 ? 4 : TN % 2 == 0 ? 2 : 1);
     // The same interleave for an A operand staged [k][m] (A^T stored): lane
@@ -186,6 +189,17 @@ struct DlTile {
     // Wave-tile column of lane li in column tile ni (see BIL).
     static __device__ __forceinline__ int bcol(int ni, int li) {
         return (ni / BV) * MI * BV + li * BV + ni % BV;
+    }
+    // Logical column held by row `slot` of a B operand staged [n][k]: within
+    // each run of MI * BV rows, row MI * c + l holds column l * BV + c (so the
+    // rows MI * ni + li that tile ni reads hold the columns bcol(ni, li)).
+    static __device__ __forceinline__ int bkc_row(int slot) {
+        if constexpr (BV == 1) {
+            return slot;
+        } else {
+            const int run = slot / (MI * BV), s = slot % (MI * BV);
+            return run * MI * BV + (s % MI) * BV + s / MI;
+        }
     }
     // Wave-tile row of row i (the lane that supplies it) in row tile mi (see AV).
     static __device__ __forceinline__ int arow(int mi, int i) {
@@ -311,8 +325,9 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
             const int r = q / T::B_QPR;
             if constexpr (T::B_KC) {
                 const int kq = (q % T::B_QPR) ^ T::swz(r);
-                const bool ok = r < cols_left && 4 * kq < kleft;
-                b_off[j] = ok ? (uint32_t)(((int64_t)r * p.ldb + 4 * kq) * 4) : kOutOfRange;
+                const int n = T::bkc_row(r);
+                const bool ok = n < cols_left && 4 * kq < kleft;
+                b_off[j] = ok ? (uint32_t)(((int64_t)n * p.ldb + 4 * kq) * 4) : kOutOfRange;
             } else {
                 const int nq = (q % T::B_QPR) ^ T::flipB(r);
                 const bool ok = r < kleft && 4 * nq < cols_left;
@@ -464,8 +479,9 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
             f32x4 x;
             if constexpr (T::B_KC) {
                 const int kq = (q % T::B_QPR) ^ T::swz(r);
-                x = ldg4_masked(B + (int64_t)r * p.ldb + k0 + 4 * kq,
-                                r < cols_left ? p.K - (k0 + 4 * kq) : 0);
+                const int n = T::bkc_row(r);
+                x = ldg4_masked(B + (int64_t)n * p.ldb + k0 + 4 * kq,
+                                n < cols_left ? p.K - (k0 + 4 * kq) : 0);
             } else {
                 const int nq = (q % T::B_QPR) ^ T::flipB(r);
                 x = ldg4_masked(B + (int64_t)(k0 + r) * p.ldb + 4 * nq,
