@@ -662,6 +662,9 @@ def main(argv=None) -> int:
                     help="GEMM path (window: counter summaries of the window kernel only)")
     ap.add_argument("--workload", default="square4096")
     ap.add_argument("--config", type=int, default=None, help="force a matrix-core tile config")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="split-K comparator: k chunks per output tile (0: the time model's "
+                         "plan, which may be the plain kernel)")
     ap.add_argument("--graph", action="store_true",
                     help="GEMM: capture the timed launches in one HIP graph (torch.cuda.CUDAGraph) and "
                          "time its replay, so host-side launch cost drops out")
@@ -748,6 +751,7 @@ def main(argv=None) -> int:
     import torch
     from workloads import WORKLOADS, workload_operands
     import tiled_fp32_gemm_sgemm_amd as sg
+    from tiled_fp32_gemm_sgemm_amd import _native
 
     w = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -760,7 +764,18 @@ def main(argv=None) -> int:
     stream = torch.cuda.current_stream(dev)
     handle = stream.cuda_stream
 
+    if w.batch == 1:
+        sk_config, sk_splits, sk_bytes = sg.splitk_plan(w.M, w.N, w.K, args.splits)
+        sk_ws = torch.zeros(max(sk_bytes, 256), dtype=torch.uint8, device=dev)
+
     def step(path=args.path, config=args.config):
+        if path == "splitk":
+            st = _native.lib().sgemm_splitk(-1, w.M, w.N, w.K, A.data_ptr(), w.lda,
+                                            B.data_ptr(), w.ldb, C.data_ptr(), w.ldc,
+                                            args.splits, sk_ws.data_ptr(), sk_ws.numel(), handle)
+            if st != 0:
+                raise sg.SgemmError(st, "sgemm_splitk")
+            return
         if path == "torch":
             # hipBLASLt / rocBLAS through torch on the same operands (the
             # result goes to a fresh output; C is not touched).
@@ -915,6 +930,14 @@ def main(argv=None) -> int:
         other = "valu" if args.path == "mfma" else "mfma"
         oms = timed(max(5, args.steps // 5), 3, other, None)
         comparators[other] = {"tflops": flops / (oms * 1e-3) / 1e12, "ms_per_step": oms}
+        if args.path == "mfma" and not args.cold:
+            s_warm, s_steps = counts("splitk", None)
+            sms = timed(s_steps, s_warm, "splitk", None)
+            comparators["splitk"] = {"tflops": flops / (sms * 1e-3) / 1e12, "ms_per_step": sms,
+                                     "tile": sg.config_info(sk_config)["name"],
+                                     "splits": sk_splits,
+                                     "note": "sgemm_splitk (k chunks joined in the launch), "
+                                             "same timing"}
     if not args.no_comparator and not args.cold:
         t_warm, t_steps = counts("torch", None)
         tms = timed(t_steps, t_warm, "torch", None)

@@ -63,7 +63,10 @@ typedef enum sgemm_status {
        not built for the general form. */
     SGEMM_STATUS_INVALID_CONFIG = -7,
     /* A transpose flag of the general form is neither 0 nor 1. */
-    SGEMM_STATUS_INVALID_OP = -8
+    SGEMM_STATUS_INVALID_OP = -8,
+    /* Split-K: the workspace is NULL or smaller than sgemm_splitk_plan
+       reports for the same arguments. */
+    SGEMM_STATUS_INVALID_WORKSPACE = -9
 } sgemm_status_t;
 
 /*
@@ -223,6 +226,51 @@ int sgemm_autotune(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
                    int64_t strideA, const float *B, int64_t ldb, int64_t strideB, float *C,
                    int64_t ldc, int64_t strideC, int64_t batch, hipStream_t stream, int reps,
                    int *best_config, float *best_ms);
+
+/*
+ * Split-K product for under-filled grids, C = A x B with the semantics of
+ * sgemm (row-major, beta = 0, C's window overwritten and nothing else
+ * written).  The k loop of "Tiling Strategies" section 2 is cut into `splits`
+ * chunks of whole BK slices; each output tile gets one workgroup per chunk,
+ * so a thin product (few BM x BN tiles, long K) still fills the CUs.  The
+ * chunks' partial tiles join inside the same launch: each workgroup writes
+ * its partial to the workspace and counts itself in on the tile's counter;
+ * the last one to arrive adds the partials in chunk order 0, 1, ... (so the
+ * result does not depend on timing and is bit-reproducible), resets the
+ * counter and stores the tile.  No workgroup waits for another.
+ *
+ * config: a configuration with a split-K variant (sgemm_config_has_splitk),
+ *   or -1 for the choice of the time model (which may be the plain kernel).
+ * splits: requested chunk count, 1 ... 64, or 0 for the time model's choice;
+ *   the count used is at most ceil(K / BK) (sgemm_splitk_plan reports it).
+ * workspace, workspace_bytes: device memory owned by the caller, at least
+ *   sgemm_splitk_plan(...) bytes for the same config, sizes and splits
+ *   (a count that resolves to one chunk needs none: NULL and 0 are accepted).
+ *   The workspace must hold zeros before its first use (e.g. allocated
+ *   with hipMemset or torch.zeros); every call that completes leaves its
+ *   counters at zero again, so it is zeroed once, not per call.  Calls that may
+ *   run at the same time need workspaces of their own; concurrent calls on
+ *   one workspace race.
+ * Errors as for sgemm, plus SGEMM_STATUS_INVALID_CONFIG (no split-K variant),
+ * SGEMM_STATUS_INVALID_SIZE (splits outside 0 ... 64) and
+ * SGEMM_STATUS_INVALID_WORKSPACE; on an error nothing is enqueued.
+ */
+int sgemm_splitk(int config, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
+                 const float *B, int64_t ldb, float *C, int64_t ldc, int64_t splits,
+                 void *workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The plan sgemm_splitk would run for these arguments: stores the tile
+ * configuration in *plan_config and the chunk count in *plan_splits (either
+ * pointer may be NULL) and returns the workspace bytes it needs (0 for one
+ * chunk or an empty product), or a negative status.  Host only.
+ */
+int64_t sgemm_splitk_plan(int config, int64_t M, int64_t N, int64_t K, int64_t splits,
+                          int *plan_config, int64_t *plan_splits);
+
+/* 1 if configuration `config` has a split-K variant, 0 if not,
+   SGEMM_STATUS_INVALID_CONFIG if unknown.  Host only. */
+int sgemm_config_has_splitk(int config);
 
 /* Static text for a status code (never NULL). */
 const char *sgemm_status_string(int status);

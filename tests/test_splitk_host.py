@@ -1,0 +1,75 @@
+"""Host-side checks of the split-K entry points (no GPU needed): the plan
+the time model makes, the workspace size it reports, and the argument errors
+sgemm_splitk returns before anything is enqueued."""
+import ctypes
+
+import pytest
+
+import tiled_fp32_gemm_sgemm_amd as sg
+from tiled_fp32_gemm_sgemm_amd import _native
+
+FAKE = 0x1000  # never dereferenced: every call below fails its checks first
+
+
+def _lib():
+    return _native.lib()
+
+
+def _tile(config):
+    bm, bn, bk, thr = (ctypes.c_int() for _ in range(4))
+    buf = ctypes.create_string_buffer(64)
+    assert _lib().sgemm_config_info(config, buf, 64, ctypes.byref(bm), ctypes.byref(bn),
+                                    ctypes.byref(bk), ctypes.byref(thr)) == 0
+    return bm.value, bn.value, bk.value
+
+
+SK = [c for c in range(sg.num_configs()) if sg.config_has_splitk(c)]
+
+
+def test_splitk_variants_exist():
+    assert len(SK) >= 4
+    assert _lib().sgemm_config_has_splitk(sg.num_configs()) == -7
+    assert _lib().sgemm_config_has_splitk(-1) == -7
+
+
+@pytest.mark.parametrize("config", SK)
+def test_plan_workspace_size(config):
+    bm, bn, bk = _tile(config)
+    M, N, K = 300, 200, 1000
+    cfg, splits, nbytes = sg.splitk_plan(M, N, K, 5, config)
+    assert cfg == config
+    slices = -(-K // bk)
+    kchunk = -(-slices // 5) * bk
+    assert splits == -(-K // kchunk)
+    tiles = -(-M // bm) * -(-N // bn)
+    assert nbytes == (tiles * 4 + 255) // 256 * 256 + tiles * splits * bm * bn * 4
+    # One chunk needs no workspace.
+    assert sg.splitk_plan(M, N, K, 1, config)[2] == 0
+
+
+def test_plan_errors():
+    plain = [c for c in range(sg.num_configs()) if not sg.config_has_splitk(c)]
+    with pytest.raises(sg.SgemmError):
+        sg.splitk_plan(10, 10, 10, 2, plain[0])
+    with pytest.raises(sg.SgemmError):
+        sg.splitk_plan(10, 10, 10, 65)
+    with pytest.raises(sg.SgemmError):
+        sg.splitk_plan(-1, 10, 10, 2)
+
+
+def test_call_errors_enqueue_nothing():
+    lib = _lib()
+    cfg = SK[0]
+    M, N, K = 64, 64, 4096
+    need = sg.splitk_plan(M, N, K, 4, cfg)[2]
+    assert need > 0
+    call = lambda **kw: lib.sgemm_splitk(
+        kw.get("config", cfg), M, N, K, FAKE, kw.get("lda", K), FAKE, N, FAKE, N,
+        kw.get("splits", 4), kw.get("ws", FAKE), kw.get("nbytes", need), None)
+    assert call(ws=None) == -9
+    assert call(nbytes=need - 1) == -9
+    assert call(splits=-1) == -1
+    assert call(splits=65) == -1
+    assert call(lda=K - 1) == -2
+    assert call(config=sg.num_configs()) == -7
+    assert "workspace" in sg.status_string(-9)

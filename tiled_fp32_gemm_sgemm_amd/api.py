@@ -115,6 +115,73 @@ def sgemm_strided_batched(A, B, out=None, *, path: str = "mfma", config=None, st
     return out
 
 
+def splitk_plan(M: int, N: int, K: int, splits: int = 0, config=None):
+    """(config, splits, workspace bytes) that sgemm_splitk runs for this shape."""
+    cfg = ctypes.c_int(-1)
+    sp = ctypes.c_int64(0)
+    st = _native.lib().sgemm_splitk_plan(-1 if config is None else int(config), M, N, K,
+                                         int(splits), ctypes.byref(cfg), ctypes.byref(sp))
+    if st < 0:
+        raise _native.SgemmError(int(st), "sgemm_splitk_plan")
+    return cfg.value, sp.value, int(st)
+
+
+def config_has_splitk(config: int) -> bool:
+    st = _native.lib().sgemm_config_has_splitk(int(config))
+    if st < 0:
+        raise _native.SgemmError(st, "sgemm_config_has_splitk")
+    return bool(st)
+
+
+# One zero-filled split-K workspace per device, grown on demand.  Calls that
+# use it are ordered by their stream; calls on several streams at once must
+# each pass a workspace of their own.
+_splitk_workspaces = {}
+
+
+def splitk_workspace(device, nbytes: int):
+    """A zero-filled uint8 device tensor of at least nbytes for sgemm_splitk."""
+    import torch
+    device = torch.device(device)
+    key = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _splitk_workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        _splitk_workspaces[key] = ws
+    return ws
+
+
+def sgemm_splitk(A, B, out=None, *, splits: int = 0, config=None, workspace=None, stream=None):
+    """C = A @ B with the k range split over `splits` workgroups per output
+    tile (0: the time model's choice), joined in the same launch.  workspace:
+    a zero-filled device tensor of at least splitk_plan(...)[2] bytes, or None
+    for this device's shared one."""
+    import torch
+    _operand(A, "A", 2)
+    _operand(B, "B", 2)
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ: %d vs %d" % (K, K2))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    _operand(out, "out", 2)
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must have shape (%d, %d)" % (M, N))
+    cfg = -1 if config is None else int(config)
+    _, _, nbytes = splitk_plan(M, N, K, splits, config)
+    if workspace is None:
+        workspace = splitk_workspace(A.device, nbytes)
+    with torch.cuda.device(A.device):
+        st = _native.lib().sgemm_splitk(cfg, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
+                                        out.data_ptr(), _ld(out), int(splits),
+                                        workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(),
+                                        _stream_handle(stream, A.device))
+    _check(st, "sgemm_splitk")
+    return out
+
+
 def num_configs() -> int:
     return _native.lib().sgemm_num_configs()
 

@@ -70,7 +70,7 @@ struct F4 {
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_, int MI_, int OCC_, int GROUP_M_,
           int STAGES_ = 2, int KSPLIT_ = 1, bool SWIZZLE_ = true, bool TA_ = false,
           bool TB_ = false, bool EX_ = false, bool BIL_ = true, bool CONV_ = false,
-          int SCHED_ = 1>
+          int SCHED_ = 1, bool SK_ = false>
 struct DlTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_;
     static constexpr int WAVES_M = WAVES_M_, WAVES_N = WAVES_N_;
@@ -137,6 +137,9 @@ struct DlTile {
     //              of the slice (a convolution keeps the burst: its copy
     //              offsets are rebuilt per filter tap).
     static constexpr int SCHED = SCHED_;
+    // Split-K (SK): the workgroups of one output tile each reduce a k range
+    // and join through a workspace (see the end of the kernel body).
+    static constexpr bool SK = SK_;
     static constexpr bool ILV = SCHED >= 1;
     static constexpr bool SPREAD_COPIES = SCHED >= 2 && !CONV_;
     static constexpr int BV = !BIL ? 1
@@ -180,6 +183,8 @@ struct DlTile {
     static_assert(SCHED >= 0 && SCHED <= 2, "slice schedule");
     static_assert(SCHED < 2 || LPS <= NKG * KG - HOLD, "one copy per k step fits in a slice");
     static_assert((KSPLIT - 1) * BM * BN <= STAGES * BUF_FLOATS, "k-group exchange fits in LDS");
+    static_assert(!SK || (A_KC && !B_KC && !EX && !CONV), "split-K: the plain product only");
+    static_assert(!SK || WTM * WTN <= 64 * 64, "split-K join holds one wave tile of sums");
 
     static __device__ __forceinline__ int swz(int r) { return SWIZZLE ? (r / RPB) % QPR : 0; }
     // Physical quad of logical quad q in row k of an operand staged [k][mn] is
@@ -282,7 +287,9 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     const int rows_left = p.M - m0;
     const int cols_left = p.N - n0;
     const bool full_mn = rows_left >= T::BM && cols_left >= T::BN;
-    const int nslices = (p.K + T::BK - 1) / T::BK;
+    // The k range this workgroup reduces: all of K, or one split's part.
+    const int Kd = T::SK ? min(p.kchunk, p.K - tc.b * p.kchunk) : p.K;
+    const int nslices = (Kd + T::BK - 1) / T::BK;
 
     const int tid = threadIdx.x;
     const int lane = tid % 64;
@@ -449,7 +456,7 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int k = k0 + 4 * kq + e;
-                        if (k < p.K) {
+                        if (k < Kd) {
                             const int tap = k / cg.C;
                             const int c = k - tap * cg.C;
                             const int fr = tap / cg.S;
@@ -464,11 +471,11 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
             } else if constexpr (T::A_KC) {
                 const int kq = (q % T::A_QPR) ^ T::swz(r);
                 x = ldg4_masked(A + (int64_t)r * p.lda + k0 + 4 * kq,
-                                r < rows_left ? p.K - (k0 + 4 * kq) : 0);
+                                r < rows_left ? Kd - (k0 + 4 * kq) : 0);
             } else {
                 const int mq = (q % T::A_QPR) ^ T::flipA(r);
                 x = ldg4_masked(A + (int64_t)(k0 + r) * p.lda + 4 * mq,
-                                k0 + r < p.K ? rows_left - 4 * mq : 0);
+                                k0 + r < Kd ? rows_left - 4 * mq : 0);
             }
             *(f32x4*)(As + 4 * q) = x;
         }
@@ -481,11 +488,11 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
                 const int kq = (q % T::B_QPR) ^ T::swz(r);
                 const int n = T::bkc_row(r);
                 x = ldg4_masked(B + (int64_t)n * p.ldb + k0 + 4 * kq,
-                                n < cols_left ? p.K - (k0 + 4 * kq) : 0);
+                                n < cols_left ? Kd - (k0 + 4 * kq) : 0);
             } else {
                 const int nq = (q % T::B_QPR) ^ T::flipB(r);
                 x = ldg4_masked(B + (int64_t)(k0 + r) * p.ldb + 4 * nq,
-                                k0 + r < p.K ? cols_left - 4 * nq : 0);
+                                k0 + r < Kd ? cols_left - 4 * nq : 0);
             }
             *(f32x4*)(Bs + 4 * q) = x;
         }
@@ -503,7 +510,7 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
                            b_span64 * 4 < (int64_t)kOutOfRange &&
                            (T::A_KC || rows_left >= T::BM || p.M % 4 == 0) &&
                            (T::B_KC || cols_left >= T::BN || p.N % 4 == 0);
-    const int full_slices = p.K / T::BK;
+    const int full_slices = Kd / T::BK;
 
     make_offsets(T::BK);
     auto load_slice = [&](int s) {
@@ -754,9 +761,10 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
             }
         }
         lds_barrier();
-        if (kgrp > 0) return;
+        // (Split-K: every wave takes part in the join's barriers below.)
+        if (kgrp > 0 && !T::SK) return;
 #pragma unroll 1
-        for (int j = 1; j < T::KSPLIT; ++j) {
+        for (int j = 1; j < T::KSPLIT && kgrp == 0; ++j) {
             const float* const src = smem + ((j - 1) * T::NWMN + wave_mn) * 64 * NACC;
 #pragma unroll
             for (int q = 0; q < NACC / 4; ++q) {
@@ -768,6 +776,64 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
                 }
             }
         }
+    }
+
+    // Split-K join.  Each workgroup writes its partial tile to the workspace
+    // and counts itself in on the tile's counter; the workgroup that arrives
+    // last adds every split's partial in split order 0, 1, ... (so the sum
+    // does not depend on which split finished last), resets the counter for
+    // the next call and stores the tile.  No workgroup waits for another.
+    // The partials are written and read with device-scope atomic stores and
+    // loads, which the L2 of each XCD keeps coherent across XCDs, and the
+    // writes have completed (vmcnt 0) before the counter is incremented.  A
+    // device-scope fence would do the same by writing back and invalidating
+    // the whole L2 of the XCD, which throws away the operand tiles every
+    // other workgroup on it is reading.  Record layout: value f of lane l at
+    // f * 64 + l, so each store or load instruction covers 256 contiguous
+    // bytes.
+    if constexpr (T::SK) {
+        constexpr int NACC = T::TM * T::TN * Op::ACC;
+        constexpr int TILE = T::BM * T::BN;
+        // The last-arrival flag goes in LDS word 0: every wave's reads of
+        // the slices and of the k-group exchange end before the barrier below.
+        int* const sk_last = (int*)smem;
+        const bool holds = T::KSPLIT == 1 || kgrp == 0;  // waves with the tile's sums
+        const int tile = tc.tm * p.tiles_n + tc.tn;
+        float* const slot0 = p.ws + (int64_t)tile * p.splits * TILE + wave_mn * 64 * NACC + lane;
+        if (holds) {
+            float* const dst = slot0 + (int64_t)tc.b * TILE;
+#pragma unroll
+            for (int f = 0; f < NACC; ++f)
+                __hip_atomic_store(dst + f * 64,
+                                   acc[f / (T::TN * Op::ACC)][(f / Op::ACC) % T::TN][f % Op::ACC],
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t before = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+            const int last = before == (uint32_t)p.splits - 1;
+            if (last)
+                __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            *sk_last = last;
+        }
+        __syncthreads();
+        if (!*sk_last || !holds) return;
+        float sum[NACC];
+#pragma unroll
+        for (int f = 0; f < NACC; ++f) sum[f] = 0.0f;
+#pragma unroll 1
+        for (int sp = 0; sp < p.splits; ++sp) {
+            const float* const src = slot0 + (int64_t)sp * TILE;
+#pragma unroll
+            for (int f = 0; f < NACC; ++f)
+                sum[f] += __hip_atomic_load(src + f * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int f = 0; f < NACC; ++f)
+            acc[f / (T::TN * Op::ACC)][(f / Op::ACC) % T::TN][f % Op::ACC] = sum[f];
     }
 
     // Epilogue: accumulator r of lane (li, lg) in MFMA tile (mi, ni) is

@@ -128,6 +128,8 @@ struct ConfigEntry {
     const void* general[4];
     // Implicit-GEMM 2-D convolution; NULL where not built.
     const void* conv;
+    // Split-K variant of the plain product; NULL where not built.
+    const void* splitk;
 };
 
 // The same tile with stored-operand layouts and the alpha/beta epilogue.
@@ -140,6 +142,21 @@ using DlGeneral = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::
 template <class T>
 using DlConv = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::OCC, T::GROUP_M,
                       T::STAGES, T::KSPLIT, T::SWIZZLE, false, true, false, T::BIL, true, T::SCHED>;
+
+// The same tile as split-K workgroups that join through a workspace (built
+// where one wave tile of sums fits the join: wave tiles up to 64 x 64).
+template <class T>
+using DlSplitK = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::OCC, T::GROUP_M,
+                        T::STAGES, T::KSPLIT, T::SWIZZLE, false, false, false, T::BIL, false,
+                        T::SCHED, true>;
+
+template <class T>
+const void* splitk_kernel() {
+    if constexpr (T::WTM * T::WTN <= 64 * 64)
+        return (const void*)&sgemm_mfma_dl_kernel<DlSplitK<T>>;
+    else
+        return nullptr;
+}
 
 #define SGEMM_CFG(T, name, per_cu, a1, b1, a2, b2) \
     { name, T::BM, T::BN, T::BK, T::NT, T::WG_PER_CU, (const void*)&sgemm_mfma_kernel<T>, per_cu, \
@@ -154,7 +171,7 @@ using DlConv = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::OCC
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, false>>,                        \
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, false, true>>,                        \
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, true>> },                        \
-      (const void*)&sgemm_mfma_dl_kernel<DlConv<T>> }
+      (const void*)&sgemm_mfma_dl_kernel<DlConv<T>>, splitk_kernel<T>() }
 // General form, no convolution variant.
 #define SGEMM_DLG_CFG(T, name, per_cu, a1, b1, a2, b2)                                       \
     { name, T::BM, T::BN, T::BK, T::NT, T::WG_PER_CU, (const void*)&sgemm_mfma_dl_kernel<T>, \
@@ -163,7 +180,7 @@ using DlConv = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::OCC
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, false>>,                        \
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, false, true>>,                        \
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, true>> },                        \
-      nullptr }
+      nullptr, splitk_kernel<T>() }
 
 const ConfigEntry kConfigs[] = {
     SGEMM_CFG(Cfg256x128, "mfma32_256x128x16_w2x2", 1, 3.6505e-04, 4.2029e-06, 4.1134e-04, 8.0806e-06),
@@ -397,6 +414,135 @@ int run_mfma(int config, int64_t M, int64_t N, int64_t K, const float* A, int64_
                        strideB, C, ldc, strideC, batch, stream);
 }
 
+// ------------------------------------------------------------------ split-K
+// Split-K: the k range is cut into `splits` chunks of whole BK slices, each
+// reduced by its own workgroup per output tile; the partial tiles join in the
+// kernel (the last workgroup of a tile to arrive adds them in split order).
+// Workspace: a uint32 arrival counter per output tile (padded to 256 bytes),
+// then splits * BM * BN floats per tile.
+constexpr int64_t kMaxSplits = 64;
+// Join cost in the plan: the partial tiles are written once and read back
+// once (device-coherent accesses that stay mostly in the MALL), at
+// kJoinBytesPerUs, plus a fixed kJoinFixedUs for the counter round trip and
+// the last workgroup's serial sum.  Set so that on a sweep of thin shapes
+// (256 and 512 x 4096 x 4096, 512 x 512 x 8192, 128 x 4096 x 8192, 768^3 to
+// 2048^3) the plan lands on the measured fastest choice or within 5 % of it.
+constexpr double kJoinBytesPerUs = 4.0e6;
+constexpr double kJoinFixedUs = 2.0;
+
+struct SplitPlan {
+    int config;        // tile configuration
+    int64_t splits;    // effective number of k chunks (1: the plain kernel)
+    int64_t kchunk;    // k values per chunk, a multiple of BK
+    int64_t ws_bytes;  // workspace needed (0 when splits == 1)
+};
+
+int64_t splitk_counter_bytes(int64_t tiles) { return (tiles * 4 + 255) / 256 * 256; }
+
+SplitPlan make_split_plan(const ConfigEntry& c, int config, int64_t M, int64_t N, int64_t K,
+                          int64_t want) {
+    SplitPlan sp;
+    sp.config = config;
+    const int64_t slices = ceil_div(K, c.bk);
+    int64_t s = want < 1 ? 1 : want;
+    if (s > slices) s = slices;
+    if (s < 1) s = 1;
+    sp.kchunk = (slices > 0 ? ceil_div(slices, s) : 1) * c.bk;
+    sp.splits = K > 0 ? ceil_div(K, sp.kchunk) : 1;
+    const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
+    sp.ws_bytes = sp.splits > 1
+                      ? splitk_counter_bytes(tiles) + tiles * sp.splits * c.bm * c.bn * 4
+                      : 0;
+    return sp;
+}
+
+double predict_split_us(const ConfigEntry& c, const SplitPlan& sp, int64_t M, int64_t N) {
+    const double t = predict_us(c, M, N, sp.kchunk, sp.splits);
+    if (sp.splits == 1) return t;
+    const double tiles = (double)(ceil_div(M, c.bm) * ceil_div(N, c.bn));
+    const double bytes = tiles * (double)c.bm * c.bn * 4.0 * 2.0 * (double)sp.splits;
+    return t + kJoinFixedUs + bytes / kJoinBytesPerUs;
+}
+
+// config < 0: every tile with a split-K variant (and the automatic plain
+// choice); splits == 0: every split count up to kMaxSplits.  The smallest
+// predicted time wins.
+int plan_splitk(int config, int64_t M, int64_t N, int64_t K, int64_t splits, SplitPlan* out) {
+    if (config >= kNumConfigs) return SGEMM_STATUS_INVALID_CONFIG;
+    if (config >= 0 && kConfigs[config].splitk == nullptr) return SGEMM_STATUS_INVALID_CONFIG;
+    if (splits < 0 || splits > kMaxSplits) return SGEMM_STATUS_INVALID_SIZE;
+    bool have = false;
+    double best_us = 0.0;
+    auto consider = [&](int idx, int64_t want) {
+        const ConfigEntry& c = kConfigs[idx];
+        const SplitPlan sp = make_split_plan(c, idx, M, N, K, want);
+        const double t = predict_split_us(c, sp, M, N);
+        if (!have || t < best_us * (1.0 - 1e-9)) {
+            have = true;
+            best_us = t;
+            *out = sp;
+        }
+    };
+    if (config < 0 && splits == 0 && M > 0 && N > 0 && K > 0) consider(choose_config(M, N, K, 1), 1);
+    for (int idx = 0; idx < kNumConfigs; ++idx) {
+        if (config >= 0 ? idx != config : (kConfigs[idx].splitk == nullptr ||
+                                           kConfigs[idx].per_cu == 0))
+            continue;
+        if (splits > 0) {
+            consider(idx, splits);
+        } else {
+            for (int64_t s = 1; s <= kMaxSplits; ++s) consider(idx, s);
+        }
+    }
+    return have ? SGEMM_STATUS_SUCCESS : SGEMM_STATUS_INVALID_CONFIG;
+}
+
+int run_splitk(int config, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+               const float* B, int64_t ldb, float* C, int64_t ldc, int64_t splits,
+               void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    int st = validate(M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, 1);
+    if (st != SGEMM_STATUS_SUCCESS) return st;
+    SplitPlan sp;
+    st = plan_splitk(config, M, N, K, splits, &sp);
+    if (st != SGEMM_STATUS_SUCCESS) return st;
+    if (M == 0 || N == 0) return SGEMM_STATUS_SUCCESS;
+    const ConfigEntry& c = kConfigs[sp.config];
+    if (K == 0 || sp.splits == 1)
+        return launch_gemm(c.kernel, c.bm, c.bn, c.threads, M, N, K, A, lda, 0, B, ldb, 0, C,
+                           ldc, 0, 1, stream);
+    if (workspace == nullptr || workspace_bytes < sp.ws_bytes) return SGEMM_STATUS_INVALID_WORKSPACE;
+    const int64_t tiles_m = ceil_div(M, c.bm), tiles_n = ceil_div(N, c.bn);
+    const int64_t blocks = tiles_m * tiles_n * sp.splits;
+    if (blocks > kMaxWorkItems / c.threads) return SGEMM_STATUS_SIZE_OVERFLOW;
+    GemmArgs p = {};
+    p.A = A;
+    p.B = B;
+    p.C = C;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.strideA = sp.kchunk;        // split b starts at column b * kchunk of A
+    p.strideB = sp.kchunk * ldb;  // and at row b * kchunk of B
+    p.strideC = 0;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.tiles_m = (int)tiles_m;
+    p.tiles_n = (int)tiles_n;
+    p.batch_base = 0;
+    p.batch_count = (int)sp.splits;
+    p.alpha = 1.0f;
+    p.beta = 0.0f;
+    p.counters = (uint32_t*)workspace;
+    p.ws = (float*)((char*)workspace + splitk_counter_bytes(tiles_m * tiles_n));
+    p.kchunk = (int)sp.kchunk;
+    p.splits = (int)sp.splits;
+    void* args[] = {&p};
+    hipError_t e = hipLaunchKernel(c.splitk, dim3((unsigned)blocks), dim3(c.threads), args, 0,
+                                   stream);
+    return e == hipSuccess ? SGEMM_STATUS_SUCCESS : SGEMM_STATUS_LAUNCH_FAILED;
+}
+
 // C = beta * C over the M x N windows (+0 when beta == 0, C not read).
 int launch_scale(int64_t M, int64_t N, float* C, int64_t ldc, int64_t strideC, int64_t batch,
                  float beta, hipStream_t stream) {
@@ -554,6 +700,30 @@ int sgemm_with_config(int config, int64_t M, int64_t N, int64_t K, const float* 
     if (config < 0 || config >= kNumConfigs) return SGEMM_STATUS_INVALID_CONFIG;
     return run_mfma(config, M, N, K, A, lda, strideA, B, ldb, strideB, C, ldc, strideC, batch,
                     stream);
+}
+
+int sgemm_splitk(int config, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                 const float* B, int64_t ldb, float* C, int64_t ldc, int64_t splits,
+                 void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    return run_splitk(config, M, N, K, A, lda, B, ldb, C, ldc, splits, workspace,
+                      workspace_bytes, stream);
+}
+
+int64_t sgemm_splitk_plan(int config, int64_t M, int64_t N, int64_t K, int64_t splits,
+                          int* plan_config, int64_t* plan_splits) {
+    if (M < 0 || N < 0 || K < 0) return SGEMM_STATUS_INVALID_SIZE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return SGEMM_STATUS_SIZE_OVERFLOW;
+    SplitPlan sp;
+    const int st = plan_splitk(config, M, N, K, splits, &sp);
+    if (st != SGEMM_STATUS_SUCCESS) return st;
+    if (plan_config != nullptr) *plan_config = sp.config;
+    if (plan_splits != nullptr) *plan_splits = sp.splits;
+    return (M == 0 || N == 0 || K == 0) ? 0 : sp.ws_bytes;
+}
+
+int sgemm_config_has_splitk(int config) {
+    if (config < 0 || config >= kNumConfigs) return SGEMM_STATUS_INVALID_CONFIG;
+    return kConfigs[config].splitk != nullptr ? 1 : 0;
 }
 
 int sgemm_num_configs(void) { return kNumConfigs; }
@@ -749,6 +919,8 @@ const char* sgemm_status_string(int status) {
         case SGEMM_STATUS_LAUNCH_FAILED: return "kernel launch failed";
         case SGEMM_STATUS_INVALID_CONFIG: return "unknown tile configuration";
         case SGEMM_STATUS_INVALID_OP: return "invalid transpose flag (must be 0 or 1)";
+        case SGEMM_STATUS_INVALID_WORKSPACE:
+            return "split-K workspace is NULL or smaller than sgemm_splitk_plan reports";
         default: return "unknown status";
     }
 }

@@ -57,6 +57,12 @@ struct GemmArgs {
     int batch_count;                    // batch members in this launch
     float alpha, beta;                  // C = alpha op(A) op(B) + beta C (general form only)
     ConvGeom conv;                      // implicit-GEMM convolution only
+    // Split-K kernels only: split b (the batch index) reduces k in
+    // [b * kchunk, min(K, (b + 1) * kchunk)); its partial tile goes to ws at
+    // [tile][split], and counters[tile] counts the splits that have arrived.
+    float* ws;
+    uint32_t* counters;
+    int kchunk, splits;
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));

@@ -58,7 +58,7 @@ def _square(n, dist, scale, seed, about):
                     about=about)
 
 
-# The five workloads, smallest first.  The 4096^3 product is the headline one.
+# The GEMM workloads.  The 4096^3 product is the headline one.
 WORKLOADS = {
     "square1024": _square(1024, "uniform", 1.0, 0,
                           "1024^3 contiguous, uniform[-1,1), seed 0"),
@@ -75,6 +75,10 @@ WORKLOADS = {
                          1.0 / math.sqrt(4096), 1.0 / math.sqrt(4096), 5,
                          about="512x4096x4096 (one of 8 row panels of 4096^3), "
                                "normal(0,1)/sqrt(K), seed 5"),
+    "longk512": Workload("longk512", 512, 512, 8192, 8192, 512, 512, "normal", "normal",
+                         1.0 / math.sqrt(8192), 1.0 / math.sqrt(8192), 6,
+                         about="512x512x8192 (16 tiles of 128^2 for 256 CUs: the split-K "
+                               "case), normal(0,1)/sqrt(K), seed 6"),
     "batched128": Workload("batched128", 128, 128, 128, 128, 128, 128, "uniform", "uniform",
                            seed=4, batch=1024, strideA=128 * 128, strideB=128 * 128,
                            strideC=128 * 128,
