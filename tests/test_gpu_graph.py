@@ -114,6 +114,31 @@ def test_graph_window_conv_attention():
     assert np.isfinite(o.cpu().numpy()).all()
 
 
+def test_graph_splitk():
+    """Split-K in a graph: the workspace counters must be back at zero after
+    every replay (the join resets them; no memset is recorded)."""
+    dev = _dev()
+    gen = torch.Generator(device=dev).manual_seed(13)
+    A = torch.randn(200, 3000, device=dev, generator=gen)
+    B = torch.randn(3000, 150, device=dev, generator=gen)
+    C = torch.empty(200, 150, device=dev)
+    A2 = torch.randn(64, 5000, device=dev, generator=gen)
+    B2 = torch.randn(5000, 96, device=dev, generator=gen)
+    C2 = torch.empty(64, 96, device=dev)
+    n1 = sg.splitk_plan(200, 150, 3000, 6)[2]
+    n2 = sg.splitk_plan(64, 96, 5000, 4)[2]
+    assert n1 > 0 and n2 > 0
+    ws = torch.zeros(max(n1, n2), dtype=torch.uint8, device=dev)
+
+    def capture():
+        sg.sgemm_splitk(A, B, C, splits=6, workspace=ws)
+        sg.sgemm_splitk(A2, B2, C2, splits=4, workspace=ws)
+    _replays_match(capture, [C, C2], _other_work(dev))
+    # Both products have at most 64 output tiles: their counters are in the
+    # first 256 bytes.
+    assert torch.count_nonzero(ws[:256]).item() == 0
+
+
 def test_host_threads_on_their_own_streams():
     """The library keeps no mutable global state: four host threads, each on
     its own stream, calling different entry points at once, give the same
