@@ -143,8 +143,11 @@ template <class T>
 using DlConv = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::OCC, T::GROUP_M,
                       T::STAGES, T::KSPLIT, T::SWIZZLE, false, true, false, T::BIL, true, T::SCHED>;
 
-// The same tile as split-K workgroups that join through a workspace (built
-// where one wave tile of sums fits the join: wave tiles up to 64 x 64).
+// The same tile as split-K workgroups that join through a workspace, built
+// for wave tiles up to 64 x 64 (one wave tile of sums in the join) and BK of
+// 32 or more: the 128 x 128 x 16 tile ran 2-4 times slower than the others
+// as split-K at every shape and chunk count measured, which the time model
+// does not see, so it is not offered.
 template <class T>
 using DlSplitK = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::OCC, T::GROUP_M,
                         T::STAGES, T::KSPLIT, T::SWIZZLE, false, false, false, T::BIL, false,
@@ -152,7 +155,7 @@ using DlSplitK = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::O
 
 template <class T>
 const void* splitk_kernel() {
-    if constexpr (T::WTM * T::WTN <= 64 * 64)
+    if constexpr (T::WTM * T::WTN <= 64 * 64 && T::BK >= 32)
         return (const void*)&sgemm_mfma_dl_kernel<DlSplitK<T>>;
     else
         return nullptr;
