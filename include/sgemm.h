@@ -246,15 +246,21 @@ int sgemm_autotune(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
  * workspace, workspace_bytes: device memory owned by the caller, at least
  *   sgemm_splitk_plan(...) bytes for the same config, sizes and splits
  *   (a count that resolves to one chunk needs none: NULL and 0 are accepted).
- *   The workspace must hold zeros before its first use (e.g. allocated
- *   with hipMemset or torch.zeros); every call that completes leaves its
- *   counters at zero again, so it is zeroed once, not per call.  Calls that may
- *   run at the same time need workspaces of their own; concurrent calls on
- *   one workspace race.
+ *   Layout: its first SGEMM_SPLITK_HEADER_BYTES hold one uint32 arrival
+ *   counter per output tile (tile t's at word t, for every shape), the
+ *   partial tiles follow.  The header must hold zeros before the first use
+ *   (e.g. allocated with hipMemset or torch.zeros); every call that completes
+ *   leaves it zero again, so one workspace is zeroed once and then serves
+ *   calls of any shape and chunk count in turn.  Calls that may run at the
+ *   same time need workspaces of their own; concurrent calls on one
+ *   workspace race.  A product with more than SGEMM_SPLITK_MAX_TILES output
+ *   tiles is not split (the plan reports one chunk).
  * Errors as for sgemm, plus SGEMM_STATUS_INVALID_CONFIG (no split-K variant),
  * SGEMM_STATUS_INVALID_SIZE (splits outside 0 ... 64) and
  * SGEMM_STATUS_INVALID_WORKSPACE; on an error nothing is enqueued.
  */
+#define SGEMM_SPLITK_MAX_TILES 16384
+#define SGEMM_SPLITK_HEADER_BYTES (SGEMM_SPLITK_MAX_TILES * 4)
 int sgemm_splitk(int config, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
                  const float *B, int64_t ldb, float *C, int64_t ldc, int64_t splits,
                  void *workspace, int64_t workspace_bytes, hipStream_t stream);

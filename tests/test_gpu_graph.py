@@ -134,9 +134,7 @@ def test_graph_splitk():
         sg.sgemm_splitk(A, B, C, splits=6, workspace=ws)
         sg.sgemm_splitk(A2, B2, C2, splits=4, workspace=ws)
     _replays_match(capture, [C, C2], _other_work(dev))
-    # Both products have at most 64 output tiles: their counters are in the
-    # first 256 bytes.
-    assert torch.count_nonzero(ws[:256]).item() == 0
+    assert torch.count_nonzero(ws[:sg.SPLITK_HEADER_BYTES]).item() == 0
 
 
 def test_host_threads_on_their_own_streams():

@@ -7,7 +7,8 @@ inputs are held to the parity bound 2e-4 * (|A||B|)_ij and must repeat bit
 for bit from call to call (the join order does not depend on timing).  C's
 row padding and a guard after C hold a sentinel that must come back
 unchanged, A's and B's padding is NaN, and after every call the workspace's
-per-tile counters must be zero again, so the next call can reuse it.
+per-tile counters must be zero again, so the next call can reuse it, whatever
+its shape.
 """
 import ctypes
 
@@ -32,12 +33,6 @@ SK_CONFIGS = [c for c in range(sg.num_configs()) if sg.config_has_splitk(c)]
 def _dev():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     return torch.device("cuda:0")
-
-
-def _counter_bytes(config, M, N):
-    bm, bn, _ = _tile(config)
-    tiles = -(-M // bm) * -(-N // bn)
-    return (tiles * 4 + 255) // 256 * 256
 
 
 def _tile(config):
@@ -74,8 +69,7 @@ def run_splitk(M, N, K, A_cpu, lda, B_cpu, ldb, ldc, config, splits, ws=None, li
     written[idx] = True
     assert np.all(Ch[~written] == SENTINEL), "C written outside its M x N window"
     if plan_splits.value > 1:
-        tiles_bytes = _counter_bytes(plan_cfg.value, M, N)
-        assert torch.count_nonzero(ws[:tiles_bytes]).item() == 0, "counters not reset"
+        assert torch.count_nonzero(ws[:sg.SPLITK_HEADER_BYTES]).item() == 0, "counters not reset"
     return Ch[idx], ws, (plan_cfg.value, plan_splits.value)
 
 
@@ -179,3 +173,85 @@ def test_racecheck_splitk_bitwise(config):
     got, _, _ = run_splitk(M, N, K, A, lda, B, ldb, ldc, config, 5, lib=rc)
     ref, _, _ = oracle.sgemm_f64(M, N, K, A.numpy(), lda, B.numpy(), ldb)
     parity.assert_bitwise(got, ref, "racecheck splitk cfg%d" % config)
+
+
+# Output tiles and chunks of the time model's plans: 16 tiles x 16 chunks,
+# 128 tiles x 2 chunks (counters past the first 64 tiles), 16 tiles x 8.
+SEQUENCE = [(128, 1024, 16384), (512, 1024, 2048), (128, 1024, 16384), (512, 512, 8192)]
+
+
+def test_splitk_workspace_serves_any_shape():
+    """One workspace through calls whose tile counts and chunk counts differ:
+    the counters sit at fixed places, so a call with more tiles than the one
+    before never reads the earlier call's partial sums as counters."""
+    plans = [sg.splitk_plan(M, N, K) for M, N, K in SEQUENCE]
+    assert all(p[1] > 1 for p in plans), plans
+    tiles = []
+    for (M, N, K), (cfg, _, _) in zip(SEQUENCE, plans):
+        bm, bn, _ = _tile(cfg)
+        tiles.append(-(-M // bm) * -(-N // bn))
+    assert min(tiles) <= 64 < max(tiles), tiles
+    ws = torch.zeros(max(p[2] for p in plans), dtype=torch.uint8, device=_dev())
+    for i, (M, N, K) in enumerate(SEQUENCE):
+        A, B = operands(M, N, K, K, N, seed=400 + i, dist_a="int4")
+        got, _, plan = run_splitk(M, N, K, A, K, B, N, N, -1, 0, ws=ws)
+        assert plan[1] == plans[i][1]
+        ref, _, _ = oracle.sgemm_f64(M, N, K, A.numpy(), K, B.numpy(), N)
+        parity.assert_bitwise(got, ref, "splitk sequence %s" % ((M, N, K),))
+
+
+def test_splitk_default_workspace():
+    """The binding's own workspace (kept per device and stream, grown on
+    demand) through the same sequence, bit-exact on integer inputs."""
+    dev = _dev()
+    for i, (M, N, K) in enumerate(SEQUENCE):
+        A, B = operands(M, N, K, K, N, seed=500 + i, dist_a="int4")
+        C = sg.sgemm_splitk(A.view(M, K).to(dev), B.view(K, N).to(dev))
+        got = C.cpu().numpy()
+        ref, _, _ = oracle.sgemm_f64(M, N, K, A.numpy(), K, B.numpy(), N)
+        parity.assert_bitwise(got, ref, "default workspace %s" % ((M, N, K),))
+    s = torch.cuda.current_stream(dev)
+    ws = sg.splitk_workspace(dev, 0, s)
+    assert torch.count_nonzero(ws[:sg.SPLITK_HEADER_BYTES]).item() == 0
+
+
+def test_splitk_two_streams_default_workspaces():
+    """Two streams calling the binding at once with no workspace of their
+    own: each stream gets its own, and both sequences equal the serial
+    results bit for bit."""
+    dev = _dev()
+    jobs = []
+    for t in range(2):
+        for i, (M, N, K) in enumerate(SEQUENCE):
+            A, B = operands(M, N, K, K, N, seed=600 + 10 * t + i, dist_a="int4")
+            jobs.append((t, A.view(M, K).to(dev), B.view(K, N).to(dev)))
+    ref = [sg.sgemm_splitk(A, B) for _, A, B in jobs]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=dev) for _ in range(2)]
+    outs = [None] * len(jobs)
+    for rep in range(3):
+        for j, (t, A, B) in enumerate(jobs):
+            with torch.cuda.stream(streams[t]):
+                outs[j] = sg.sgemm_splitk(A, B)
+    torch.cuda.synchronize()
+    for j, (t, _, _) in enumerate(jobs):
+        assert torch.equal(outs[j], ref[j]), "stream %d job %d" % (t, j)
+    keys = {(dev.index, int(s.cuda_stream)) for s in streams}
+    assert len(keys) == 2
+
+
+@pytest.mark.parametrize("name", ["square1024", "square1024_int"])
+def test_square1024_splitk_full(name):
+    """The 1024^3 workload through sgemm_splitk at the time model's plan and
+    at 2, 4 and 8 chunks, every entry against the oracle (bit for bit on the
+    integer variant)."""
+    w = WORKLOADS[name]
+    A, B = workload_operands(w)
+    ref, mag, _ = oracle.sgemm_f64(w.M, w.N, w.K, A.numpy(), w.lda, B.numpy(), w.ldb)
+    for splits in (0, 2, 4, 8):
+        got, _, plan = run_splitk(w.M, w.N, w.K, A, w.lda, B, w.ldb, w.ldc, -1, splits)
+        what = "%s splits=%d plan=%s" % (name, splits, plan)
+        if name.endswith("_int"):
+            parity.assert_bitwise(got, ref, what)
+        else:
+            parity.assert_within_tolerance(got, ref, mag, what)

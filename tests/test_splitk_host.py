@@ -42,9 +42,29 @@ def test_plan_workspace_size(config):
     kchunk = -(-slices // 5) * bk
     assert splits == -(-K // kchunk)
     tiles = -(-M // bm) * -(-N // bn)
-    assert nbytes == (tiles * 4 + 255) // 256 * 256 + tiles * splits * bm * bn * 4
+    # A fixed header of per-tile counters, whatever the shape, then the partials.
+    assert nbytes == sg.SPLITK_HEADER_BYTES + tiles * splits * bm * bn * 4
     # One chunk needs no workspace.
     assert sg.splitk_plan(M, N, K, 1, config)[2] == 0
+
+
+def test_header_constants_match_the_c_header():
+    import os
+    import re
+    text = open(os.path.join(os.path.dirname(__file__), "..", "include", "sgemm.h")).read()
+    m = re.search(r"#define SGEMM_SPLITK_MAX_TILES (\d+)", text)
+    assert m and int(m.group(1)) == sg.SPLITK_MAX_TILES
+    assert sg.SPLITK_HEADER_BYTES == 4 * sg.SPLITK_MAX_TILES
+
+
+@pytest.mark.parametrize("config", SK)
+def test_more_tiles_than_the_header_are_not_split(config):
+    bm, bn, _ = _tile(config)
+    per_side = int(sg.SPLITK_MAX_TILES ** 0.5)
+    M, N = per_side * bm, per_side * bn          # exactly the header's tile count
+    assert sg.splitk_plan(M, N, 4096, 4, config)[1:] == (4, sg.SPLITK_HEADER_BYTES +
+                                                         sg.SPLITK_MAX_TILES * 4 * bm * bn * 4)
+    assert sg.splitk_plan(M + 1, N, 4096, 4, config)[1:] == (1, 0)
 
 
 def test_plan_errors():

@@ -7,7 +7,7 @@ The product runs in libsgemm.so (hand-written HIP kernels behind the C ABI
 in include/sgemm.h); this package only passes tensors' device addresses,
 leading dimensions and the current stream to it.
 """
-from .api import (attention, attention_raw, autotune, autotune_raw, config_has_general_form, config_info,
+from .api import (SPLITK_HEADER_BYTES, SPLITK_MAX_TILES, attention, attention_raw, autotune, autotune_raw, config_has_general_form, config_info,
                   conv2d_config_available, conv2d_nhwc, conv2d_nhwc_raw, conv2d_output_size,
                   conv2d_select_config,
                   config_selectable, num_configs, predict_us, select_config,
@@ -24,5 +24,5 @@ __all__ = ["sgemm", "sgemm_strided_batched", "sgemm_raw", "sgemm_strided_batched
            "conv2d_nhwc_raw", "conv2d_output_size", "conv2d_config_available",
            "conv2d_select_config", "workgroups_per_cu", "attention", "attention_raw",
            "sgemm_splitk", "splitk_plan", "splitk_workspace", "config_has_splitk",
-           "SgemmError",
+           "SPLITK_HEADER_BYTES", "SPLITK_MAX_TILES", "SgemmError",
            "status_string"]

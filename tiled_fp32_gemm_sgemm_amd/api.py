@@ -14,6 +14,11 @@ from . import _native
 
 PATHS = ("mfma", "valu")
 
+# The split-K workspace header (include/sgemm.h): one uint32 arrival counter
+# per output tile, at the same place for every shape.
+SPLITK_MAX_TILES = 16384
+SPLITK_HEADER_BYTES = SPLITK_MAX_TILES * 4
+
 
 def _stream_handle(stream, device) -> int:
     import torch
@@ -133,20 +138,39 @@ def config_has_splitk(config: int) -> bool:
     return bool(st)
 
 
-# One zero-filled split-K workspace per device, grown on demand.  Calls that
-# use it are ordered by their stream; calls on several streams at once must
-# each pass a workspace of their own.
+# One zero-filled split-K workspace per (device, stream), grown on demand.
+# It is allocated and zeroed on the stream whose launches use it, so the
+# zeros land before the first join reads them, and a buffer dropped when it
+# grows goes back to the allocator on that stream, behind every launch that
+# used it.  Calls on different streams never share one.
 _splitk_workspaces = {}
 
 
-def splitk_workspace(device, nbytes: int):
-    """A zero-filled uint8 device tensor of at least nbytes for sgemm_splitk."""
+def _torch_stream(stream, device):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
+def splitk_workspace(device, nbytes: int, stream=None):
+    """A zero-filled uint8 device tensor of at least nbytes for sgemm_splitk
+    calls on `stream` (None: the device's current stream), made on that
+    stream.  Its header of per-tile counters is back at zero after every
+    completed call, so it serves calls of any shape on the same stream."""
     import torch
     device = torch.device(device)
-    key = device.index if device.index is not None else torch.cuda.current_device()
+    if device.index is None:
+        device = torch.device("cuda", torch.cuda.current_device())
+    s = _torch_stream(stream, device)
+    key = (device.index, int(s.cuda_stream))
     ws = _splitk_workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+        with torch.cuda.device(device), torch.cuda.stream(s):
+            _splitk_workspaces.pop(key, None)
+            ws = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
         _splitk_workspaces[key] = ws
     return ws
 
@@ -154,8 +178,8 @@ def splitk_workspace(device, nbytes: int):
 def sgemm_splitk(A, B, out=None, *, splits: int = 0, config=None, workspace=None, stream=None):
     """C = A @ B with the k range split over `splits` workgroups per output
     tile (0: the time model's choice), joined in the same launch.  workspace:
-    a zero-filled device tensor of at least splitk_plan(...)[2] bytes, or None
-    for this device's shared one."""
+    a device tensor of at least splitk_plan(...)[2] bytes whose header starts
+    at zero, or None for the one kept for this device and stream."""
     import torch
     _operand(A, "A", 2)
     _operand(B, "B", 2)
@@ -171,7 +195,7 @@ def sgemm_splitk(A, B, out=None, *, splits: int = 0, config=None, workspace=None
     cfg = -1 if config is None else int(config)
     _, _, nbytes = splitk_plan(M, N, K, splits, config)
     if workspace is None:
-        workspace = splitk_workspace(A.device, nbytes)
+        workspace = splitk_workspace(A.device, nbytes, stream)
     with torch.cuda.device(A.device):
         st = _native.lib().sgemm_splitk(cfg, M, N, K, A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
                                         out.data_ptr(), _ld(out), int(splits),

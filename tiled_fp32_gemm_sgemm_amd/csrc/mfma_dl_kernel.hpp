@@ -783,12 +783,23 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     // last adds every split's partial in split order 0, 1, ... (so the sum
     // does not depend on which split finished last), resets the counter for
     // the next call and stores the tile.  No workgroup waits for another.
-    // The partials are written and read with device-scope atomic stores and
-    // loads, which the L2 of each XCD keeps coherent across XCDs, and the
-    // writes have completed (vmcnt 0) before the counter is incremented.  A
-    // device-scope fence would do the same by writing back and invalidating
-    // the whole L2 of the XCD, which throws away the operand tiles every
-    // other workgroup on it is reading.  Record layout: value f of lane l at
+    // Ordering rests on how gfx950 (a member of the GFX942 family in LLVM's
+    // AMDGPU memory model) performs relaxed device-scope atomics, not on
+    // C++ release/acquire: the model maps relaxed agent-scope atomic stores
+    // and loads of global memory to global_store / global_load with the sc1
+    // bit (performed coherently across the XCDs' L2 caches) and atomic RMWs
+    // to global_atomic at the device's coherence point.  Every partial is
+    // such a store; s_waitcnt vmcnt(0) holds each wave until its stores are
+    // acknowledged, the barrier holds lane 0 until every wave has done so,
+    // and only then does lane 0 increment the counter.  The last arriver
+    // sees every other increment, so every partial was complete before its
+    // own increment returned, and its sc1 loads issue after that return.
+    // A device-scope release on the increment and an acquire fence after it
+    // would state the same order in the language's model, but on gfx950
+    // they write back and invalidate the XCD's whole L2 per workgroup (the
+    // operand tiles of every other workgroup on it included): measured at
+    // 1024^3 with 4 chunks, 24.6 -> 53.7 us per product; at 512x4096x4096
+    // with 8 chunks, 154 -> 172 us.  Record layout: value f of lane l at
     // f * 64 + l, so each store or load instruction covers 256 contiguous
     // bytes.
     if constexpr (T::SK) {

@@ -421,9 +421,14 @@ int run_mfma(int config, int64_t M, int64_t N, int64_t K, const float* A, int64_
 // Split-K: the k range is cut into `splits` chunks of whole BK slices, each
 // reduced by its own workgroup per output tile; the partial tiles join in the
 // kernel (the last workgroup of a tile to arrive adds them in split order).
-// Workspace: a uint32 arrival counter per output tile (padded to 256 bytes),
-// then splits * BM * BN floats per tile.
+// Workspace: a header of kSplitMaxTiles uint32 arrival counters, counter t
+// for output tile t whatever the shape, then splits * BM * BN floats per
+// tile.  The header's place and size do not depend on the call, so the zeros
+// that every completed call leaves there serve the next call of any shape;
+// products with more output tiles than the header holds are not split.
 constexpr int64_t kMaxSplits = 64;
+constexpr int64_t kSplitMaxTiles = SGEMM_SPLITK_MAX_TILES;
+constexpr int64_t kSplitHeaderBytes = kSplitMaxTiles * 4;
 // Join cost in the plan: the partial tiles are written once and read back
 // once (device-coherent accesses that stay mostly in the MALL), at
 // kJoinBytesPerUs, plus a fixed kJoinFixedUs for the counter round trip and
@@ -440,22 +445,18 @@ struct SplitPlan {
     int64_t ws_bytes;  // workspace needed (0 when splits == 1)
 };
 
-int64_t splitk_counter_bytes(int64_t tiles) { return (tiles * 4 + 255) / 256 * 256; }
-
 SplitPlan make_split_plan(const ConfigEntry& c, int config, int64_t M, int64_t N, int64_t K,
                           int64_t want) {
     SplitPlan sp;
     sp.config = config;
     const int64_t slices = ceil_div(K, c.bk);
+    const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
     int64_t s = want < 1 ? 1 : want;
     if (s > slices) s = slices;
-    if (s < 1) s = 1;
+    if (tiles > kSplitMaxTiles || s < 1) s = 1;
     sp.kchunk = (slices > 0 ? ceil_div(slices, s) : 1) * c.bk;
     sp.splits = K > 0 ? ceil_div(K, sp.kchunk) : 1;
-    const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
-    sp.ws_bytes = sp.splits > 1
-                      ? splitk_counter_bytes(tiles) + tiles * sp.splits * c.bm * c.bn * 4
-                      : 0;
+    sp.ws_bytes = sp.splits > 1 ? kSplitHeaderBytes + tiles * sp.splits * c.bm * c.bn * 4 : 0;
     return sp;
 }
 
@@ -537,7 +538,7 @@ int run_splitk(int config, int64_t M, int64_t N, int64_t K, const float* A, int6
     p.alpha = 1.0f;
     p.beta = 0.0f;
     p.counters = (uint32_t*)workspace;
-    p.ws = (float*)((char*)workspace + splitk_counter_bytes(tiles_m * tiles_n));
+    p.ws = (float*)((char*)workspace + kSplitHeaderBytes);
     p.kchunk = (int)sp.kchunk;
     p.splits = (int)sp.splits;
     void* args[] = {&p};

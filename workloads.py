@@ -50,7 +50,20 @@ class Workload:
         if self.batch != 1:
             s += " batch=%d strides=%d/%d/%d" % (self.batch, self.strideA, self.strideB,
                                                  self.strideC)
-        return s + " A~%s B~%s seed=%d" % (self.dist_a, self.dist_b, self.seed)
+        return s + " A~%s B~%s seed=%d" % (_dist_text(self.dist_a, self.scale_a, self.K),
+                                            _dist_text(self.dist_b, self.scale_b, self.K),
+                                            self.seed)
+
+
+def _dist_text(dist: str, scale: float, K: int) -> str:
+    """The value distribution as drawn, scale included: normal(0, std),
+    uniform[-a, a), or the integers -4..4."""
+    if dist == "int4":
+        return "int{-4..4}"
+    sq = " (1/sqrt(K))" if K > 0 and abs(scale * math.sqrt(K) - 1.0) < 1e-12 and scale != 1.0 else ""
+    if dist == "normal":
+        return "normal(0,%g)%s" % (scale, sq)
+    return "uniform[-%g,%g)%s" % (scale, scale, sq)
 
 
 def _square(n, dist, scale, seed, about):
