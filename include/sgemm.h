@@ -66,7 +66,10 @@ typedef enum sgemm_status {
     SGEMM_STATUS_INVALID_OP = -8,
     /* Split-K: the workspace is NULL or smaller than sgemm_splitk_plan
        reports for the same arguments. */
-    SGEMM_STATUS_INVALID_WORKSPACE = -9
+    SGEMM_STATUS_INVALID_WORKSPACE = -9,
+    /* sgemm_splitk_noalloc: the requested tile and chunk count need more
+       workspace than SGEMM_SPLITK_SCRATCH_BYTES. */
+    SGEMM_STATUS_SCRATCH_TOO_SMALL = -10
 } sgemm_status_t;
 
 /*
@@ -264,6 +267,35 @@ int sgemm_autotune(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
 int sgemm_splitk(int config, int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
                  const float *B, int64_t ldb, float *C, int64_t ldc, int64_t splits,
                  void *workspace, int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * sgemm_splitk for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same product, kernels and chunk-order join, with the workspace taken
+ * from a buffer the library holds, SGEMM_SPLITK_SCRATCH_BYTES (64 MiB) per
+ * GPU, kept from the first call on that GPU until the process ends.  The
+ * caller passes only inputs, output and stream; the call allocates and frees
+ * nothing.  Its first call on a GPU looks up that GPU's buffer and enqueues
+ * one small kernel that zeroes the counter header (again on later calls
+ * until one such launch was made outside graph capture); every completed
+ * call leaves the header zero.
+ *
+ * config, splits: as for sgemm_splitk.  With config = -1 and splits = 0 the
+ * time model chooses among the plans whose workspace fits the buffer (the
+ * plain kernel always does); an explicit tile or chunk count whose plan
+ * needs more returns SGEMM_STATUS_SCRATCH_TOO_SMALL.  Results are bit for
+ * bit those of sgemm_splitk with the same plan.
+ * Every call on one GPU shares that GPU's buffer: calls that may overlap on
+ * one GPU (other streams, other host threads) race and must use
+ * sgemm_splitk with workspaces of their own.
+ * Errors as for sgemm_splitk, plus SGEMM_STATUS_SCRATCH_TOO_SMALL, and
+ * SGEMM_STATUS_LAUNCH_FAILED when HIP cannot name the stream's device or the
+ * buffer's address; on an error nothing is enqueued.
+ */
+#define SGEMM_SPLITK_SCRATCH_BYTES (64 * 1024 * 1024)
+int sgemm_splitk_noalloc(int config, int64_t M, int64_t N, int64_t K, const float *A,
+                         int64_t lda, const float *B, int64_t ldb, float *C, int64_t ldc,
+                         int64_t splits, hipStream_t stream);
 
 /*
  * The plan sgemm_splitk would run for these arguments: stores the tile

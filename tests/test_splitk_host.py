@@ -93,3 +93,26 @@ def test_call_errors_enqueue_nothing():
     assert call(lda=K - 1) == -2
     assert call(config=sg.num_configs()) == -7
     assert "workspace" in sg.status_string(-9)
+
+
+def test_noalloc_argument_errors_enqueue_nothing():
+    """sgemm_splitk_noalloc checks its arguments and its plan against the
+    library's buffer before touching the GPU."""
+    lib = _lib()
+    cfg = SK[0]
+    M, N, K = 64, 64, 4096
+    def call(**kw):
+        n = kw.get("N", N)
+        return lib.sgemm_splitk_noalloc(kw.get("config", cfg), kw.get("M", M), n, kw.get("K", K),
+                                        FAKE, kw.get("lda", K), FAKE, n, FAKE, n,
+                                        kw.get("splits", 4), None)
+    assert call(splits=-1) == -1
+    assert call(splits=65) == -1
+    assert call(lda=K - 1) == -2
+    assert call(config=sg.num_configs()) == -7
+    assert call(M=-1) == -1
+    # 4096 x 4096 tiles of a 64 x 64 tile at 8 chunks: far more than 64 MiB.
+    big = dict(M=4096, N=4096, K=8192, lda=8192, splits=8)
+    assert sg.splitk_plan(4096, 4096, 8192, 8, cfg)[2] > 64 * 1024 * 1024
+    assert call(**big) == -10
+    assert "scratch" in sg.status_string(-10)

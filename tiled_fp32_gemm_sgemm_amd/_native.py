@@ -78,6 +78,8 @@ _SIGS = {
         ctypes.c_int),
     "sgemm_splitk": ([ctypes.c_int, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64, _i64, _p,
                       _i64, _p], ctypes.c_int),
+    "sgemm_splitk_noalloc": ([ctypes.c_int, _i64, _i64, _i64, _p, _i64, _p, _i64, _p, _i64,
+                              _i64, _p], ctypes.c_int),
     "sgemm_splitk_plan": ([ctypes.c_int, _i64, _i64, _i64, _i64, ctypes.POINTER(ctypes.c_int),
                            ctypes.POINTER(_i64)], _i64),
     "sgemm_config_has_splitk": ([ctypes.c_int], ctypes.c_int),

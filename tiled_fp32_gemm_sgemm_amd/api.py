@@ -206,6 +206,29 @@ def sgemm_splitk(A, B, out=None, *, splits: int = 0, config=None, workspace=None
     return out
 
 
+def sgemm_splitk_noalloc(A, B, out, *, splits: int = 0, config=None, stream=None):
+    """sgemm_splitk with the workspace taken from the library's own per-GPU
+    buffer: nothing is allocated, so `out` must be given.  Calls that may
+    overlap on one GPU share that buffer and race."""
+    _operand(A, "A", 2)
+    _operand(B, "B", 2)
+    _operand(out, "out", 2)
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ: %d vs %d" % (K, K2))
+    if tuple(out.shape) != (M, N):
+        raise ValueError("out must have shape (%d, %d)" % (M, N))
+    import torch
+    with torch.cuda.device(A.device):
+        st = _native.lib().sgemm_splitk_noalloc(-1 if config is None else int(config), M, N, K,
+                                                A.data_ptr(), _ld(A), B.data_ptr(), _ld(B),
+                                                out.data_ptr(), _ld(out), int(splits),
+                                                _stream_handle(stream, A.device))
+    _check(st, "sgemm_splitk_noalloc")
+    return out
+
+
 def num_configs() -> int:
     return _native.lib().sgemm_num_configs()
 

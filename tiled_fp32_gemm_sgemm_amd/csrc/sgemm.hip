@@ -12,6 +12,7 @@
 #include <string.h>
 
 #include <cmath>
+#include <mutex>
 
 #include "mfma_dl_kernel.hpp"
 #include "mfma_kernel.hpp"
@@ -50,7 +51,23 @@ __global__ void scale_kernel(float* C, int64_t ldc, int64_t strideC, int M, int 
     }
 }
 
+// n words set to zero (n a multiple of the block size).
+__global__ void clear_words_kernel(uint32_t* p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
 }  // namespace sgemm_dev
+
+// The split-K workspace kept by the library for callers that cannot
+// allocate device memory (sgemm_splitk_noalloc): the same layout as a
+// caller's workspace (counter header, then partial tiles),
+// SGEMM_SPLITK_SCRATCH_BYTES long.  Every device that loads this code object
+// holds its own copy until the process ends.  In host code the name stands
+// for a host-side shadow, not a device address, so it is never passed to a
+// kernel or a copy: the address of each device's copy comes from
+// hipGetSymbolAddress (scratch_for_stream).
+static __device__ __align__(256) unsigned char scratch[SGEMM_SPLITK_SCRATCH_BYTES];
 
 namespace {
 
@@ -469,9 +486,10 @@ double predict_split_us(const ConfigEntry& c, const SplitPlan& sp, int64_t M, in
 }
 
 // config < 0: every tile with a split-K variant (and the automatic plain
-// choice); splits == 0: every split count up to kMaxSplits.  The smallest
-// predicted time wins.
-int plan_splitk(int config, int64_t M, int64_t N, int64_t K, int64_t splits, SplitPlan* out) {
+// choice); splits == 0: every split count up to kMaxSplits.  Plans whose
+// workspace exceeds max_ws are left out.  The smallest predicted time wins.
+int plan_splitk(int config, int64_t M, int64_t N, int64_t K, int64_t splits, SplitPlan* out,
+                int64_t max_ws = INT64_MAX) {
     if (config >= kNumConfigs) return SGEMM_STATUS_INVALID_CONFIG;
     if (config >= 0 && kConfigs[config].splitk == nullptr) return SGEMM_STATUS_INVALID_CONFIG;
     if (splits < 0 || splits > kMaxSplits) return SGEMM_STATUS_INVALID_SIZE;
@@ -480,6 +498,7 @@ int plan_splitk(int config, int64_t M, int64_t N, int64_t K, int64_t splits, Spl
     auto consider = [&](int idx, int64_t want) {
         const ConfigEntry& c = kConfigs[idx];
         const SplitPlan sp = make_split_plan(c, idx, M, N, K, want);
+        if (sp.ws_bytes > max_ws) return;
         const double t = predict_split_us(c, sp, M, N);
         if (!have || t < best_us * (1.0 - 1e-9)) {
             have = true;
@@ -498,26 +517,39 @@ int plan_splitk(int config, int64_t M, int64_t N, int64_t K, int64_t splits, Spl
             for (int64_t s = 1; s <= kMaxSplits; ++s) consider(idx, s);
         }
     }
-    return have ? SGEMM_STATUS_SUCCESS : SGEMM_STATUS_INVALID_CONFIG;
+    if (have) return SGEMM_STATUS_SUCCESS;
+    return max_ws < INT64_MAX ? SGEMM_STATUS_SCRATCH_TOO_SMALL : SGEMM_STATUS_INVALID_CONFIG;
 }
 
-int run_splitk(int config, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
-               const float* B, int64_t ldb, float* C, int64_t ldc, int64_t splits,
-               void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+// Arguments checked and the plan made, nothing enqueued yet: *needs_ws is
+// set when the plan joins chunks through a workspace.
+int prepare_splitk(int config, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                   const float* B, int64_t ldb, float* C, int64_t ldc, int64_t splits,
+                   int64_t max_ws, SplitPlan* sp, bool* needs_ws) {
     int st = validate(M, N, K, A, lda, 0, B, ldb, 0, C, ldc, 0, 1);
     if (st != SGEMM_STATUS_SUCCESS) return st;
-    SplitPlan sp;
-    st = plan_splitk(config, M, N, K, splits, &sp);
+    st = plan_splitk(config, M, N, K, splits, sp, max_ws);
     if (st != SGEMM_STATUS_SUCCESS) return st;
+    *needs_ws = M > 0 && N > 0 && K > 0 && sp->splits > 1;
+    if (*needs_ws) {
+        const ConfigEntry& c = kConfigs[sp->config];
+        const int64_t blocks = ceil_div(M, c.bm) * ceil_div(N, c.bn) * sp->splits;
+        if (blocks > kMaxWorkItems / c.threads) return SGEMM_STATUS_SIZE_OVERFLOW;
+    }
+    return SGEMM_STATUS_SUCCESS;
+}
+
+// Enqueues a prepared plan; the workspace is used only when the plan splits.
+int launch_splitk(const SplitPlan& sp, int64_t M, int64_t N, int64_t K, const float* A,
+                  int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
+                  void* workspace, hipStream_t stream) {
     if (M == 0 || N == 0) return SGEMM_STATUS_SUCCESS;
     const ConfigEntry& c = kConfigs[sp.config];
     if (K == 0 || sp.splits == 1)
         return launch_gemm(c.kernel, c.bm, c.bn, c.threads, M, N, K, A, lda, 0, B, ldb, 0, C,
                            ldc, 0, 1, stream);
-    if (workspace == nullptr || workspace_bytes < sp.ws_bytes) return SGEMM_STATUS_INVALID_WORKSPACE;
     const int64_t tiles_m = ceil_div(M, c.bm), tiles_n = ceil_div(N, c.bn);
     const int64_t blocks = tiles_m * tiles_n * sp.splits;
-    if (blocks > kMaxWorkItems / c.threads) return SGEMM_STATUS_SIZE_OVERFLOW;
     GemmArgs p = {};
     p.A = A;
     p.B = B;
@@ -545,6 +577,85 @@ int run_splitk(int config, int64_t M, int64_t N, int64_t K, const float* A, int6
     hipError_t e = hipLaunchKernel(c.splitk, dim3((unsigned)blocks), dim3(c.threads), args, 0,
                                    stream);
     return e == hipSuccess ? SGEMM_STATUS_SUCCESS : SGEMM_STATUS_LAUNCH_FAILED;
+}
+
+int run_splitk(int config, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+               const float* B, int64_t ldb, float* C, int64_t ldc, int64_t splits,
+               void* workspace, int64_t workspace_bytes, hipStream_t stream) {
+    SplitPlan sp;
+    bool needs_ws = false;
+    const int st = prepare_splitk(config, M, N, K, A, lda, B, ldb, C, ldc, splits, INT64_MAX,
+                                  &sp, &needs_ws);
+    if (st != SGEMM_STATUS_SUCCESS) return st;
+    if (needs_ws && (workspace == nullptr || workspace_bytes < sp.ws_bytes))
+        return SGEMM_STATUS_INVALID_WORKSPACE;
+    return launch_splitk(sp, M, N, K, A, lda, B, ldb, C, ldc, workspace, stream);
+}
+
+// ------------------------------------------------- split-K without allocation
+// The device addresses of `scratch` (declared at file scope above), one per
+// GPU, each looked up once with that device current.
+constexpr int kMaxScratchDevices = 64;
+struct ScratchState {
+    void* ptr;     // device address of this device's scratch
+    bool cleared;  // its counter header zeroed by a kernel that has run eagerly
+};
+std::mutex g_scratch_mutex;
+ScratchState g_scratch[kMaxScratchDevices];
+
+// The scratch of the device that `stream` runs on, its counter header
+// zeroed on `stream` until one clearing launch has been made outside graph
+// capture (zeros after loading are then not relied on; every completed call
+// leaves the header zero again).
+int scratch_for_stream(hipStream_t stream, void** out) {
+    int dev = -1;
+    if (stream != nullptr) {
+        if (hipStreamGetDevice(stream, &dev) != hipSuccess) return SGEMM_STATUS_LAUNCH_FAILED;
+    } else if (hipGetDevice(&dev) != hipSuccess) {
+        return SGEMM_STATUS_LAUNCH_FAILED;
+    }
+    if (dev < 0 || dev >= kMaxScratchDevices) return SGEMM_STATUS_LAUNCH_FAILED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    ScratchState& st = g_scratch[dev];
+    if (st.ptr == nullptr) {
+        int cur = -1;
+        if (hipGetDevice(&cur) != hipSuccess) return SGEMM_STATUS_LAUNCH_FAILED;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return SGEMM_STATUS_LAUNCH_FAILED;
+        void* ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return SGEMM_STATUS_LAUNCH_FAILED;
+        if (e != hipSuccess || ptr == nullptr) return SGEMM_STATUS_LAUNCH_FAILED;
+        st.ptr = ptr;
+    }
+    if (!st.cleared) {
+        uint32_t* words = (uint32_t*)st.ptr;
+        int64_t n = kSplitHeaderBytes / 4;
+        void* args[] = {&words, &n};
+        if (hipLaunchKernel((const void*)&clear_words_kernel, dim3((unsigned)(n / 256)), dim3(256),
+                            args, 0, stream) != hipSuccess)
+            return SGEMM_STATUS_LAUNCH_FAILED;
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) == hipSuccess && cs == hipStreamCaptureStatusNone)
+            st.cleared = true;
+    }
+    *out = st.ptr;
+    return SGEMM_STATUS_SUCCESS;
+}
+
+int run_splitk_noalloc(int config, int64_t M, int64_t N, int64_t K, const float* A,
+                       int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
+                       int64_t splits, hipStream_t stream) {
+    SplitPlan sp;
+    bool needs_ws = false;
+    int st = prepare_splitk(config, M, N, K, A, lda, B, ldb, C, ldc, splits,
+                            SGEMM_SPLITK_SCRATCH_BYTES, &sp, &needs_ws);
+    if (st != SGEMM_STATUS_SUCCESS) return st;
+    void* ws = nullptr;
+    if (needs_ws) {
+        st = scratch_for_stream(stream, &ws);
+        if (st != SGEMM_STATUS_SUCCESS) return st;
+    }
+    return launch_splitk(sp, M, N, K, A, lda, B, ldb, C, ldc, ws, stream);
 }
 
 // C = beta * C over the M x N windows (+0 when beta == 0, C not read).
@@ -711,6 +822,12 @@ int sgemm_splitk(int config, int64_t M, int64_t N, int64_t K, const float* A, in
                  void* workspace, int64_t workspace_bytes, hipStream_t stream) {
     return run_splitk(config, M, N, K, A, lda, B, ldb, C, ldc, splits, workspace,
                       workspace_bytes, stream);
+}
+
+int sgemm_splitk_noalloc(int config, int64_t M, int64_t N, int64_t K, const float* A,
+                         int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
+                         int64_t splits, hipStream_t stream) {
+    return run_splitk_noalloc(config, M, N, K, A, lda, B, ldb, C, ldc, splits, stream);
 }
 
 int64_t sgemm_splitk_plan(int config, int64_t M, int64_t N, int64_t K, int64_t splits,
@@ -925,6 +1042,9 @@ const char* sgemm_status_string(int status) {
         case SGEMM_STATUS_INVALID_OP: return "invalid transpose flag (must be 0 or 1)";
         case SGEMM_STATUS_INVALID_WORKSPACE:
             return "split-K workspace is NULL or smaller than sgemm_splitk_plan reports";
+        case SGEMM_STATUS_SCRATCH_TOO_SMALL:
+            return "split-K plan needs more workspace than the library's scratch "
+                   "(SGEMM_SPLITK_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
