@@ -45,6 +45,18 @@ CSRC = os.path.join(ROOT, "tiled_fp32_gemm_sgemm_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sgemm_mfma_square4096_counters.txt")
 COPY_BYTES = 512 * 1024 * 1024   # larger than the 256 MB last-level cache
 GEMM_WORK_S = 0.1                # default warm-up and timed work per GEMM phase (s)
+SETTLE_S = 0.1                   # GEMM launches before the warm-up steps (clock settle)
+
+
+def gemm_metric(w) -> str:
+    """The metric a GEMM line reports: the headline string for the 4096^3
+    product, the workload's own shape otherwise."""
+    if w.name == "square4096":
+        return METRIC
+    shape = "M=%d N=%d K=%d" % (w.M, w.N, w.K)
+    if w.batch != 1:
+        shape = "batch %d x %s" % (w.batch, shape)
+    return "FP32 GEMM TFLOP/s at %s on 1 MI355X; %% of FP32 peak" % shape
 
 
 # Device sources each kernel family is compiled from.  A counter summary is
@@ -84,7 +96,7 @@ def read_traffic(path: str, names=GEMM_SOURCES, tile=None):
             "(tile %s)" % tile):
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals["beyond_l2_bytes_per_launch"].split()[0])
     except (KeyError, ValueError):
         return None
 
@@ -154,11 +166,48 @@ def conv_compulsory_bytes(w) -> int:
     return 4 * (w.N * w.H * w.W * w.C + w.K * w.R * w.S * w.C + w.N * P * Q * w.K)
 
 
+def trace_average_us(path: str):
+    """The kernel's average duration from a committed trace summary: the
+    timed dispatches' average when recorded, else the plain average (first
+    kernel listed), or None."""
+    if not path or not os.path.exists(path):
+        return None
+    plain = None
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("timed_average_us"):
+                return float(line.rsplit(":", 1)[1])
+            if plain is None and line.startswith("calls:") and "average_us:" in line:
+                plain = float(line.split("average_us:")[1].split()[0])
+    return plain
+
+
+MAX_CLOCK_GHZ = 2.4           # MI355X peak engine clock
+SIMDS = 1024                  # 256 CUs x 4 SIMDs
+MFMA_FLOP_PER_SIMD_CYCLE = 64  # 157.3 TFLOP/s / (1024 SIMDs x 2.4 GHz)
+
+
 def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fetch_csv: str,
-                       write_csv: str, sq_csvs, commands, config=None) -> None:
-    """Counter summary: utilisation, instruction counts against the closed
-    forms, LDS bank conflicts and HBM traffic scaled by a copy kernel of known
-    size (FETCH_SIZE / WRITE_SIZE in KiB per dispatch)."""
+                       write_csv: str, sq_csvs, commands, config=None, trace_summary=None,
+                       splits: int = 0) -> None:
+    """Counter summary: instruction counts against the closed forms, LDS bank
+    conflicts, utilisation and the bytes that cross from L2 to memory.
+
+    Utilisation is taken over the kernel's duration without the profiler
+    (the trace summary's timed average), at the 2.4 GHz peak clock: busy
+    cycles / (SIMDs x 2.4 GHz x duration).  That denominator is the most
+    cycles the kernel could have had, so the fraction never exceeds 1 and
+    times peak it gives the rate the trace timed.  GRBM_GUI_ACTIVE over the
+    counter run's own dispatch gives a clock only for dispatches long enough
+    that the profiler's set-up and drain around them do not count: it is left
+    out when it comes above 2.4 GHz.
+    Memory side: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) count requests
+    from the L2 caches to memory, that is misses of each XCD's L2, which the
+    256 MB last-level cache (MALL) in front of HBM may still serve; they are
+    scaled by the same counters on a copy kernel of known size.  The read
+    requests by size (32, 64 and 128 bytes) give the same bytes without a
+    scale, as a check of it."""
     from workloads import WINDOW_WORKLOADS, WORKLOADS
     from tiled_fp32_gemm_sgemm_amd import model
     import tiled_fp32_gemm_sgemm_amd as sg
@@ -166,6 +215,7 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
     window = workload in WINDOW_WORKLOADS
     conv = workload in CONV_WORKLOADS
     attn = workload in ATTN_WORKLOADS
+    gemm = not (window or conv or attn)
     w = (WINDOW_WORKLOADS[workload] if window else
          CONV_WORKLOADS[workload] if conv else
          ATTN_WORKLOADS[workload] if attn else WORKLOADS[workload])
@@ -174,14 +224,79 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
     L += ["#   " + c for c in commands]
     L.append("kernel_source_sha256_16: %s" % kernel_source_hash(
         WINDOW_SOURCES if window else ATTN_SOURCES if attn else GEMM_SOURCES))
-    if attn:
+    if attn or conv:
         L.append("flops_per_launch: %d" % w.flops)
-    if conv:
-        L.append("flops_per_launch: %d" % w.flops)
+    t_us = trace_average_us(trace_summary)
+    if t_us is not None:
+        L.append("trace_average_us: %.2f (%s, timed dispatches without the profiler)"
+                 % (t_us, os.path.relpath(trace_summary, ROOT)))
+
+    merged = {}
+    durs = []
+    for c in sq_csvs:
+        for d in _per_dispatch(_read_csv(c), kernel_part).values():
+            for k, v in d.items():
+                if k not in ("name", "dur_s"):
+                    merged.setdefault(k, []).append(v)
+            if "GRBM_GUI_ACTIVE" in d:
+                merged.setdefault("_clk", []).append(d["GRBM_GUI_ACTIVE"] / 8 / d["dur_s"])
+            durs.append(d["dur_s"])
+            merged.setdefault("_name", []).append(d["name"])
+    val = {k: _mean(v) for k, v in merged.items() if not k.startswith("_")}
+    if merged.get("_name"):
+        L.append("kernel: %s" % merged["_name"][0])
+    if durs:
+        L.append("counter_run_dispatch_average_us: %.2f" % (_mean(durs) * 1e6))
+    for k in sorted(val):
+        L.append("%s: %.6g" % (k, val[k]))
+
+    # ------------------------------------------------------------ utilisation
+    cap = SIMDS * MAX_CLOCK_GHZ * 1e9 * (t_us * 1e-6) if t_us else None
+    if "_clk" in merged:
+        g = _mean(merged["_clk"]) / 1e9
+        if g <= MAX_CLOCK_GHZ:
+            L.append("grbm_clock_ghz_counter_run: %.3f (GRBM_GUI_ACTIVE / 8 XCDs / counter-run "
+                     "dispatch duration)" % g)
+        else:
+            L.append("grbm_clock_ghz_counter_run: omitted (GRBM_GUI_ACTIVE / 8 / dispatch "
+                     "duration = %.3f GHz exceeds the %.1f GHz maximum: on a dispatch this short "
+                     "the active count includes the profiler's set-up and drain)"
+                     % (g, MAX_CLOCK_GHZ))
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in val:
+        busy = val["SQ_VALU_MFMA_BUSY_CYCLES"]
+        if val.get("SQ_INSTS_VALU_MFMA_F32"):
+            L.append("mfma_busy_cycles_per_instruction: %.2f (the counter adds the instruction's "
+                     "issue cycles: busy / peak cycles is achieved / peak FLOP rate)"
+                     % (busy / val["SQ_INSTS_VALU_MFMA_F32"]))
+        if cap:
+            u = busy / cap
+            L.append("mfma_busy_fraction_at_2.4GHz: %.4f (SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs "
+                     "x 2.4 GHz x trace_average_us))" % u)
+            L.append("mfma_rate_tflops_from_busy: %.2f (fraction x 157.3)" % (u * PEAK_FP32_TFLOPS))
+            flops = (w.flops if (attn or conv) else w.flops) if not window else 0
+            if flops:
+                L.append("trace_rate_tflops: %.2f (FLOPs per launch / trace_average_us)"
+                         % (flops / (t_us * 1e-6) / 1e12))
+    if "SQ_ACTIVE_INST_VALU" in val and cap:
+        # quad-cycles, summed over the SIMDs of every SE
+        L.append("valu_busy_fraction_at_2.4GHz: %.4f (4 x SQ_ACTIVE_INST_VALU / (1024 SIMDs x "
+                 "2.4 GHz x trace_average_us))" % (4 * val["SQ_ACTIVE_INST_VALU"] / cap))
+    if "SQ_ACTIVE_INST_VALU2" in val and cap:
+        L.append("valu_dual_issue_fraction_at_2.4GHz: %.4f (4 x SQ_ACTIVE_INST_VALU2 / (1024 "
+                 "SIMDs x 2.4 GHz x trace_average_us): quad-cycles in which a SIMD issued two "
+                 "VALU instructions)" % (4 * val["SQ_ACTIVE_INST_VALU2"] / cap))
+    if "SQ_INSTS_VALU_FMA_F32" in val and cap:
+        # one wave64 v_fmac_f32 is 64 FMAs = 128 FLOPs
+        L.append("valu_fma_rate_tflops: %.2f (SQ_INSTS_VALU_FMA_F32 x 128 FLOP / trace_average_us)"
+                 % (val["SQ_INSTS_VALU_FMA_F32"] * 128 / (t_us * 1e-6) / 1e12))
+
+    # ----------------------------------------------------------- memory side
+    compulsory = (w.bytes if window else conv_compulsory_bytes(w) if conv else
+                  4 * w.BH * w.D * (2 * w.Sq + 2 * w.Skv) if attn else
+                  model.compulsory_bytes(w.M, w.N, w.K, w.batch))
     copy_part = "MulFunctor"
     fetch = _per_dispatch(_read_csv(fetch_csv), kernel_part) if fetch_csv else {}
     write = _per_dispatch(_read_csv(write_csv), kernel_part) if write_csv else {}
-    hbm = None
     if fetch and write:
         cf = _per_dispatch(_read_csv(fetch_csv), copy_part)
         cw = _per_dispatch(_read_csv(write_csv), copy_part)
@@ -191,37 +306,35 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
         w_scale = COPY_BYTES / (w_copy * 1024.0)
         f_kib = _mean(d["FETCH_SIZE"] for d in fetch.values())
         w_kib = _mean(d["WRITE_SIZE"] for d in write.values())
-        hbm = f_kib * 1024 * f_scale + w_kib * 1024 * w_scale
+        rd = f_kib * 1024 * f_scale
+        wr = w_kib * 1024 * w_scale
         L += ["copy_kernel_bytes_each_way: %d" % COPY_BYTES,
               "copy_fetch_size_kib: %.1f" % f_copy, "copy_write_size_kib: %.1f" % w_copy,
               "fetch_scale: %.4f" % f_scale, "write_scale: %.4f" % w_scale,
               "kernel_fetch_size_kib: %.1f" % f_kib, "kernel_write_size_kib: %.1f" % w_kib,
-              "hbm_read_bytes_per_launch: %.0f" % (f_kib * 1024 * f_scale),
-              "hbm_write_bytes_per_launch: %.0f" % (w_kib * 1024 * w_scale),
-              "hbm_bytes_per_launch: %.0f" % hbm,
-              "compulsory_bytes: %d" % (w.bytes if window else
-                                        conv_compulsory_bytes(w) if conv else
-                                        4 * w.BH * w.D * (2 * w.Sq + 2 * w.Skv) if attn else
-                                        model.compulsory_bytes(w.M, w.N, w.K, w.batch))]
-    merged = {}
-    for c in sq_csvs:
-        for d in _per_dispatch(_read_csv(c), kernel_part).values():
-            for k, v in d.items():
-                if k not in ("name", "dur_s"):
-                    merged.setdefault(k, []).append(v)
-            if "GRBM_GUI_ACTIVE" in d and "SQ_VALU_MFMA_BUSY_CYCLES" in d:
-                merged.setdefault("_util", []).append(
-                    d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] / 8 * 1024))
-                merged.setdefault("_clk", []).append(d["GRBM_GUI_ACTIVE"] / 8 / d["dur_s"])
-            merged.setdefault("_name", []).append(d["name"])
-    if merged.get("_name"):
-        L.append("kernel: %s" % merged["_name"][0])
-    for k in sorted(merged):
-        if not k.startswith("_"):
-            L.append("%s: %.6g" % (k, _mean(merged[k])))
-    if "_util" in merged:
-        L.append("mfma_busy_fraction: %.4f" % _mean(merged["_util"]))
-        L.append("effective_clock_ghz_under_profiler: %.3f" % (_mean(merged["_clk"]) / 1e9))
+              "beyond_l2_read_bytes_per_launch: %.0f (FETCH_SIZE x fetch_scale)" % rd,
+              "beyond_l2_write_bytes_per_launch: %.0f (WRITE_SIZE x write_scale)" % wr,
+              "beyond_l2_bytes_per_launch: %.0f" % (rd + wr),
+              "compulsory_bytes: %d" % compulsory,
+              "beyond_l2_over_compulsory: %.3f" % ((rd + wr) / compulsory)]
+    if all(k in val for k in ("TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum",
+                              "TCC_EA0_RDREQ_128B_sum")):
+        by_size = (32 * val["TCC_EA0_RDREQ_32B_sum"] + 64 * val["TCC_EA0_RDREQ_64B_sum"] +
+                   128 * val["TCC_EA0_RDREQ_128B_sum"])
+        L.append("beyond_l2_read_bytes_by_request_size: %.0f (32 x RDREQ_32B + 64 x RDREQ_64B + "
+                 "128 x RDREQ_128B)" % by_size)
+        if fetch:
+            L.append("fetch_scale_check: %.4f (read bytes by request size / FETCH_SIZE x "
+                     "fetch_scale)" % (by_size / rd))
+        if "TCC_EA0_RDREQ_sum" in val:
+            n = (val["TCC_EA0_RDREQ_32B_sum"] + val["TCC_EA0_RDREQ_64B_sum"] +
+                 val["TCC_EA0_RDREQ_128B_sum"])
+            L.append("read_requests_by_size_over_all: %.4f" % (n / max(val["TCC_EA0_RDREQ_sum"], 1)))
+    if "TCC_EA0_RDREQ_DRAM_sum" in val and "TCC_EA0_RDREQ_sum" in val:
+        L.append("read_requests_to_dram_share: %.4f (TCC_EA0_RDREQ_DRAM / TCC_EA0_RDREQ)"
+                 % (val["TCC_EA0_RDREQ_DRAM_sum"] / max(val["TCC_EA0_RDREQ_sum"], 1)))
+
+    # --------------------------------------------------- closed forms, models
     if conv:
         P, Q = w.out_hw
         cfg = config if config is not None else sg.conv2d_select_config(
@@ -240,10 +353,14 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
                     for b in range(qb))
         L.append("mfma_instructions_closed_form: %d (attention, 256 x 64 blocks)"
                  % (w.BH * pairs * 8 * 2 * w.D))
-    if path == "mfma" and not window and not conv and not attn:
-        cfg = sg.select_config(w.M, w.N, w.K, w.batch) if config is None else config
+    if path in ("mfma", "splitk") and gemm:
+        n_split = 1
+        if path == "splitk":
+            cfg, n_split, _ = sg.splitk_plan(w.M, w.N, w.K, splits)
+        else:
+            cfg = sg.select_config(w.M, w.N, w.K, w.batch) if config is None else config
         info = sg.config_info(cfg)
-        mi = 16 if info["name"].startswith("mfma16") else 32
+        mi = 16 if info["name"].startswith("dl16") or info["name"].startswith("mfma16") else 32
         want = model.mfma_instructions(w.M, w.N, w.K, info["bm"], info["bn"], info["bk"], mi,
                                        w.batch)
         L.append("mfma_instructions_closed_form: %d (tile %s)" % (want, info["name"]))
@@ -252,20 +369,39 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
         L.append("global_to_lds_values_model: %d" % staged)
         # one 64-lane dwordx4 instruction moves 256 values
         L.append("global_dwordx4_wave_instructions_closed_form: %d" % (staged // 256))
-        if "TCP_TCC_READ_REQ_sum" in merged:
+        if "TCP_TCC_READ_REQ_sum" in val:
             # L1 -> L2 read requests, taken as one 128-byte line each
-            req = _mean(merged["TCP_TCC_READ_REQ_sum"])
+            req = val["TCP_TCC_READ_REQ_sum"]
             L.append("l2_read_request_bytes_at_128B: %.0f (%.4f x the global-to-LDS model)"
                      % (req * 128, req * 128 / (4.0 * staged)))
-    if path == "valu" and "SQ_INSTS_VALU_FMA_F32" in merged:
+        resident = 32 * sg.workgroups_per_cu(cfg)
+        # Split-K: chunk b of every tile runs as batch member b over K / chunks.
+        panels = model.per_xcd_operand_bytes(w.M, w.N, model.ceil_div(w.K, n_split), info["bm"],
+                                             info["bn"], w.batch * n_split, resident=resident)
+        L.append("per_xcd_panel_read_bytes_model: %d (each XCD's L2 fetches the A and B panels "
+                 "of each round of %d resident tiles once)" % (panels, resident))
+        if fetch:
+            L.append("beyond_l2_read_over_panel_model: %.4f" % (rd / panels))
+        if n_split > 1:
+            tiles = model.ceil_div(w.M, info["bm"]) * model.ceil_div(w.N, info["bn"])
+            part = tiles * n_split * info["bm"] * info["bn"] * 4
+            L.append("splitk_chunks: %d" % n_split)
+            L.append("splitk_partial_bytes_model: %d (tiles x chunks x BM x BN x 4, written once "
+                     "and read once by the join)" % part)
+            if fetch and write:
+                L.append("beyond_l2_write_minus_output_over_partials: %.4f ((write bytes - 4MN) "
+                         "/ partial bytes)" % ((wr - 4.0 * w.M * w.N) / part))
+                L.append("beyond_l2_read_minus_panels_over_partials: %.4f ((read bytes - panel "
+                         "model) / partial bytes)" % ((rd - panels) / part))
+    if path == "valu" and "SQ_INSTS_VALU_FMA_F32" in val:
         L.append("valu_fma_instructions_closed_form: %d" % model.valu_fma_instructions(
             w.M, w.N, w.K, batch=w.batch))
-    if "SQ_WAIT_ANY" in merged and "SQ_WAVE_CYCLES" in merged:
+    if "SQ_WAIT_ANY" in val and "SQ_WAVE_CYCLES" in val:
         L.append("wave_cycles_waiting_fraction: %.4f"
-                 % (_mean(merged["SQ_WAIT_ANY"]) / _mean(merged["SQ_WAVE_CYCLES"])))
-    if "SQ_LDS_BANK_CONFLICT" in merged and "SQ_LDS_IDX_ACTIVE" in merged:
-        c = _mean(merged["SQ_LDS_BANK_CONFLICT"])
-        a = _mean(merged["SQ_LDS_IDX_ACTIVE"])
+                 % (val["SQ_WAIT_ANY"] / val["SQ_WAVE_CYCLES"]))
+    if "SQ_LDS_BANK_CONFLICT" in val and "SQ_LDS_IDX_ACTIVE" in val:
+        c = val["SQ_LDS_BANK_CONFLICT"]
+        a = val["SQ_LDS_IDX_ACTIVE"]
         L.append("lds_bank_conflicts_per_access: %.4f" % (c / max(1.0, a - c)))
     open(out, "w").write("\n".join(L) + "\n")
 
@@ -658,8 +794,10 @@ def main(argv=None) -> int:
                     help="untimed steps first (default: GEMMs as many as fill 0.1 s, at least "
                          "30, so clocks have settled; 200 for the window and convolution; 30 "
                          "for attention)")
-    ap.add_argument("--path", choices=["mfma", "valu", "window"], default="mfma",
-                    help="GEMM path (window: counter summaries of the window kernel only)")
+    ap.add_argument("--path", choices=["mfma", "valu", "splitk", "window"], default="mfma",
+                    help="GEMM path: the matrix-core product (sgemm), the vector-ALU comparator, "
+                         "or the split-K entry point at --splits (window: counter summaries of "
+                         "the window kernel only)")
     ap.add_argument("--workload", default="square4096")
     ap.add_argument("--config", type=int, default=None, help="force a matrix-core tile config")
     ap.add_argument("--splits", type=int, default=0,
@@ -689,6 +827,9 @@ def main(argv=None) -> int:
     ap.add_argument("--fetch-csv")
     ap.add_argument("--write-csv")
     ap.add_argument("--sq-csv", action="append", default=[])
+    ap.add_argument("--trace-summary",
+                    help="committed kernel-trace summary whose timed average is the duration "
+                         "the counter summary's utilisation is taken over")
     ap.add_argument("--kernel-part", default="sgemm_mfma")
     ap.add_argument("--command", action="append", default=[])
     ap.add_argument("--out")
@@ -715,7 +856,8 @@ def main(argv=None) -> int:
         return 0
     if args.summarize_counters:
         summarize_counters(args.out, args.workload, args.path, args.kernel_part, args.fetch_csv,
-                           args.write_csv, args.sq_csv, args.command + [own_cmd], args.config)
+                           args.write_csv, args.sq_csv, args.command + [own_cmd], args.config,
+                           args.trace_summary, args.splits)
         return 0
 
     if args.gpus != 1:
@@ -886,6 +1028,25 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) / n_steps
 
+    if args.path == "splitk" and (args.graph or w.batch != 1):
+        print("--path splitk times single products, launched on a stream", file=sys.stderr)
+        return 2
+    # Clock settle: the workload's own launches, back to back, for
+    # SETTLE_S before the warm-up steps.  After an idle spell (loading the
+    # operands, the oracle) the first ~25 ms of launches run 10-20 % slow
+    # while the clock ramps up; the timed steps measure the settled clock.
+    t0 = time.perf_counter()
+    n_settle = 0
+    batch = 4
+    while time.perf_counter() - t0 < SETTLE_S:
+        tb = time.perf_counter()
+        for _ in range(batch):
+            step()
+        torch.cuda.synchronize()
+        n_settle += batch
+        # about 10 ms of launches between synchronisations
+        batch = max(4, min(4096, int(0.01 * batch / max(time.perf_counter() - tb, 1e-6))))
+    settle = {"launches": n_settle, "seconds": round(time.perf_counter() - t0, 4)}
     args.warmup, args.steps = counts()
     if args.graph and args.cold:
         print("--graph and --cold exclude each other", file=sys.stderr)
@@ -904,7 +1065,9 @@ def main(argv=None) -> int:
     flops = float(w.flops)
     tflops = flops / (ms * 1e-3) / 1e12
 
-    if args.config is not None:
+    if args.path == "splitk":
+        tile = "%s_splits%d" % (sg.config_info(sk_config)["name"], sk_splits)
+    elif args.config is not None:
         tile = sg.config_info(args.config)["name"]
     elif args.path == "mfma":
         tile = sg.config_info(sg.select_config(w.M, w.N, w.K, w.batch))["name"]
@@ -915,18 +1078,18 @@ def main(argv=None) -> int:
     traffic = (read_traffic(TRAFFIC_FILE, GEMM_SOURCES, tile)
                if args.path == "mfma" and args.workload == "square4096" and args.config is None
                and not args.cold else None)
-    roofline = {"bound": "mfma" if args.path == "mfma" else "alu",
+    roofline = {"bound": "alu" if args.path == "valu" else "mfma",
                 "achieved": tflops,
                 "peak": PEAK_FP32_TFLOPS,
                 "unit": "TFLOP/s",
                 "frac": None,
                 "traffic": traffic,
                 "kernel": tile,
-                "avg_kernel_ms": ms}
+                "event_ms_per_launch": ms}
     roofline["frac"] = roofline["achieved"] / roofline["peak"]
 
     comparators = {}
-    if not args.no_comparator and w.batch == 1:
+    if not args.no_comparator and w.batch == 1 and args.path != "splitk":
         other = "valu" if args.path == "mfma" else "mfma"
         oms = timed(max(5, args.steps // 5), 3, other, None)
         comparators[other] = {"tflops": flops / (oms * 1e-3) / 1e12, "ms_per_step": oms}
@@ -959,7 +1122,7 @@ def main(argv=None) -> int:
             parity = gemm_parity(C_rows, keep)
 
     out = {
-        "metric": METRIC,
+        "metric": gemm_metric(w),
         "value": tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -973,6 +1136,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "pct_of_fp32_peak": 100.0 * tflops / PEAK_FP32_TFLOPS,
         "cache": "cold" if args.cold else "warm",
+        "clock_settle": settle,
         "launch": "hip_graph" if args.graph else "stream",
         "single_launch": {"n": len(single),
                           "median_ms": single[len(single) // 2],

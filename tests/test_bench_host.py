@@ -19,7 +19,7 @@ def _summary(tmp_path, source_hash, tile, hbm="123456.0"):
     p = tmp_path / "counters.txt"
     p.write_text("# counters\nkernel_source_sha256_16: %s\n"
                  "mfma_instructions_closed_form: 33554432 (tile %s)\n"
-                 "hbm_bytes_per_launch: %s\n" % (source_hash, tile, hbm))
+                 "beyond_l2_bytes_per_launch: %s\n" % (source_hash, tile, hbm))
     return str(p)
 
 
@@ -92,3 +92,70 @@ def test_gemm_parity_ratio():
     bad = ref.astype(np.float32).copy()
     bad[1, 1] = 1e-30
     assert not bench.gemm_parity(bad, keep)["within_bound"]
+
+
+def test_trace_average_and_metric_strings(tmp_path):
+    from workloads import WORKLOADS
+    p = tmp_path / "t.txt"
+    p.write_text("kernel: k\n  calls: 9  average_us: 12.50  min_us: 1\n"
+                 "  timed_average_us (100 dispatches before the last 50): 11.25\n")
+    assert bench.trace_average_us(str(p)) == 11.25
+    p.write_text("kernel: k\n  calls: 9  average_us: 12.50  min_us: 1\n")
+    assert bench.trace_average_us(str(p)) == 12.5
+    assert bench.trace_average_us(str(tmp_path / "none.txt")) is None
+    assert bench.gemm_metric(WORKLOADS["square4096"]) == bench.METRIC
+    assert "batch 1024 x M=128 N=128 K=128" in bench.gemm_metric(WORKLOADS["batched128"])
+    assert "M=1024 N=1024 K=1024" in bench.gemm_metric(WORKLOADS["square1024"])
+    assert "(1/sqrt(K))" in WORKLOADS["square4096"].describe()
+
+
+def _counter_csv(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value",
+                    "Start_Timestamp", "End_Timestamp"])
+        for r in rows:
+            w.writerow(r)
+
+
+def test_counter_summary_derivations(tmp_path):
+    """Utilisation over the trace duration at 2.4 GHz; the GRBM clock shown
+    only when it is at most 2.4 GHz; beyond-L2 bytes scaled by the copy
+    kernel and checked against the request sizes."""
+    k = "sgemm_dev::sgemm_mfma_dl_kernel<x>"
+    cp = "MulFunctor<float>"
+    trace = tmp_path / "trace.txt"
+    trace.write_text("kernel: %s\n  calls: 3  average_us: 20.00\n"
+                     "  timed_average_us (last 3 dispatches): 20.00\n" % k)
+    copy_kib = bench.COPY_BYTES / 1024.0
+    _counter_csv(tmp_path / "f.csv", [(1, cp, "FETCH_SIZE", copy_kib / 2, 0, 1000),
+                                      (2, k, "FETCH_SIZE", 1000.0, 0, 25000)])
+    _counter_csv(tmp_path / "w.csv", [(1, cp, "WRITE_SIZE", copy_kib, 0, 1000),
+                                      (2, k, "WRITE_SIZE", 4096.0, 0, 25000)])
+    busy = 0.5 * 1024 * 2.4e9 * 20e-6
+    # 25 us dispatch: 2.0 GHz would be 50000 cycles per XCD; 3.0 GHz 75000.
+    _counter_csv(tmp_path / "s1.csv", [(2, k, "SQ_VALU_MFMA_BUSY_CYCLES", busy, 0, 25000),
+                                       (2, k, "SQ_INSTS_VALU_MFMA_F32", busy / 64, 0, 25000),
+                                       (2, k, "GRBM_GUI_ACTIVE", 8 * 50000, 0, 25000)])
+    _counter_csv(tmp_path / "s2.csv", [(2, k, "TCC_EA0_RDREQ_32B_sum", 0, 0, 25000),
+                                       (2, k, "TCC_EA0_RDREQ_64B_sum", 0, 0, 25000),
+                                       (2, k, "TCC_EA0_RDREQ_128B_sum", 16000, 0, 25000),
+                                       (2, k, "TCC_EA0_RDREQ_sum", 16000, 0, 25000),
+                                       (2, k, "GRBM_GUI_ACTIVE", 8 * 75000, 0, 25000)])
+    out = tmp_path / "c.txt"
+
+    def summary(sq):
+        bench.summarize_counters(str(out), "square1024", "mfma", "sgemm_", str(tmp_path / "f.csv"),
+                                 str(tmp_path / "w.csv"), sq, ["cmd"], None, str(trace))
+        return dict(l.split(": ", 1) for l in out.read_text().splitlines()
+                    if ": " in l and not l.startswith("#"))
+
+    v = summary([str(tmp_path / "s1.csv")])
+    assert v["mfma_busy_fraction_at_2.4GHz"].startswith("0.5000")
+    assert v["mfma_busy_cycles_per_instruction"].startswith("64.00")
+    assert v["grbm_clock_ghz_counter_run"].startswith("2.000")
+    assert v["beyond_l2_read_bytes_per_launch"].startswith("2048000")
+    assert v["beyond_l2_write_bytes_per_launch"].startswith("4194304")
+    v = summary([str(tmp_path / "s2.csv")])
+    assert v["grbm_clock_ghz_counter_run"].startswith("omitted")
+    assert v["fetch_scale_check"].startswith("1.0000")

@@ -74,3 +74,34 @@ def test_mfma_instruction_closed_form(MI, kstep):
 
 def test_valu_fma_closed_form():
     assert model.valu_fma_instructions(1024, 1024, 1024) == 1024 ** 3 // 64
+
+
+def test_per_xcd_panel_bytes_closed_forms():
+    """4096^3 on 256 x 256 tiles: 256 tiles, 32 per XCD in one round, which in
+    the grouped order (8 tile rows per group) are 8 tile rows x 4 tile columns;
+    each XCD fetches 8 A panels and 4 B panels of 256 x 4096 floats."""
+    panel = 256 * 4096 * 4
+    assert model.per_xcd_operand_bytes(4096, 4096, 4096, 256, 256, resident=32) == \
+        8 * (8 + 4) * panel
+    # One XCD holding every tile in one round: each panel once (compulsory A + B).
+    assert model.per_xcd_operand_bytes(4096, 4096, 4096, 256, 256, xcds=1) == \
+        4 * (2 * 4096 * 4096)
+    # 16384 x 4096 x 4096: 128 tiles per XCD in 4 rounds of 32; every round
+    # re-reads the XCD's 8 A panels and reads 4 new B panels.
+    assert model.per_xcd_operand_bytes(16384, 4096, 4096, 256, 256, resident=32) == \
+        8 * 4 * (8 + 4) * panel
+    # Independent products of a batch share nothing: A and B once each.
+    assert model.per_xcd_operand_bytes(128, 128, 128, 128, 128, batch=1024, resident=128) == \
+        1024 * 2 * 128 * 128 * 4
+    # Ragged edges count only the rows and columns that exist.
+    assert model.per_xcd_operand_bytes(100, 70, 10, 64, 64, xcds=1) == 4 * (100 * 10 + 70 * 10)
+
+
+def test_grouped_order_and_xcd_runs():
+    assert model.xcd_of_blocks(20, 8) == [(0, 3), (3, 3), (6, 3), (9, 3), (12, 2), (14, 2),
+                                          (16, 2), (18, 2)]
+    # group of 8 tile rows: the tile row varies fastest
+    assert [model.grouped_tile(p, 16, 16, 8) for p in (0, 1, 7, 8, 127, 128)] == \
+        [(0, 0), (1, 0), (7, 0), (0, 1), (7, 15), (8, 0)]
+    # a last group shorter than group_m
+    assert model.grouped_tile(130, 10, 16, 8) == (8, 1)

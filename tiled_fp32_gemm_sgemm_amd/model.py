@@ -140,3 +140,62 @@ def window_bytes(n: int, W: int, elem: int = 4) -> int:
     """Compulsory traffic of the window sum: the n + W - 1 inputs read once
     and the n outputs written once."""
     return elem * ((n + W - 1 if n > 0 else 0) + n)
+
+
+def xcd_of_blocks(nblocks: int, xcds: int = 8):
+    """Tile id handled by each workgroup, by XCD: workgroups go to the XCDs
+    round-robin (block id % xcds), and the kernels renumber them so that each
+    XCD owns a contiguous run of tile ids (the first nblocks % xcds XCDs one
+    more).  Returns a list of (first tile id, count) per XCD."""
+    q, r = divmod(nblocks, xcds)
+    out = []
+    first = 0
+    for x in range(xcds):
+        n = q + (1 if x < r else 0)
+        out.append((first, n))
+        first += n
+    return out
+
+
+def grouped_tile(pid: int, tiles_m: int, tiles_n: int, group_m: int):
+    """(tile row, tile column) of tile id pid in the grouped order: groups of
+    group_m tile rows, the tile row varying fastest inside a group."""
+    per_group = group_m * tiles_n
+    group = pid // per_group
+    first_m = group * group_m
+    gsize = min(tiles_m - first_m, group_m)
+    in_group = pid - group * per_group
+    return first_m + in_group % gsize, in_group // gsize
+
+
+def per_xcd_operand_bytes(M: int, N: int, K: int, BM: int, BN: int, batch: int = 1,
+                          group_m: int = 8, xcds: int = 8, resident: int = 0,
+                          elem: int = 4) -> int:
+    """Bytes of A and B that reach the L2 caches when each XCD's L2 fetches
+    every operand row panel and column panel that a round of its tiles uses
+    exactly once.
+
+    Each XCD has its own L2, so a panel used by tiles on several XCDs crosses
+    into L2 once per XCD.  An XCD runs its tiles in rounds of `resident`
+    (the workgroups its CUs hold at once; 0: all of them in one round), in
+    tile-id order; a round streams its panels through K, far more than one
+    L2 holds, so a panel used again in a later round is fetched again.  The
+    count is the sum over XCDs and rounds of the distinct A panels (BM rows x
+    K, clipped at M) and B panels (K x BN, clipped at N).  The output is not
+    included.  Compulsory traffic counts each panel once for the whole chip.
+    """
+    tiles_m, tiles_n = ceil_div(M, BM), ceil_div(N, BN)
+    per_matrix = tiles_m * tiles_n
+    total = 0
+    for first, count in xcd_of_blocks(per_matrix * batch, xcds):
+        step = resident if resident > 0 else max(count, 1)
+        for r0 in range(first, first + count, step):
+            rows, cols = set(), set()
+            for pid in range(r0, min(first + count, r0 + step)):
+                b, t = divmod(pid, per_matrix)
+                tm, tn = grouped_tile(t, tiles_m, tiles_n, group_m)
+                rows.add((b, tm))
+                cols.add((b, tn))
+            total += sum(min(BM, M - tm * BM) for _, tm in rows) * K
+            total += sum(min(BN, N - tn * BN) for _, tn in cols) * K
+    return elem * total
