@@ -277,14 +277,24 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
             if flops:
                 L.append("trace_rate_tflops: %.2f (FLOPs per launch / trace_average_us)"
                          % (flops / (t_us * 1e-6) / 1e12))
-    if "SQ_ACTIVE_INST_VALU" in val and cap:
-        # quad-cycles, summed over the SIMDs of every SE
-        L.append("valu_busy_fraction_at_2.4GHz: %.4f (4 x SQ_ACTIVE_INST_VALU / (1024 SIMDs x "
-                 "2.4 GHz x trace_average_us))" % (4 * val["SQ_ACTIVE_INST_VALU"] / cap))
-    if "SQ_ACTIVE_INST_VALU2" in val and cap:
-        L.append("valu_dual_issue_fraction_at_2.4GHz: %.4f (4 x SQ_ACTIVE_INST_VALU2 / (1024 "
-                 "SIMDs x 2.4 GHz x trace_average_us): quad-cycles in which a SIMD issued two "
-                 "VALU instructions)" % (4 * val["SQ_ACTIVE_INST_VALU2"] / cap))
+    if "SQ_ACTIVE_INST_VALU" in val and "SQ_ACTIVE_INST_VALU2" in val and cap:
+        # Quad-cycles summed over every SIMD: SQ_ACTIVE_INST_VALU adds one per
+        # wave64 VALU instruction, SQ_ACTIVE_INST_VALU2 one per quad-cycle in
+        # which a SIMD issued two (from two waves), so quad-cycles with any
+        # VALU issue = ACTIVE - ACTIVE2.
+        quads = cap / 4
+        act, act2 = val["SQ_ACTIVE_INST_VALU"], val["SQ_ACTIVE_INST_VALU2"]
+        L.append("valu_issue_quad_cycle_fraction_at_2.4GHz: %.4f ((SQ_ACTIVE_INST_VALU - "
+                 "SQ_ACTIVE_INST_VALU2) / quad-cycles of 1024 SIMDs at 2.4 GHz over "
+                 "trace_average_us)" % ((act - act2) / quads))
+        L.append("valu_dual_issue_quad_cycle_fraction_at_2.4GHz: %.4f (SQ_ACTIVE_INST_VALU2 / "
+                 "the same quad-cycles: a SIMD issued two VALU instructions)" % (act2 / quads))
+        if "SQ_INSTS_VALU_FMA_F32" in val:
+            # Two issue slots per SIMD quad-cycle, each a wave64 instruction
+            # of 64 FMAs: all of them v_fmac_f32 is the 157.3 TFLOP/s peak.
+            L.append("valu_fma_issue_slot_efficiency: %.4f (SQ_INSTS_VALU_FMA_F32 / (2 x the "
+                     "quad-cycles): the pages' eta, FMA-issuing slots over all slots)"
+                     % (val["SQ_INSTS_VALU_FMA_F32"] / (2 * quads)))
     if "SQ_INSTS_VALU_FMA_F32" in val and cap:
         # one wave64 v_fmac_f32 is 64 FMAs = 128 FLOPs
         L.append("valu_fma_rate_tflops: %.2f (SQ_INSTS_VALU_FMA_F32 x 128 FLOP / trace_average_us)"
@@ -545,7 +555,7 @@ def bench_window(args) -> int:
         "config": {"workload": w.describe(), "n": w.n, "W": w.W},
         "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": gbs / PEAK_HBM_GBS, "traffic": traffic,
-                     "kernel": "window_sum_kernel", "avg_kernel_ms": ms},
+                     "kernel": "window_sum_kernel", "event_ms_per_launch": ms},
         "cpu_baseline": None if args.no_cpu_baseline else window_cpu_baseline(w, x_cpu),
         "comparators": comparators,
         "device": torch.cuda.get_device_name(dev),
@@ -651,6 +661,10 @@ def bench_conv(args) -> int:
         "dtype": "f32",
         "data": "synthetic",
         "pct_of_fp32_peak": 100.0 * tflops / PEAK_FP32_TFLOPS,
+        # value counts every multiply-add of the implicit product (dense
+        # equivalent); the useful rate leaves out the taps on the zero padding
+        "useful_tflops": w.useful_flops / (ms * 1e-3) / 1e12,
+        "useful_flop_share": w.useful_flops / w.flops,
         "config": {"workload": w.describe(), "N": w.N, "H": w.H, "W": w.W, "C": w.C, "K": w.K,
                    "R": w.R, "S": w.S, "tile": sg.config_info(cfg)["name"]},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_FP32_TFLOPS,
@@ -659,7 +673,7 @@ def bench_conv(args) -> int:
                                               sg.config_info(cfg)["name"])
                                  if args.workload == "conv3x3_c256" and args.config is None
                                  else None),
-                     "kernel": sg.config_info(cfg)["name"], "avg_kernel_ms": ms},
+                     "kernel": sg.config_info(cfg)["name"], "event_ms_per_launch": ms},
         "cpu_baseline": None if args.no_cpu_baseline else conv_cpu_baseline(w, x_cpu, wt_cpu),
         "comparators": comparators,
         "device": torch.cuda.get_device_name(dev),
@@ -774,7 +788,7 @@ def bench_attention(args) -> int:
                      "unit": "TFLOP/s", "frac": tflops / PEAK_FP32_TFLOPS,
                      "traffic": (read_traffic(ATTN_TRAFFIC_FILE, ATTN_SOURCES)
                                  if args.workload == "attn_s2048_d128" else None),
-                     "kernel": kernel, "avg_kernel_ms": ms},
+                     "kernel": kernel, "event_ms_per_launch": ms},
         "cpu_baseline": (None if args.no_cpu_baseline
                          else attn_cpu_baseline(w, q_cpu, k_cpu, v_cpu, scale)),
         "comparators": comparators,

@@ -105,3 +105,27 @@ def test_grouped_order_and_xcd_runs():
         [(0, 0), (1, 0), (7, 0), (0, 1), (7, 15), (8, 0)]
     # a last group shorter than group_m
     assert model.grouped_tile(130, 10, 16, 8) == (8, 1)
+
+
+def test_convolution_useful_flops_by_brute_force():
+    """Taps on the zero padding are left out of the useful count: checked by
+    counting, output by output, the input pixels each filter tap lands on."""
+    from workloads import ConvWorkload
+    for (H, W, R, S, pad, stride, dil) in [(14, 14, 3, 3, (1, 1), (1, 1), (1, 1)),
+                                           (9, 7, 3, 2, (2, 0), (2, 1), (1, 2)),
+                                           (5, 6, 1, 1, (0, 0), (1, 1), (1, 1))]:
+        w = ConvWorkload("t", 2, H, W, 3, 4, R, S, pad, stride, dil, 0)
+        P, Q = w.out_hw
+        n = 0
+        for p in range(P):
+            for q in range(Q):
+                for r in range(R):
+                    for s in range(S):
+                        ih = p * stride[0] - pad[0] + r * dil[0]
+                        iw = q * stride[1] - pad[1] + s * dil[1]
+                        n += 0 <= ih < H and 0 <= iw < W
+        assert w.useful_flops == 2 * w.N * w.K * w.C * n
+        assert w.useful_flops <= w.flops
+    # 14 x 14, 3 x 3, pad 1: 40 of 42 taps per axis land inside, 1600 / 1764.
+    w = ConvWorkload("t", 64, 14, 14, 256, 256, 3, 3, (1, 1), (1, 1), (1, 1), 0)
+    assert w.useful_flops * 1764 == w.flops * 1600

@@ -148,8 +148,51 @@ def check_magnitudes(att):
         assert np.allclose(smax[0], np.where(allowed, sabs, 0.0).max(axis=1), rtol=1e-13)
 
 
+def check_magnitude_closed_forms(att):
+    """mag and smax against values written out by hand, not by restating the
+    oracle's formula: one key (every weight is 1, so mag is |v| of that key
+    and smax is scale * sum_d |q_d||k_d|); zero queries (uniform weights over
+    the allowed keys, so mag is the mean |v| over them, and smax is 0); keys
+    that grow with their index (the largest allowed key gives smax)."""
+    H, D = 1, 4
+    # One key: q = (1, -2, 3, 0), k = (2, 1, -1, 5), scale 1/4.
+    Q = np.array([[[1, -2, 3, 0], [0, 0, 0, 0]]], np.float32)
+    K = np.array([[[2, 1, -1, 5]]], np.float32)
+    V = np.array([[[-1.5, 2.0, 0.25, -3.0]]], np.float32)
+    _, mag, smax = att(Q, K, V, H, 2, 1, D, 0.25, False)
+    assert np.array_equal(mag[0], np.abs(V[0, [0, 0]]).astype(np.float64))
+    assert smax[0, 0] == 0.25 * (2 + 2 + 3 + 0) and smax[0, 1] == 0.0
+    # Zero queries, five keys: uniform weights.
+    Sq, Skv = 3, 5
+    Q = np.zeros((H, Sq, D), np.float32)
+    K = np.arange(H * Skv * D, dtype=np.float32).reshape(H, Skv, D) - 7
+    V = np.array([[[1, -2, 0, 4], [3, 0, -1, 1], [-5, 2, 2, 0], [0, 1, 1, -1],
+                   [2, 2, -3, 3]]], np.float32)
+    _, mag, smax = att(Q, K, V, H, Sq, Skv, D, 0.5, False)
+    want = np.array([11, 7, 7, 9], np.float64) / 5      # column sums of |V| over 5 keys
+    for i in range(Sq):
+        assert np.allclose(mag[0, i], want, rtol=1e-15, atol=0)
+    assert np.all(smax == 0.0)
+    # Causal: query i sees keys 0..i, uniform weights over them.
+    _, mag, smax = att(Q, K, V, H, Sq, Skv, D, 0.5, True)
+    want_rows = [np.array([1, 2, 0, 4]) / 1, np.array([4, 2, 1, 5]) / 2,
+                 np.array([9, 4, 3, 5]) / 3]
+    for i in range(Sq):
+        assert np.allclose(mag[0, i], want_rows[i], rtol=1e-15, atol=0)
+    # Keys k_j = (j, j, j, j) and q = (1, 1, 1, 1): scale * sum_d |q||k_j| = 4 j / 8.
+    Sq, Skv = 4, 6
+    Q = np.ones((H, Sq, D), np.float32)
+    K = np.repeat(np.arange(Skv, dtype=np.float32)[None, :, None], D, axis=2)
+    V = np.ones((H, Skv, D), np.float32)
+    _, _, smax = att(Q, K, V, H, Sq, Skv, D, 0.125, False)
+    assert np.all(smax[0] == 0.125 * 4 * (Skv - 1))
+    _, _, smax = att(Q, K, V, H, Sq, Skv, D, 0.125, True)
+    assert np.array_equal(smax[0], 0.125 * 4 * np.arange(Sq, dtype=np.float64))
+
+
 PIN_CHECKS = [check_torch_sdpa, check_single_key, check_uniform_weights, check_dominant_key,
-              check_key_shift_invariance, check_kv_permutation, check_magnitudes]
+              check_key_shift_invariance, check_kv_permutation, check_magnitudes,
+              check_magnitude_closed_forms]
 
 
 @pytest.mark.parametrize("chk", PIN_CHECKS, ids=lambda c: c.__name__)

@@ -910,12 +910,15 @@ int sgemm_config_workgroups_per_cu(int config) {
     const ConfigEntry& c = kConfigs[config];
     // The runtime's answer counts the registers the compiler actually used;
     // the launch bound in the table is only the floor it guarantees.
+    // A failed lookup clears only an error of its own: one the caller had
+    // pending (an earlier asynchronous launch failure, say) stays in place.
+    const hipError_t before = hipPeekAtLastError();
     int blocks = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, c.kernel, c.threads, 0) ==
             hipSuccess &&
         blocks > 0)
         return blocks;
-    (void)hipGetLastError();
+    if (before == hipSuccess) (void)hipGetLastError();
     return c.wg_per_cu;
 }
 

@@ -160,9 +160,25 @@ class ConvWorkload:
 
     @property
     def flops(self) -> int:
-        # every multiply-add of the definition, zero-padded taps included
+        # every multiply-add of the implicit product, zero-padded taps included
+        # (the dense-equivalent count)
         P, Q = self.out_hw
         return 2 * self.N * P * Q * self.K * self.R * self.S * self.C
+
+    def _valid_taps_1d(self, size, pad, stride, dil, taps, out):
+        """Sum over the output positions of the filter taps that land inside
+        the input along one axis."""
+        return sum(1 for o in range(out) for t in range(taps)
+                   if 0 <= o * stride - pad + t * dil < size)
+
+    @property
+    def useful_flops(self) -> int:
+        # multiply-adds whose input pixel lies inside the image: the taps on
+        # the zero padding left out
+        P, Q = self.out_hw
+        rows = self._valid_taps_1d(self.H, self.pad[0], self.stride[0], self.dil[0], self.R, P)
+        cols = self._valid_taps_1d(self.W, self.pad[1], self.stride[1], self.dil[1], self.S, Q)
+        return 2 * self.N * rows * cols * self.K * self.C
 
     def describe(self) -> str:
         return ("conv2d_nhwc N=%d H=%d W=%d C=%d K=%d R=%d S=%d pad=%s stride=%s dil=%s "
