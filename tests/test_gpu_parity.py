@@ -87,7 +87,7 @@ def _call(path, *args, **kw):
     return run_gpu(*args, path=path, **kw)
 
 
-ALL_PATHS = ["valu"] + ["cfg%d" % i for i in range(32)]
+ALL_PATHS = ["valu"] + ["cfg%d" % i for i in range(33)]
 
 
 @pytest.mark.parametrize("path", ALL_PATHS)
@@ -179,7 +179,7 @@ def test_invalid_arguments_enqueue_nothing():
 
 # ------------------------------------------------------------------ batched
 
-@pytest.mark.parametrize("path", ["mfma", "valu", "cfg1", "cfg2", "cfg5", "cfg6", "cfg7", "cfg11", "cfg13",
+@pytest.mark.parametrize("path", ["mfma", "valu", "cfg1", "cfg2", "cfg5", "cfg6", "cfg7", "cfg11", "cfg13", "cfg32",
                                   "cfg15", "cfg16", "cfg17", "cfg23", "cfg25"])
 def test_batched_ragged_members_differ(path):
     M, N, K, lda, ldb, ldc, batch = 45, 77, 33, 36, 80, 79, 6

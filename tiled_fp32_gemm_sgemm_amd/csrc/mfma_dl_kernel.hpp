@@ -30,7 +30,8 @@
 // 4 bytes, and ds_read_b32 32 lanes per pass over 32 banks (measured):
 //  * A slice As[m][k], BK floats per row, quad kq of row r stored at
 //    kq ^ ((r / rows_per_256_bytes) % (BK/4)) (as in mfma_kernel.hpp): the 16
-//    rows of a b128 pass hit 16 distinct quads of the bank row.
+//    rows of a b128 pass hit 16 distinct quads of the bank row.  With BK = 128
+//    (512-byte rows) the flip is kq ^ (r % 16), inside each 16-quad half.
 //  * B slice Bs[k][n], BN floats per row, unpadded.  The output columns are
 //    interleaved over a wave's column tiles (DlTile::bcol): lane li of column
 //    tile ni owns column li * BV + ni % BV of each BV-tile run, so the BV
@@ -108,7 +109,7 @@ struct DlTile {
     static constexpr int A_FLOATS = BM * BK;
     static constexpr int B_FLOATS = BK * BN;
     static constexpr int BUF_FLOATS = A_FLOATS + B_FLOATS;
-    static constexpr int RPB = 16 / QPR;
+    static constexpr int RPB = QPR >= 16 ? 1 : 16 / QPR;  // stored rows per 256 bytes
     static constexpr int KG = 4;
     static constexpr int NKG = KPL / KG;
     static constexpr int HOLD = 2;                       // k steps issued after the barrier
@@ -168,7 +169,7 @@ struct DlTile {
                                          ? (4 * OCC * 64 / NT) : (160 * 1024 / LDS_BYTES);
 
     static_assert(MI == 16 || MI == 32, "MFMA tile edge");
-    static_assert(BK == 16 || BK == 32 || BK == 64, "BK must be 16, 32 or 64");
+    static_assert(BK == 16 || BK == 32 || BK == 64 || BK == 128, "BK must be 16, 32, 64 or 128");
     static_assert(KPL % KG == 0 && NKG % 2 == 0, "whole, even number of A operand groups");
     static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile must be MFMA tile multiples");
     static_assert(A_CH % NW == 0 && B_CH % NW == 0, "slice chunks must split over the waves");
@@ -186,7 +187,14 @@ struct DlTile {
     static_assert(!SK || (A_KC && !B_KC && !EX && !CONV), "split-K: the plain product only");
     static_assert(!SK || WTM * WTN <= 64 * 64, "split-K join holds one wave tile of sums");
 
-    static __device__ __forceinline__ int swz(int r) { return SWIZZLE ? (r / RPB) % QPR : 0; }
+    // Quad swizzle of k-contiguous row r.  Rows of at most 256 bytes: the 16
+    // rows of a b128 pass fill one 256-byte bank row each, so each takes a
+    // different quad of it.  Rows of 512 bytes (BK = 128): quads are flipped
+    // within their half by r % 16, so the 16 rows of a pass again cover all
+    // 16 quads of a 256-byte span.
+    static __device__ __forceinline__ int swz(int r) {
+        return SWIZZLE ? (QPR >= 16 ? r % 16 : (r / RPB) % QPR) : 0;
+    }
     // Physical quad of logical quad q in row k of an operand staged [k][mn] is
     // q ^ flip(k).
     static __device__ __forceinline__ int flipA(int k) { return ((k / KPL) & 1) * AFLIP; }
