@@ -899,7 +899,11 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
                         }
                     }
                     if (!masked) {
-                        *(cvec_t*)c = v;
+                        // Non-temporal: C is not read again by this kernel,
+                        // and the hint keeps it from displacing operands in
+                        // the caches (batched 1024 x 128^3: 42.5 -> 41.1 us;
+                        // large products unchanged).
+                        __builtin_nontemporal_store(v, (cvec_t*)c);
                     } else {
 #pragma unroll
                         for (int u = 0; u < T::BV; ++u)
