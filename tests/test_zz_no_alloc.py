@@ -108,3 +108,49 @@ def test_noalloc_rejects_plans_beyond_the_buffer():
     assert st == -10, sg.status_string(st)
     torch.cuda.synchronize()
     assert torch.all(C == SENTINEL)
+
+
+def test_noalloc_in_a_captured_graph():
+    """The callers it is for: two split-K products captured in a HIP graph with
+    no allocation in the graph, replayed three times with eager calls of the
+    same entry point on other shapes in between (one stream, so no overlap);
+    every replay equals the eager results bit for bit."""
+    dev = _dev()
+    gen = torch.Generator(device=dev).manual_seed(23)
+    A1 = torch.randn(200, 3000, device=dev, generator=gen)
+    B1 = torch.randn(3000, 150, device=dev, generator=gen)
+    A2 = torch.randn(64, 5000, device=dev, generator=gen)
+    B2 = torch.randn(5000, 96, device=dev, generator=gen)
+    A3 = torch.randn(130, 2000, device=dev, generator=gen)
+    B3 = torch.randn(2000, 70, device=dev, generator=gen)
+    C1 = torch.empty(200, 150, device=dev)
+    C2 = torch.empty(64, 96, device=dev)
+    C3 = torch.empty(130, 70, device=dev)
+    assert sg.splitk_plan(200, 150, 3000, 6)[1] > 1 and sg.splitk_plan(64, 96, 5000, 4)[1] > 1
+
+    def calls():
+        sg.sgemm_splitk_noalloc(A1, B1, C1, splits=6)
+        sg.sgemm_splitk_noalloc(A2, B2, C2, splits=4)
+
+    calls()  # eager first: the buffer's address is looked up outside capture
+    torch.cuda.synchronize()
+    ref = [C1.clone(), C2.clone()]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    torch.cuda.synchronize()
+    for r in range(3):
+        C1.fill_(float("nan"))
+        C2.fill_(float("nan"))
+        sg.sgemm_splitk_noalloc(A3, B3, C3, splits=5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((C1, C2), ref):
+            assert torch.equal(got.view(torch.int32), want.view(torch.int32)), "replay %d" % r
