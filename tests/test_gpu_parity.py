@@ -87,7 +87,7 @@ def _call(path, *args, **kw):
     return run_gpu(*args, path=path, **kw)
 
 
-ALL_PATHS = ["valu"] + ["cfg%d" % i for i in range(33)]
+ALL_PATHS = ["valu"] + ["cfg%d" % i for i in range(34)]
 
 
 @pytest.mark.parametrize("path", ALL_PATHS)

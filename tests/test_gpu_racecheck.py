@@ -65,7 +65,7 @@ SHAPES = [(256, 256, 256, 256, 256, 256, 1),
           (64, 640, 513, 515, 640, 641, 1),
           (130, 70, 1000, 1003, 70, 75, 1),
           (65, 63, 150, 151, 65, 66, 3)]
-PATHS = ["valu"] + ["cfg%d" % i for i in range(33)]
+PATHS = ["valu"] + ["cfg%d" % i for i in range(34)]
 
 
 def test_every_config_is_covered():
