@@ -764,36 +764,82 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     // k groups 1..KSPLIT-1 hand their partial sums to group 0 through LDS
     // (lane-contiguous 16-byte records, conflict-free); group 0 adds them in
     // group order, so the result does not depend on timing.
-    // With four or more k groups (and no split-K join after) the adding and
-    // the stores are shared: every group writes its records, and group g sums
-    // the accumulator rows r in [g, g + 1) * ACC / KSPLIT over all groups, in
-    // the same group order 0, 1, ... (the same FP32 operations, so the same
-    // bits), and stores those rows: 1024^3 on the 64 x 64 x 128 tile with four
-    // k groups, 19.95 -> 19.69 us (with two groups it measured 0.5 % slower,
-    // and stays with group 0).
-    constexpr bool SHARED_EXCHANGE = T::KSPLIT >= 4 && !T::SK &&
-                                     Op::ACC % (4 * T::KSPLIT) == 0 &&
-                                     T::KSPLIT * T::BM * T::BN <= T::STAGES * T::BUF_FLOATS;
+    // With four or more k groups the adding and the stores are shared: every
+    // group writes its records, and group g sums the accumulator rows r in
+    // [g, g + 1) * ACC / KSPLIT over all groups, in the same group order
+    // 0, 1, ... (the same FP32 operations, so the same bits), and stores
+    // those rows: 1024^3 on the 64 x 64 x 128 tile with four k groups,
+    // 19.95 -> 19.69 us (with two groups it measured 0.5 % slower, and stays
+    // with group 0).  Split-K shares the partial tile and the join the same
+    // way (SK_SHARED, below).
+    constexpr bool SHARED_ROWS = T::KSPLIT >= 4 && Op::ACC % (4 * T::KSPLIT) == 0 &&
+                                 T::KSPLIT * T::BM * T::BN <= T::STAGES * T::BUF_FLOATS;
+    constexpr bool SHARED_EXCHANGE = SHARED_ROWS && !T::SK;
+    constexpr bool SK_SHARED = SHARED_ROWS && T::SK;
+    constexpr int NACC = T::TM * T::TN * Op::ACC;  // accumulator values per lane
+    static_assert(T::KSPLIT == 1 || NACC % 4 == 0, "whole 16-byte records");
+    // Record q of a wave holds its accumulator values f = 4q .. 4q + 3,
+    // f = (mi * TN + ni) * ACC + r, lane l's at 4 * (q * 64 + l) of `dst`.
+    auto write_records = [&](float* const dst) {
+#pragma unroll
+        for (int q = 0; q < NACC / 4; ++q) {
+            f32x4 v;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int f = 4 * q + c;
+                v[c] = acc[f / (T::TN * Op::ACC)][(f / Op::ACC) % T::TN][f % Op::ACC];
+            }
+            *(f32x4*)(dst + 4 * (q * 64 + lane)) = v;
+        }
+    };
+    // Split-K join.  Each workgroup writes its partial tile to the workspace
+    // and counts itself in on the tile's counter; the workgroup that arrives
+    // last adds every split's partial in split order 0, 1, ... (so the sum
+    // does not depend on which split finished last), resets the counter for
+    // the next call and stores the tile.  No workgroup waits for another.
+    // Ordering rests on how gfx950 (a member of the GFX942 family in LLVM's
+    // AMDGPU memory model) performs relaxed device-scope atomics, not on
+    // C++ release/acquire: the model maps relaxed agent-scope atomic stores
+    // and loads of global memory to global_store / global_load with the sc1
+    // bit (performed coherently across the XCDs' L2 caches) and atomic RMWs
+    // to global_atomic at the device's coherence point.  Every partial is
+    // such a store; s_waitcnt vmcnt(0) holds each wave until its stores are
+    // acknowledged, the barrier holds lane 0 until every wave has done so,
+    // and only then does lane 0 increment the counter.  The last arriver
+    // sees every other increment, so every partial was complete before its
+    // own increment returned, and its sc1 loads issue after that return.
+    // A device-scope release on the increment and an acquire fence after it
+    // would state the same order in the language's model, but on gfx950
+    // they write back and invalidate the XCD's whole L2 per workgroup (the
+    // operand tiles of every other workgroup on it included): measured at
+    // 1024^3 with 4 chunks, 24.6 -> 53.7 us per product; at 512x4096x4096
+    // with 8 chunks, 154 -> 172 us.
+    // sk_arrive: once every wave's partial stores are acknowledged, lane 0
+    // counts the workgroup in on the tile's counter; returns whether it
+    // arrived last.  The flag goes in LDS word 0: every wave's reads of the
+    // slices and records end before the first barrier here.
+    auto sk_arrive = [&](int tile) {
+        int* const sk_last = (int*)smem;
+        wait_vmcnt<0>();
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t before = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+            const int last = before == (uint32_t)p.splits - 1;
+            if (last)
+                __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            *sk_last = last;
+        }
+        __syncthreads();
+        return *sk_last != 0;
+    };
     if constexpr (SHARED_EXCHANGE) {
-        constexpr int NACC = T::TM * T::TN * Op::ACC;
         constexpr int RQ = Op::ACC / T::KSPLIT;  // accumulator rows per group
         lds_barrier();  // every wave is done reading the slices
-        {
-            float* const dst = smem + (kgrp * T::NWMN + wave_mn) * 64 * NACC;
-#pragma unroll
-            for (int q = 0; q < NACC / 4; ++q) {
-                f32x4 v;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int f = 4 * q + c;
-                    v[c] = acc[f / (T::TN * Op::ACC)][(f / Op::ACC) % T::TN][f % Op::ACC];
-                }
-                *(f32x4*)(dst + 4 * (q * 64 + lane)) = v;
-            }
-        }
+        write_records(smem + (kgrp * T::NWMN + wave_mn) * 64 * NACC);
         lds_barrier();
-        // Group G's rows, summed in group order; record q of a wave holds
-        // accumulator values f = 4q .. 4q + 3, f = (mi * TN + ni) * ACC + r.
+        // Group G's rows, summed in group order.
         auto sum_rows = [&](auto gtag) {
             constexpr int G = decltype(gtag)::value;
 #pragma unroll
@@ -824,23 +870,101 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
                     }
         };
         for_group<0, T::KSPLIT>(kgrp, sum_rows);
-    } else if constexpr (T::KSPLIT > 1) {
-        constexpr int NACC = T::TM * T::TN * Op::ACC;
-        static_assert(NACC % 4 == 0, "whole 16-byte records");
+    } else if constexpr (SK_SHARED) {
+        // Split-K with shared rows: group g sums its rows over the k groups,
+        // writes them as its part of the partial tile, and in the workgroup
+        // that arrives last adds them over the splits and stores them.
+        constexpr int RQ = Op::ACC / T::KSPLIT;  // accumulator rows per group
+        constexpr int NQ = T::TM * T::TN * RQ;   // values per lane of a group's rows
+        constexpr int TILE = T::BM * T::BN;
         lds_barrier();  // every wave is done reading the slices
-        if (kgrp > 0) {
-            float* const dst = smem + ((kgrp - 1) * T::NWMN + wave_mn) * 64 * NACC;
+        write_records(smem + (kgrp * T::NWMN + wave_mn) * 64 * NACC);
+        lds_barrier();
+        // All terms are read back from the records (the group's own
+        // included), so no accumulator is picked by the run-time group index
+        // (which would move the accumulators to scratch memory).
+        float part[NQ];
 #pragma unroll
-            for (int q = 0; q < NACC / 4; ++q) {
-                f32x4 v;
+        for (int mi = 0; mi < T::TM; ++mi)
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const int f = 4 * q + c;
-                    v[c] = acc[f / (T::TN * Op::ACC)][(f / Op::ACC) % T::TN][f % Op::ACC];
+            for (int ni = 0; ni < T::TN; ++ni)
+#pragma unroll
+                for (int q4 = 0; q4 < RQ / 4; ++q4) {
+                    const int q = ((mi * T::TN + ni) * Op::ACC + kgrp * RQ) / 4 + q4;
+                    f32x4 sum = *(const f32x4*)(smem + wave_mn * 64 * NACC + 4 * (q * 64 + lane));
+#pragma unroll
+                    for (int j = 1; j < T::KSPLIT; ++j)
+                        sum += *(const f32x4*)(smem + (j * T::NWMN + wave_mn) * 64 * NACC +
+                                               4 * (q * 64 + lane));
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) part[(mi * T::TN + ni) * RQ + 4 * q4 + c] = sum[c];
                 }
-                *(f32x4*)(dst + 4 * (q * 64 + lane)) = v;
+        // The partial tile of a split: value j (= (mi * TN + ni) * RQ + r)
+        // of lane l of wave (kgrp, wave_mn) at ((kgrp * NWMN + wave_mn) * NQ
+        // + j) * 64 + l, so each store or load covers 256 contiguous bytes.
+        const int tile = tc.tm * p.tiles_n + tc.tn;
+        float* const slot0 = p.ws + (int64_t)tile * p.splits * TILE +
+                             (kgrp * T::NWMN + wave_mn) * 64 * NQ + lane;
+        {
+            float* const dst = slot0 + (int64_t)tc.b * TILE;
+#pragma unroll
+            for (int j = 0; j < NQ; ++j)
+                __hip_atomic_store(dst + j * 64, part[j], __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (!sk_arrive(tile)) return;
+        // Sums over the splits in split order; the loads of up to four
+        // splits go out together (splits past the last repeat the last one's
+        // loads, whose values are not added).
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) part[j] = 0.0f;
+#pragma unroll 1
+        for (int sp0 = 0; sp0 < p.splits; sp0 += 4) {
+            float v[4][NQ];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float* const src = slot0 + (int64_t)min(sp0 + u, p.splits - 1) * TILE;
+#pragma unroll
+                for (int j = 0; j < NQ; ++j)
+                    v[u][j] = __hip_atomic_load(src + j * 64, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool in = sp0 + u < p.splits;
+#pragma unroll
+                for (int j = 0; j < NQ; ++j) part[j] = in ? part[j] + v[u][j] : part[j];
             }
         }
+        // The group's rows of C, as in the epilogue below with the rows
+        // taken at run time.
+        typedef float svec_t __attribute__((ext_vector_type(T::BV), aligned(4)));
+#pragma unroll
+        for (int mi = 0; mi < T::TM; ++mi)
+#pragma unroll
+            for (int h = 0; h < NBV; ++h) {
+                const int col = wx * T::WTN + T::bcol(h * T::BV, li);
+#pragma unroll
+                for (int r = 0; r < RQ; ++r) {
+                    const int row = wy * T::WTM + T::arow(mi, Op::row(kgrp * RQ + r, lg));
+                    float* const c = C + (int64_t)row * p.ldc + col;
+                    svec_t v;
+#pragma unroll
+                    for (int u = 0; u < T::BV; ++u)
+                        v[u] = part[(mi * T::TN + h * T::BV + u) * RQ + r];
+                    if (full_mn) {
+                        __builtin_nontemporal_store(v, (svec_t*)c);
+                    } else {
+#pragma unroll
+                        for (int u = 0; u < T::BV; ++u)
+                            if (row < rows_left && col + u < cols_left) c[u] = v[u];
+                    }
+                }
+            }
+        return;
+    } else if constexpr (T::KSPLIT > 1) {
+        lds_barrier();  // every wave is done reading the slices
+        if (kgrp > 0) write_records(smem + ((kgrp - 1) * T::NWMN + wave_mn) * 64 * NACC);
         lds_barrier();
         // (Split-K: every wave takes part in the join's barriers below.)
         if (kgrp > 0 && !T::SK) return;
@@ -859,36 +983,11 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
         }
     }
 
-    // Split-K join.  Each workgroup writes its partial tile to the workspace
-    // and counts itself in on the tile's counter; the workgroup that arrives
-    // last adds every split's partial in split order 0, 1, ... (so the sum
-    // does not depend on which split finished last), resets the counter for
-    // the next call and stores the tile.  No workgroup waits for another.
-    // Ordering rests on how gfx950 (a member of the GFX942 family in LLVM's
-    // AMDGPU memory model) performs relaxed device-scope atomics, not on
-    // C++ release/acquire: the model maps relaxed agent-scope atomic stores
-    // and loads of global memory to global_store / global_load with the sc1
-    // bit (performed coherently across the XCDs' L2 caches) and atomic RMWs
-    // to global_atomic at the device's coherence point.  Every partial is
-    // such a store; s_waitcnt vmcnt(0) holds each wave until its stores are
-    // acknowledged, the barrier holds lane 0 until every wave has done so,
-    // and only then does lane 0 increment the counter.  The last arriver
-    // sees every other increment, so every partial was complete before its
-    // own increment returned, and its sc1 loads issue after that return.
-    // A device-scope release on the increment and an acquire fence after it
-    // would state the same order in the language's model, but on gfx950
-    // they write back and invalidate the XCD's whole L2 per workgroup (the
-    // operand tiles of every other workgroup on it included): measured at
-    // 1024^3 with 4 chunks, 24.6 -> 53.7 us per product; at 512x4096x4096
-    // with 8 chunks, 154 -> 172 us.  Record layout: value f of lane l at
-    // f * 64 + l, so each store or load instruction covers 256 contiguous
-    // bytes.
-    if constexpr (T::SK) {
-        constexpr int NACC = T::TM * T::TN * Op::ACC;
+    // Split-K join with the tile's sums in k group 0 (record layout: value
+    // f of lane l at f * 64 + l, so each store or load instruction covers
+    // 256 contiguous bytes).
+    if constexpr (T::SK && !SK_SHARED) {
         constexpr int TILE = T::BM * T::BN;
-        // The last-arrival flag goes in LDS word 0: every wave's reads of
-        // the slices and of the k-group exchange end before the barrier below.
-        int* const sk_last = (int*)smem;
         const bool holds = T::KSPLIT == 1 || kgrp == 0;  // waves with the tile's sums
         const int tile = tc.tm * p.tiles_n + tc.tn;
         float* const slot0 = p.ws + (int64_t)tile * p.splits * TILE + wave_mn * 64 * NACC + lane;
@@ -900,19 +999,7 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
                                    acc[f / (T::TN * Op::ACC)][(f / Op::ACC) % T::TN][f % Op::ACC],
                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        wait_vmcnt<0>();
-        __syncthreads();
-        if (tid == 0) {
-            const uint32_t before = __hip_atomic_fetch_add(p.counters + tile, 1u, __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT);
-            const int last = before == (uint32_t)p.splits - 1;
-            if (last)
-                __hip_atomic_store(p.counters + tile, 0u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            *sk_last = last;
-        }
-        __syncthreads();
-        if (!*sk_last || !holds) return;
+        if (!sk_arrive(tile) || !holds) return;
         float sum[NACC];
 #pragma unroll
         for (int f = 0; f < NACC; ++f) sum[f] = 0.0f;
