@@ -42,7 +42,9 @@ METRIC = "FP32 GEMM TFLOP/s at M=N=K=4096 on 1 MI355X; % of FP32 peak"
 PEAK_FP32_TFLOPS = 157.3      # MI355X dense FP32 (vector and matrix)
 PEAK_HBM_GBS = 8000.0
 CSRC = os.path.join(ROOT, "tiled_fp32_gemm_sgemm_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sgemm_mfma_square4096_counters.txt")
+def gemm_traffic_file(path: str, workload: str) -> str:
+    """The committed counter summary of a GEMM workload on a path."""
+    return os.path.join(ROOT, "profiles", "sgemm_%s_%s_counters.txt" % (path, workload))
 COPY_BYTES = 512 * 1024 * 1024   # larger than the 256 MB last-level cache
 GEMM_WORK_S = 0.1                # default warm-up and timed work per GEMM phase (s)
 SETTLE_S = 0.1                   # GEMM launches before the warm-up steps (clock settle)
@@ -79,9 +81,10 @@ def kernel_source_hash(names=GEMM_SOURCES) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(path: str, names=GEMM_SOURCES, tile=None):
+def read_traffic(path: str, names=GEMM_SOURCES, tile=None, chunks=None):
     """HBM bytes per launch from a committed counter summary, or None when it
-    is missing, was taken on a different kernel source or on another tile."""
+    is missing, was taken on a different kernel source, on another tile or
+    (split-K) with another chunk count."""
     if not os.path.exists(path):
         return None
     vals = {}
@@ -94,6 +97,8 @@ def read_traffic(path: str, names=GEMM_SOURCES, tile=None):
         return None
     if tile is not None and not vals.get("mfma_instructions_closed_form", "").endswith(
             "(tile %s)" % tile):
+        return None
+    if chunks is not None and vals.get("splitk_chunks", "").split()[:1] != [str(chunks)]:
         return None
     try:
         return float(vals["beyond_l2_bytes_per_launch"].split()[0])
@@ -1088,10 +1093,17 @@ def main(argv=None) -> int:
     else:
         tile = "valu_128x128x8_t8x8"
 
-    # The counter summary was taken with warm caches.
-    traffic = (read_traffic(TRAFFIC_FILE, GEMM_SOURCES, tile)
-               if args.path == "mfma" and args.workload == "square4096" and args.config is None
-               and not args.cold else None)
+    # Each workload's counter summary was taken with warm caches on the tile
+    # the time model chooses; it counts only for that tile (and chunk count).
+    traffic = None
+    if not args.cold:
+        f = gemm_traffic_file(args.path, args.workload)
+        if args.path == "splitk":
+            traffic = read_traffic(f, GEMM_SOURCES, sg.config_info(sk_config)["name"], sk_splits)
+        elif args.path == "mfma":
+            traffic = read_traffic(f, GEMM_SOURCES, tile)
+        else:
+            traffic = read_traffic(f, GEMM_SOURCES)
     roofline = {"bound": "alu" if args.path == "valu" else "mfma",
                 "achieved": tflops,
                 "peak": PEAK_FP32_TFLOPS,

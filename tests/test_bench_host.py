@@ -34,6 +34,30 @@ def test_traffic_only_for_the_same_kernel_source_and_tile(tmp_path):
     assert bench.read_traffic(str(tmp_path / "missing.txt")) is None
 
 
+def test_traffic_of_a_split_needs_the_same_chunk_count(tmp_path):
+    h = bench.kernel_source_hash()
+    tile = "dl32_64x64x128_w2x1_s2_k4"
+    p = tmp_path / "counters.txt"
+    p.write_text("kernel_source_sha256_16: %s\n"
+                 "splitk_chunks: 4\n"
+                 "mfma_instructions_closed_form: 1048576 (tile %s)\n"
+                 "beyond_l2_bytes_per_launch: 59909651\n" % (h, tile))
+    assert bench.read_traffic(str(p), tile=tile, chunks=4) == 59909651.0
+    assert bench.read_traffic(str(p), tile=tile, chunks=8) is None
+
+
+def test_every_committed_gemm_summary_is_found_by_its_workload():
+    import os
+    for path, workload in [("mfma", "square4096"), ("mfma", "square1024"), ("mfma", "tall"),
+                           ("mfma", "ragged"), ("mfma", "shard512"), ("mfma", "batched128"),
+                           ("splitk", "longk512"), ("valu", "square4096")]:
+        f = bench.gemm_traffic_file(path, workload)
+        assert os.path.exists(f), f
+        with open(f) as fh:
+            text = fh.read()
+        assert "beyond_l2_bytes_per_launch:" in text and "kernel_source_sha256_16:" in text, f
+
+
 def test_source_hash_depends_on_every_listed_file(tmp_path, monkeypatch):
     for name in ("a.hpp", "b.hpp"):
         (tmp_path / name).write_text("int %s;\n" % name[0])
