@@ -240,7 +240,12 @@ int sgemm_autotune(int64_t M, int64_t N, int64_t K, const float *A, int64_t lda,
  * its partial to the workspace and counts itself in on the tile's counter;
  * the last one to arrive adds the partials in chunk order 0, 1, ... (so the
  * result does not depend on timing and is bit-reproducible), resets the
- * counter and stores the tile.  No workgroup waits for another.
+ * counter and stores the tile.  No workgroup waits for another.  With
+ * splits = 0 the plan may be hybrid: when the tile count is not a multiple of
+ * the 256 CUs, the tiles of the whole layers (one tile per CU each) take all
+ * of K and only the R tiles of the last partial layer are split, so that
+ * their chunks even out the work per CU ("Tiling Strategies" section 4 on
+ * tail effects; sgemm_splitk_plan_full_tiles reports the unsplit tiles).
  *
  * config: a configuration with a split-K variant (sgemm_config_has_splitk),
  *   or -1 for the choice of the time model (which may be the plain kernel).
@@ -305,6 +310,14 @@ int sgemm_splitk_noalloc(int config, int64_t M, int64_t N, int64_t K, const floa
  */
 int64_t sgemm_splitk_plan(int config, int64_t M, int64_t N, int64_t K, int64_t splits,
                           int *plan_config, int64_t *plan_splits);
+
+/*
+ * For the plan sgemm_splitk would run with these arguments: the number of
+ * output tiles that take all of K without a join (0 when every tile is split
+ * or the plan is the plain kernel), or a negative status.  Host only.
+ */
+int64_t sgemm_splitk_plan_full_tiles(int config, int64_t M, int64_t N, int64_t K,
+                                     int64_t splits);
 
 /* 1 if configuration `config` has a split-K variant, 0 if not,
    SGEMM_STATUS_INVALID_CONFIG if unknown.  Host only. */

@@ -255,3 +255,46 @@ def test_square1024_splitk_full(name):
             parity.assert_bitwise(got, ref, what)
         else:
             parity.assert_within_tolerance(got, ref, mag, what)
+
+
+# Shapes whose automatic plan is hybrid (whole layers of 256 tiles take all
+# of K, the last partial layer is split), on four different tiles; odd
+# leading dimensions and a ragged tile row and column.
+HYBRID = [(3300, 300, 1000, 1001, 301, 307), (3456, 301, 1501, 1503, 305, 301),
+          (2486, 903, 1501, 1501, 907, 910), (3262, 701, 1501, 1505, 701, 703)]
+
+
+@pytest.mark.parametrize("shape", HYBRID, ids=lambda s: "x".join(map(str, s[:3])))
+def test_hybrid_plan_bitwise(shape):
+    M, N, K, lda, ldb, ldc = shape
+    full = sg.splitk_plan_full_tiles(M, N, K)
+    cfg, splits, nbytes = sg.splitk_plan(M, N, K)
+    bm, bn, _ = _tile(cfg)
+    tiles = -(-M // bm) * -(-N // bn)
+    assert full > 0 and full % 256 == 0 and full < tiles and splits > 1, (full, cfg, splits)
+    assert nbytes == sg.SPLITK_HEADER_BYTES + (tiles - full) * splits * bm * bn * 4
+    A, B = operands(M, N, K, lda, ldb, seed=M + 3 * N + K, dist_a="int4")
+    got, ws, plan = run_splitk(M, N, K, A, lda, B, ldb, ldc, -1, 0)
+    assert plan == (cfg, splits)
+    ref, _, _ = oracle.sgemm_f64(M, N, K, A.numpy(), lda, B.numpy(), ldb)
+    parity.assert_bitwise(got, ref, "hybrid %s cfg%d splits=%d" % (shape, cfg, splits))
+    # Again on the same workspace, and through the race-check build (reversed
+    # block order, poisoned LDS).
+    again, _, _ = run_splitk(M, N, K, A, lda, B, ldb, ldc, -1, 0, ws=ws)
+    assert np.array_equal(got, again)
+    rc, _, _ = run_splitk(M, N, K, A, lda, B, ldb, ldc, -1, 0, lib=_native.racecheck_lib())
+    parity.assert_bitwise(rc, ref, "racecheck hybrid %s" % (shape,))
+
+
+def test_hybrid_real_valued_matches_across_calls_and_tolerance():
+    """Normal-like data on a hybrid plan: bit-identical when repeated, and
+    within the parity bound on every entry."""
+    M, N, K = 3300, 300, 1000
+    assert sg.splitk_plan_full_tiles(M, N, K) > 0
+    A, B = operands(M, N, K, K, N, seed=77, dist_a="normal", scale_a=K ** -0.5,
+                    scale_b=K ** -0.5)
+    got, ws, _ = run_splitk(M, N, K, A, K, B, N, N, -1, 0)
+    again, _, _ = run_splitk(M, N, K, A, K, B, N, N, -1, 0, ws=ws)
+    assert np.array_equal(got.view(np.int32), again.view(np.int32))
+    ref, mag, _ = oracle.sgemm_f64(M, N, K, A.numpy(), K, B.numpy(), N)
+    parity.assert_within_tolerance(got, ref, mag, "hybrid real-valued")

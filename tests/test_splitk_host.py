@@ -116,3 +116,21 @@ def test_noalloc_argument_errors_enqueue_nothing():
     assert sg.splitk_plan(4096, 4096, 8192, 8, cfg)[2] > 64 * 1024 * 1024
     assert call(**big) == -10
     assert "scratch" in sg.status_string(-10)
+
+
+def test_hybrid_plan_splits_only_the_last_partial_layer():
+    """12544 x 256 x 2304 on 64 x 64 tiles: 784 tiles = 3 layers of 256 and
+    16 more.  The automatic plan runs the 768 as whole tiles and splits the 16,
+    so the workspace holds only their chunks."""
+    M, N, K = 12544, 256, 2304
+    cfg, splits, nbytes = sg.splitk_plan(M, N, K)
+    full = sg.splitk_plan_full_tiles(M, N, K)
+    info = sg.config_info(cfg)
+    tiles = -(-M // info["bm"]) * -(-N // info["bn"])
+    assert full == tiles - tiles % 256 and 0 < full < tiles
+    assert splits > 1 and ((tiles - full) * splits) % 8 == 0
+    assert nbytes == sg.SPLITK_HEADER_BYTES + (tiles - full) * splits * info["bm"] * info["bn"] * 4
+    # An explicit chunk count splits every tile; whole layers never go hybrid.
+    assert sg.splitk_plan_full_tiles(M, N, K, 4, cfg) == 0
+    assert sg.splitk_plan_full_tiles(12288, 256, 2304) == 0
+    assert sg.splitk_plan_full_tiles(512, 512, 8192) == 0

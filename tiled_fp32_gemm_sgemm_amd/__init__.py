@@ -12,7 +12,8 @@ from .api import (SPLITK_HEADER_BYTES, SPLITK_MAX_TILES, attention, attention_ra
                   conv2d_select_config,
                   config_selectable, num_configs, predict_us, select_config,
                   select_general_config, sgemm, sgemm_ex, sgemm_ex_raw, sgemm_raw,
-                  config_has_splitk, sgemm_splitk, sgemm_splitk_noalloc, splitk_plan, splitk_workspace,
+                  config_has_splitk, sgemm_splitk, sgemm_splitk_noalloc, splitk_plan,
+                  splitk_plan_full_tiles, splitk_workspace,
                   sgemm_strided_batched, sgemm_strided_batched_raw, window_sum,
                   window_sum_raw, workgroups_per_cu)
 from ._native import SgemmError, status_string
@@ -23,6 +24,7 @@ __all__ = ["sgemm", "sgemm_strided_batched", "sgemm_raw", "sgemm_strided_batched
            "select_general_config", "window_sum", "window_sum_raw", "conv2d_nhwc",
            "conv2d_nhwc_raw", "conv2d_output_size", "conv2d_config_available",
            "conv2d_select_config", "workgroups_per_cu", "attention", "attention_raw",
-           "sgemm_splitk", "sgemm_splitk_noalloc", "splitk_plan", "splitk_workspace", "config_has_splitk",
+           "sgemm_splitk", "sgemm_splitk_noalloc", "splitk_plan", "splitk_plan_full_tiles",
+           "splitk_workspace", "config_has_splitk",
            "SPLITK_HEADER_BYTES", "SPLITK_MAX_TILES", "SgemmError",
            "status_string"]

@@ -131,6 +131,15 @@ def splitk_plan(M: int, N: int, K: int, splits: int = 0, config=None):
     return cfg.value, sp.value, int(st)
 
 
+def splitk_plan_full_tiles(M: int, N: int, K: int, splits: int = 0, config=None) -> int:
+    """Output tiles of sgemm_splitk's plan that take all of K with no join."""
+    st = _native.lib().sgemm_splitk_plan_full_tiles(-1 if config is None else int(config), M, N,
+                                                    K, int(splits))
+    if st < 0:
+        raise _native.SgemmError(int(st), "sgemm_splitk_plan_full_tiles")
+    return int(st)
+
+
 def config_has_splitk(config: int) -> bool:
     st = _native.lib().sgemm_config_has_splitk(int(config))
     if st < 0:

@@ -291,7 +291,18 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     using Op = MfmaOp<T::MI>;
     __shared__ __attribute__((aligned(16))) float smem[T::STAGES * T::BUF_FLOATS];
 
-    const TileCoord tc = map_block(p, T::GROUP_M);
+    // Split-K: the tile, the chunk (tc.b) and whether the tile is split.
+    TileCoord tc;
+    int sk_tail = 0;
+    bool sk_full = false;
+    if constexpr (T::SK) {
+        const SplitCoord sc = map_split_block(p, T::GROUP_M);
+        tc = sc.tc;
+        sk_tail = sc.tail;
+        sk_full = sc.full;
+    } else {
+        tc = map_block(p, T::GROUP_M);
+    }
     const int m0 = tc.tm * T::BM;
     const int n0 = tc.tn * T::BN;
     // Tile origin in each stored operand (element offsets); k advances along
@@ -309,7 +320,7 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     const int cols_left = p.N - n0;
     const bool full_mn = rows_left >= T::BM && cols_left >= T::BN;
     // The k range this workgroup reduces: all of K, or one split's part.
-    const int Kd = T::SK ? min(p.kchunk, p.K - tc.b * p.kchunk) : p.K;
+    const int Kd = T::SK && !sk_full ? min(p.kchunk, p.K - tc.b * p.kchunk) : p.K;
     const int nslices = (Kd + T::BK - 1) / T::BK;
 
     const int tid = threadIdx.x;
@@ -902,38 +913,40 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
         // The partial tile of a split: value j (= (mi * TN + ni) * RQ + r)
         // of lane l of wave (kgrp, wave_mn) at ((kgrp * NWMN + wave_mn) * NQ
         // + j) * 64 + l, so each store or load covers 256 contiguous bytes.
-        const int tile = tc.tm * p.tiles_n + tc.tn;
-        float* const slot0 = p.ws + (int64_t)tile * p.splits * TILE +
-                             (kgrp * T::NWMN + wave_mn) * 64 * NQ + lane;
-        {
-            float* const dst = slot0 + (int64_t)tc.b * TILE;
-#pragma unroll
-            for (int j = 0; j < NQ; ++j)
-                __hip_atomic_store(dst + j * 64, part[j], __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (!sk_arrive(tile)) return;
-        // Sums over the splits in split order; the loads of up to four
-        // splits go out together (splits past the last repeat the last one's
-        // loads, whose values are not added).
-#pragma unroll
-        for (int j = 0; j < NQ; ++j) part[j] = 0.0f;
-#pragma unroll 1
-        for (int sp0 = 0; sp0 < p.splits; sp0 += 4) {
-            float v[4][NQ];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const float* const src = slot0 + (int64_t)min(sp0 + u, p.splits - 1) * TILE;
+        if (!sk_full) {
+            const int tile = sk_tail;
+            float* const slot0 = p.ws + (int64_t)tile * p.splits * TILE +
+                                 (kgrp * T::NWMN + wave_mn) * 64 * NQ + lane;
+            {
+                float* const dst = slot0 + (int64_t)tc.b * TILE;
 #pragma unroll
                 for (int j = 0; j < NQ; ++j)
-                    v[u][j] = __hip_atomic_load(src + j * 64, __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(dst + j * 64, part[j], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             }
+            if (!sk_arrive(tile)) return;
+            // Sums over the splits in split order; the loads of up to four
+            // splits go out together (splits past the last repeat the last one's
+            // loads, whose values are not added).
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const bool in = sp0 + u < p.splits;
+            for (int j = 0; j < NQ; ++j) part[j] = 0.0f;
+#pragma unroll 1
+            for (int sp0 = 0; sp0 < p.splits; sp0 += 4) {
+                float v[4][NQ];
 #pragma unroll
-                for (int j = 0; j < NQ; ++j) part[j] = in ? part[j] + v[u][j] : part[j];
+                for (int u = 0; u < 4; ++u) {
+                    const float* const src = slot0 + (int64_t)min(sp0 + u, p.splits - 1) * TILE;
+#pragma unroll
+                    for (int j = 0; j < NQ; ++j)
+                        v[u][j] = __hip_atomic_load(src + j * 64, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const bool in = sp0 + u < p.splits;
+#pragma unroll
+                    for (int j = 0; j < NQ; ++j) part[j] = in ? part[j] + v[u][j] : part[j];
+                }
             }
         }
         // The group's rows of C, as in the epilogue below with the rows
@@ -989,30 +1002,37 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     if constexpr (T::SK && !SK_SHARED) {
         constexpr int TILE = T::BM * T::BN;
         const bool holds = T::KSPLIT == 1 || kgrp == 0;  // waves with the tile's sums
-        const int tile = tc.tm * p.tiles_n + tc.tn;
-        float* const slot0 = p.ws + (int64_t)tile * p.splits * TILE + wave_mn * 64 * NACC + lane;
-        if (holds) {
-            float* const dst = slot0 + (int64_t)tc.b * TILE;
+        // A tile that takes all of K has its sums in k group 0 already.
+        if (sk_full && !holds) return;
+        if (!sk_full) {
+            const int tile = sk_tail;
+            float* const slot0 =
+                p.ws + (int64_t)tile * p.splits * TILE + wave_mn * 64 * NACC + lane;
+            if (holds) {
+                float* const dst = slot0 + (int64_t)tc.b * TILE;
 #pragma unroll
-            for (int f = 0; f < NACC; ++f)
-                __hip_atomic_store(dst + f * 64,
-                                   acc[f / (T::TN * Op::ACC)][(f / Op::ACC) % T::TN][f % Op::ACC],
-                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (!sk_arrive(tile) || !holds) return;
-        float sum[NACC];
+                for (int f = 0; f < NACC; ++f)
+                    __hip_atomic_store(
+                        dst + f * 64,
+                        acc[f / (T::TN * Op::ACC)][(f / Op::ACC) % T::TN][f % Op::ACC],
+                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            if (!sk_arrive(tile) || !holds) return;
+            float sum[NACC];
 #pragma unroll
-        for (int f = 0; f < NACC; ++f) sum[f] = 0.0f;
+            for (int f = 0; f < NACC; ++f) sum[f] = 0.0f;
 #pragma unroll 1
-        for (int sp = 0; sp < p.splits; ++sp) {
-            const float* const src = slot0 + (int64_t)sp * TILE;
+            for (int sp = 0; sp < p.splits; ++sp) {
+                const float* const src = slot0 + (int64_t)sp * TILE;
+#pragma unroll
+                for (int f = 0; f < NACC; ++f)
+                    sum[f] += __hip_atomic_load(src + f * 64, __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT);
+            }
 #pragma unroll
             for (int f = 0; f < NACC; ++f)
-                sum[f] += __hip_atomic_load(src + f * 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                acc[f / (T::TN * Op::ACC)][(f / Op::ACC) % T::TN][f % Op::ACC] = sum[f];
         }
-#pragma unroll
-        for (int f = 0; f < NACC; ++f)
-            acc[f / (T::TN * Op::ACC)][(f / Op::ACC) % T::TN][f % Op::ACC] = sum[f];
     }
 
     // Epilogue: accumulator r of lane (li, lg) in MFMA tile (mi, ni) is

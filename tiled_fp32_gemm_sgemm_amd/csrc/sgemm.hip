@@ -460,6 +460,10 @@ int run_mfma(int config, int64_t M, int64_t N, int64_t K, const float* A, int64_
 // Split-K: the k range is cut into `splits` chunks of whole BK slices, each
 // reduced by its own workgroup per output tile; the partial tiles join in the
 // kernel (the last workgroup of a tile to arrive adds them in split order).
+// A hybrid plan splits only the tiles past the last whole layer of one tile
+// per CU: the first F = tiles - tiles % 256 take all of K with no join, and
+// the chunks of the other R tiles fill one more layer, so every CU gets F / 256
+// tiles plus about one chunk instead of some CUs one tile more than others.
 // Workspace: a header of kSplitMaxTiles uint32 arrival counters, counter t
 // for output tile t whatever the shape, then splits * BM * BN floats per
 // tile.  The header's place and size do not depend on the call, so the zeros
@@ -476,12 +480,21 @@ constexpr int64_t kSplitHeaderBytes = kSplitMaxTiles * 4;
 // 2048^3) the plan lands on the measured fastest choice or within 5 % of it.
 constexpr double kJoinBytesPerUs = 4.0e6;
 constexpr double kJoinFixedUs = 2.0;
+// Hybrid plans: a chunk workgroup pays about kHybridChunkUs beyond its
+// slices (first-slice latency, k-group exchange, partial write and arrival),
+// and the join on the launch's tail path kHybridJoinUs.  Set so that on
+// 12544 x 256 x 2304, 50176 x 128 x 1152, 12544 x 512 x 4608 (hybrid 8-23 %
+// faster) and 3000 x 2000 x 1000, 2100 x 1000 x 1000 (2-8 % slower) the plan
+// takes the faster kind.
+constexpr double kHybridChunkUs = 3.0;
+constexpr double kHybridJoinUs = 3.0;
 
 struct SplitPlan {
-    int config;        // tile configuration
-    int64_t splits;    // effective number of k chunks (1: the plain kernel)
-    int64_t kchunk;    // k values per chunk, a multiple of BK
-    int64_t ws_bytes;  // workspace needed (0 when splits == 1)
+    int config;          // tile configuration
+    int64_t splits;      // effective number of k chunks (1: the plain kernel)
+    int64_t kchunk;      // k values per chunk, a multiple of BK
+    int64_t ws_bytes;    // workspace needed (0 when splits == 1)
+    int64_t full_tiles;  // hybrid: tiles that take all of K (0: every tile splits)
 };
 
 SplitPlan make_split_plan(const ConfigEntry& c, int config, int64_t M, int64_t N, int64_t K,
@@ -496,15 +509,67 @@ SplitPlan make_split_plan(const ConfigEntry& c, int config, int64_t M, int64_t N
     sp.kchunk = (slices > 0 ? ceil_div(slices, s) : 1) * c.bk;
     sp.splits = K > 0 ? ceil_div(K, sp.kchunk) : 1;
     sp.ws_bytes = sp.splits > 1 ? kSplitHeaderBytes + tiles * sp.splits * c.bm * c.bn * 4 : 0;
+    sp.full_tiles = 0;
     return sp;
 }
 
-double predict_split_us(const ConfigEntry& c, const SplitPlan& sp, int64_t M, int64_t N) {
-    const double t = predict_us(c, M, N, sp.kchunk, sp.splits);
-    if (sp.splits == 1) return t;
+// The hybrid plan with `want` chunks per split tile; false when the shape has
+// no partial layer of tiles, no whole one, or the chunks do not spread evenly
+// over the 8 XCDs.
+bool make_hybrid_plan(const ConfigEntry& c, int config, int64_t M, int64_t N, int64_t K,
+                      int64_t want, SplitPlan* out) {
+    const int64_t tiles = ceil_div(M, c.bm) * ceil_div(N, c.bn);
+    const int64_t rest = tiles % kNumCu, full = tiles - rest;
+    if (tiles > kSplitMaxTiles || rest == 0 || full == 0) return false;
+    SplitPlan sp = make_split_plan(c, config, M, N, K, want);
+    if (sp.splits < 2 || (rest * sp.splits) % kNumXcd != 0) return false;
+    sp.full_tiles = full;
+    sp.ws_bytes = kSplitHeaderBytes + rest * sp.splits * c.bm * c.bn * 4;
+    *out = sp;
+    return true;
+}
+
+// Workgroups of a split launch: every chunk of every split tile, plus the
+// hybrid's whole tiles.
+int64_t split_blocks(const SplitPlan& sp, int64_t tiles) {
+    return sp.full_tiles + (tiles - sp.full_tiles) * sp.splits;
+}
+
+double predict_split_us(const ConfigEntry& c, const SplitPlan& sp, int64_t M, int64_t N,
+                        int64_t K) {
     const double tiles = (double)(ceil_div(M, c.bm) * ceil_div(N, c.bn));
-    const double bytes = tiles * (double)c.bm * c.bn * 4.0 * 2.0 * (double)sp.splits;
-    return t + kJoinFixedUs + bytes / kJoinBytesPerUs;
+    const double joined = tiles - (double)sp.full_tiles;  // tiles whose chunks join
+    const double join_bytes = joined * (double)c.bm * c.bn * 4.0 * 2.0 * (double)sp.splits;
+    if (sp.full_tiles > 0) {
+        // Each CU runs full_tiles / 256 whole tiles and ceil(chunks / 256)
+        // chunks; a chunk counts as its own one-tile time over a whole
+        // tile's in the model's interpolation between one and w tiles per CU.
+        const double area = (double)c.bm * c.bn;
+        const double one = area * (c.one_a + c.one_b * (double)K);
+        const double full_t = area * (c.two_a + c.two_b * (double)K);
+        const double one_chunk = area * (c.one_a + c.one_b * (double)sp.kchunk) + kHybridChunkUs;
+        const double chunks_per_cu = std::ceil(joined * (double)sp.splits / kNumCu);
+        const double e = (double)sp.full_tiles / kNumCu + chunks_per_cu * one_chunk / one;
+        const int w = c.per_cu < 1 ? 1 : c.per_cu;
+        double t;
+        if (w < 2) {
+            t = e * one;
+        } else {
+            const double rounds = std::floor(e / w);
+            const double rest = e - rounds * w;
+            double last = 0.0;
+            if (rest >= 1.0)
+                last = one + (full_t - one) * (rest - 1.0) / (w - 1);
+            else if (rest > 0.0)
+                last = rest * one;
+            t = rounds * full_t + last;
+        }
+        return t + kHybridJoinUs + join_bytes / kJoinBytesPerUs;
+    }
+    // One chunk is the plain kernel over all of K.
+    const double t = predict_us(c, M, N, sp.splits == 1 ? K : sp.kchunk, sp.splits);
+    if (sp.splits == 1) return t;
+    return t + kJoinFixedUs + join_bytes / kJoinBytesPerUs;
 }
 
 // config < 0: every tile with a split-K variant (and the automatic plain
@@ -517,16 +582,22 @@ int plan_splitk(int config, int64_t M, int64_t N, int64_t K, int64_t splits, Spl
     if (splits < 0 || splits > kMaxSplits) return SGEMM_STATUS_INVALID_SIZE;
     bool have = false;
     double best_us = 0.0;
-    auto consider = [&](int idx, int64_t want) {
-        const ConfigEntry& c = kConfigs[idx];
-        const SplitPlan sp = make_split_plan(c, idx, M, N, K, want);
+    auto take = [&](const ConfigEntry& c, const SplitPlan& sp) {
         if (sp.ws_bytes > max_ws) return;
-        const double t = predict_split_us(c, sp, M, N);
+        const double t = predict_split_us(c, sp, M, N, K);
         if (!have || t < best_us * (1.0 - 1e-9)) {
             have = true;
             best_us = t;
             *out = sp;
         }
+    };
+    auto consider = [&](int idx, int64_t want) {
+        const ConfigEntry& c = kConfigs[idx];
+        take(c, make_split_plan(c, idx, M, N, K, want));
+        // The library's own choice (splits == 0) may also split only the
+        // last partial layer of tiles.
+        SplitPlan hp;
+        if (splits == 0 && make_hybrid_plan(c, idx, M, N, K, want, &hp)) take(c, hp);
     };
     if (config < 0 && splits == 0 && M > 0 && N > 0 && K > 0) consider(choose_config(M, N, K, 1), 1);
     for (int idx = 0; idx < kNumConfigs; ++idx) {
@@ -555,7 +626,7 @@ int prepare_splitk(int config, int64_t M, int64_t N, int64_t K, const float* A, 
     *needs_ws = M > 0 && N > 0 && K > 0 && sp->splits > 1;
     if (*needs_ws) {
         const ConfigEntry& c = kConfigs[sp->config];
-        const int64_t blocks = ceil_div(M, c.bm) * ceil_div(N, c.bn) * sp->splits;
+        const int64_t blocks = split_blocks(*sp, ceil_div(M, c.bm) * ceil_div(N, c.bn));
         if (blocks > kMaxWorkItems / c.threads) return SGEMM_STATUS_SIZE_OVERFLOW;
     }
     return SGEMM_STATUS_SUCCESS;
@@ -571,7 +642,7 @@ int launch_splitk(const SplitPlan& sp, int64_t M, int64_t N, int64_t K, const fl
         return launch_gemm(c.kernel, c.bm, c.bn, c.threads, M, N, K, A, lda, 0, B, ldb, 0, C,
                            ldc, 0, 1, stream);
     const int64_t tiles_m = ceil_div(M, c.bm), tiles_n = ceil_div(N, c.bn);
-    const int64_t blocks = tiles_m * tiles_n * sp.splits;
+    const int64_t blocks = split_blocks(sp, tiles_m * tiles_n);
     GemmArgs p = {};
     p.A = A;
     p.B = B;
@@ -595,6 +666,7 @@ int launch_splitk(const SplitPlan& sp, int64_t M, int64_t N, int64_t K, const fl
     p.ws = (float*)((char*)workspace + kSplitHeaderBytes);
     p.kchunk = (int)sp.kchunk;
     p.splits = (int)sp.splits;
+    p.full_tiles = (int)sp.full_tiles;
     void* args[] = {&p};
     hipError_t e = hipLaunchKernel(c.splitk, dim3((unsigned)blocks), dim3(c.threads), args, 0,
                                    stream);
@@ -862,6 +934,16 @@ int64_t sgemm_splitk_plan(int config, int64_t M, int64_t N, int64_t K, int64_t s
     if (plan_config != nullptr) *plan_config = sp.config;
     if (plan_splits != nullptr) *plan_splits = sp.splits;
     return (M == 0 || N == 0 || K == 0) ? 0 : sp.ws_bytes;
+}
+
+int64_t sgemm_splitk_plan_full_tiles(int config, int64_t M, int64_t N, int64_t K,
+                                      int64_t splits) {
+    if (M < 0 || N < 0 || K < 0) return SGEMM_STATUS_INVALID_SIZE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return SGEMM_STATUS_SIZE_OVERFLOW;
+    SplitPlan sp;
+    const int st = plan_splitk(config, M, N, K, splits, &sp);
+    if (st != SGEMM_STATUS_SUCCESS) return st;
+    return sp.splits > 1 ? sp.full_tiles : 0;
 }
 
 int sgemm_config_has_splitk(int config) {

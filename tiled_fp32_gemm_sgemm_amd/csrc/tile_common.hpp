@@ -63,6 +63,7 @@ struct GemmArgs {
     float* ws;
     uint32_t* counters;
     int kchunk, splits;
+    int full_tiles;  // split-K: tiles taking all of K with no join (0: every tile splits)
 };
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -116,6 +117,49 @@ __device__ __forceinline__ TileCoord map_block(const GemmArgs& p, int group_m) {
     grouped_tile(pid - (uint32_t)t.b * per_matrix, p.tiles_m, p.tiles_n, group_m, t.tm, t.tn);
     t.b += p.batch_base;
     return t;
+}
+
+// Split-K block -> (tile, chunk).  With full_tiles = F > 0 the first F tiles
+// (in grouped order) take all of K and need no join, and the other R tiles
+// are split: each XCD receives F / 8 full tiles and (gridDim - F) / 8
+// chunks, the full tiles first.  The host keeps both multiples of 8.
+struct SplitCoord {
+    TileCoord tc;  // tc.b: the chunk (0 for a full tile)
+    int tail;      // join slot of a split tile, in [0, R) (every tile when F = 0)
+    bool full;
+};
+
+__device__ __forceinline__ SplitCoord map_split_block(const GemmArgs& p, int group_m) {
+    const uint32_t nblocks = gridDim.x;
+    const uint32_t bid = kRaceCheck ? nblocks - 1 - blockIdx.x : blockIdx.x;
+    const uint32_t tiles = (uint32_t)p.tiles_m * (uint32_t)p.tiles_n;
+    SplitCoord s;
+    uint32_t lin;
+    if (p.full_tiles == 0) {
+        const uint32_t pid = xcd_contiguous_id(bid, nblocks);
+        s.tc.b = (int)(pid / tiles);
+        lin = pid - (uint32_t)s.tc.b * tiles;
+        s.tail = (int)lin;
+        s.full = false;
+    } else {
+        const uint32_t F = (uint32_t)p.full_tiles, R = tiles - F;
+        const uint32_t fx = F / kNumXcd, tx = (nblocks - F) / kNumXcd;
+        const uint32_t xcd = bid % kNumXcd, slot = bid / kNumXcd;
+        if (slot < fx) {
+            lin = xcd * fx + slot;
+            s.tc.b = 0;
+            s.tail = 0;
+            s.full = true;
+        } else {
+            const uint32_t u = xcd * tx + (slot - fx);
+            s.tail = (int)(u % R);
+            s.tc.b = (int)(u / R);
+            lin = F + (uint32_t)s.tail;
+            s.full = false;
+        }
+    }
+    grouped_tile(lin, p.tiles_m, p.tiles_n, group_m, s.tc.tm, s.tc.tn);
+    return s;
 }
 
 __device__ __forceinline__ f32x4 ldg4(const float* p) {
