@@ -45,6 +45,13 @@ CSRC = os.path.join(ROOT, "tiled_fp32_gemm_sgemm_amd", "csrc")
 def gemm_traffic_file(path: str, workload: str) -> str:
     """The committed counter summary of a GEMM workload on a path."""
     return os.path.join(ROOT, "profiles", "sgemm_%s_%s_counters.txt" % (path, workload))
+
+
+def conv_traffic_file(path: str, workload: str) -> str:
+    """The committed counter summary of a convolution workload: conv2d_nhwc
+    (path mfma) or conv2d_nhwc_splitk (path splitk)."""
+    return os.path.join(ROOT, "profiles", "conv2d_%s%s_counters.txt"
+                        % ("splitk_" if path == "splitk" else "", workload))
 COPY_BYTES = 512 * 1024 * 1024   # larger than the 256 MB last-level cache
 GEMM_WORK_S = 0.1                # default warm-up and timed work per GEMM phase (s)
 SETTLE_S = 0.1                   # GEMM launches before the warm-up steps (clock settle)
@@ -67,7 +74,6 @@ def gemm_metric(w) -> str:
 GEMM_SOURCES = ("tile_common.hpp", "mfma_dl_kernel.hpp", "mfma_kernel.hpp", "valu_kernel.hpp")
 WINDOW_SOURCES = ("window.hip", "window_kernel.hpp", "tile_common.hpp")
 WINDOW_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "window_sum_window5_counters.txt")
-CONV_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "conv2d_conv3x3_c256_counters.txt")
 ATTN_SOURCES = ("attention_kernel.hpp", "mfma_dl_kernel.hpp", "mfma_kernel.hpp", "tile_common.hpp")
 ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_attn_s2048_d128_counters.txt")
 
@@ -352,12 +358,25 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
     # --------------------------------------------------- closed forms, models
     if conv:
         P, Q = w.out_hw
-        cfg = config if config is not None else sg.conv2d_select_config(
-            w.N, w.H, w.W, w.C, w.K, w.R, w.S, w.pad, w.stride, w.dil)
+        n_split, full = 1, 0
+        if path == "splitk":
+            cfg, n_split, _, full = sg.conv2d_splitk_plan(w.N, w.H, w.W, w.C, w.K, w.R, w.S,
+                                                          w.pad, w.stride, w.dil, splits, config)
+        else:
+            cfg = config if config is not None else sg.conv2d_select_config(
+                w.N, w.H, w.W, w.C, w.K, w.R, w.S, w.pad, w.stride, w.dil)
         info = sg.config_info(cfg)
+        # Chunks of whole BK slices: a split tile does the slices of a whole one.
         want = model.mfma_instructions(w.N * P * Q, w.K, w.R * w.S * w.C, info["bm"], info["bn"],
                                        info["bk"], 32, 1)
         L.append("mfma_instructions_closed_form: %d (tile %s)" % (want, info["name"]))
+        if n_split > 1:
+            tiles = model.ceil_div(w.N * P * Q, info["bm"]) * model.ceil_div(w.K, info["bn"])
+            part = (tiles - full) * n_split * info["bm"] * info["bn"] * 4
+            L.append("splitk_chunks: %d" % n_split)
+            L.append("splitk_full_tiles: %d of %d (all of R*S*C, no join)" % (full, tiles))
+            L.append("splitk_partial_bytes_model: %d (split tiles x chunks x BM x BN x 4, "
+                     "written once and read once by the join)" % part)
     if attn:
         # Each of the 8 waves issues 2 D v_mfma_f32_32x32x2_f32 per visited
         # (256-query, 64-key) block pair: D for the scores, D for P V.
@@ -399,10 +418,12 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
             L.append("beyond_l2_read_over_panel_model: %.4f" % (rd / panels))
         if n_split > 1:
             tiles = model.ceil_div(w.M, info["bm"]) * model.ceil_div(w.N, info["bn"])
-            part = tiles * n_split * info["bm"] * info["bn"] * 4
+            full = sg.splitk_plan_full_tiles(w.M, w.N, w.K, splits)
+            part = (tiles - full) * n_split * info["bm"] * info["bn"] * 4
             L.append("splitk_chunks: %d" % n_split)
-            L.append("splitk_partial_bytes_model: %d (tiles x chunks x BM x BN x 4, written once "
-                     "and read once by the join)" % part)
+            L.append("splitk_full_tiles: %d of %d (all of K, no join)" % (full, tiles))
+            L.append("splitk_partial_bytes_model: %d (split tiles x chunks x BM x BN x 4, "
+                     "written once and read once by the join)" % part)
             if fetch and write:
                 L.append("beyond_l2_write_minus_output_over_partials: %.4f ((write bytes - 4MN) "
                          "/ partial bytes)" % ((wr - 4.0 * w.M * w.N) / part))
@@ -609,12 +630,31 @@ def bench_conv(args) -> int:
     y = torch.empty((w.N, P, Q, w.K), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     handle = stream.cuda_stream
+    splitk = args.path == "splitk"
+    if splitk:
+        # conv2d_nhwc_splitk: the reduction split over workgroups (the time
+        # model's plan at --splits 0), joined through a workspace zeroed once.
+        cfg, n_split, ws_bytes, full_tiles = sg.conv2d_splitk_plan(
+            w.N, w.H, w.W, w.C, w.K, w.R, w.S, w.pad, w.stride, w.dil, args.splits, args.config)
+        ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
 
-    def step(config=args.config):
-        st = sg.conv2d_nhwc_raw(w.N, w.H, w.W, w.C, w.K, w.R, w.S, x.data_ptr(), wt.data_ptr(),
-                                y.data_ptr(), w.pad, w.stride, w.dil, handle, config)
-        if st != 0:
-            raise sg.SgemmError(st, "conv2d_nhwc")
+        def step():
+            st = sg.conv2d_nhwc_splitk_raw(w.N, w.H, w.W, w.C, w.K, w.R, w.S, x.data_ptr(),
+                                           wt.data_ptr(), y.data_ptr(), ws.data_ptr(),
+                                           ws.numel(), w.pad, w.stride, w.dil, args.splits,
+                                           handle, args.config)
+            if st != 0:
+                raise sg.SgemmError(st, "conv2d_nhwc_splitk")
+    else:
+        cfg = args.config if args.config is not None else sg.conv2d_select_config(
+            w.N, w.H, w.W, w.C, w.K, w.R, w.S, w.pad, w.stride, w.dil)
+
+        def step():
+            st = sg.conv2d_nhwc_raw(w.N, w.H, w.W, w.C, w.K, w.R, w.S, x.data_ptr(),
+                                    wt.data_ptr(), y.data_ptr(), w.pad, w.stride, w.dil, handle,
+                                    args.config)
+            if st != 0:
+                raise sg.SgemmError(st, "conv2d_nhwc")
 
     def timed(fn, n_steps, n_warm):
         for _ in range(n_warm):
@@ -639,8 +679,7 @@ def bench_conv(args) -> int:
 
     ms = timed(step, args.steps, args.warmup)
     tflops = w.flops / (ms * 1e-3) / 1e12
-    cfg = args.config if args.config is not None else sg.conv2d_select_config(
-        w.N, w.H, w.W, w.C, w.K, w.R, w.S, w.pad, w.stride, w.dil)
+    tile = sg.config_info(cfg)["name"]
     comparators = {}
     if not args.no_comparator:
         # MIOpen through torch, FP32, on the same NHWC memory (channels_last).
@@ -652,6 +691,12 @@ def bench_conv(args) -> int:
                     max(5, args.steps // 2), 3)
         comparators["torch_conv2d_channels_last"] = {
             "tflops": w.flops / (tms * 1e-3) / 1e12, "ms_per_step": tms}
+    conf = {"workload": w.describe(), "N": w.N, "H": w.H, "W": w.W, "C": w.C, "K": w.K,
+            "R": w.R, "S": w.S, "tile": tile,
+            "entry": "conv2d_nhwc_splitk" if splitk else "conv2d_nhwc"}
+    if splitk:
+        conf["splitk"] = {"chunks": n_split, "full_tiles": full_tiles,
+                          "workspace_bytes": ws_bytes}
     out = {
         "metric": "FP32 2-D convolution TFLOP/s (implicit GEMM, NHWC)",
         "value": tflops,
@@ -670,15 +715,13 @@ def bench_conv(args) -> int:
         # equivalent); the useful rate leaves out the taps on the zero padding
         "useful_tflops": w.useful_flops / (ms * 1e-3) / 1e12,
         "useful_flop_share": w.useful_flops / w.flops,
-        "config": {"workload": w.describe(), "N": w.N, "H": w.H, "W": w.W, "C": w.C, "K": w.K,
-                   "R": w.R, "S": w.S, "tile": sg.config_info(cfg)["name"]},
+        "config": conf,
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_FP32_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / PEAK_FP32_TFLOPS,
-                     "traffic": (read_traffic(CONV_TRAFFIC_FILE, GEMM_SOURCES,
-                                              sg.config_info(cfg)["name"])
-                                 if args.workload == "conv3x3_c256" and args.config is None
-                                 else None),
-                     "kernel": sg.config_info(cfg)["name"], "event_ms_per_launch": ms},
+                     "traffic": read_traffic(conv_traffic_file(args.path, args.workload),
+                                             GEMM_SOURCES, tile,
+                                             n_split if splitk else None),
+                     "kernel": tile, "event_ms_per_launch": ms},
         "cpu_baseline": None if args.no_cpu_baseline else conv_cpu_baseline(w, x_cpu, wt_cpu),
         "comparators": comparators,
         "device": torch.cuda.get_device_name(dev),
@@ -815,8 +858,9 @@ def main(argv=None) -> int:
                          "for attention)")
     ap.add_argument("--path", choices=["mfma", "valu", "splitk", "window"], default="mfma",
                     help="GEMM path: the matrix-core product (sgemm), the vector-ALU comparator, "
-                         "or the split-K entry point at --splits (window: counter summaries of "
-                         "the window kernel only)")
+                         "or the split-K entry point at --splits; for a convolution workload, "
+                         "conv2d_nhwc (mfma) or conv2d_nhwc_splitk (splitk) (window: counter "
+                         "summaries of the window kernel only)")
     ap.add_argument("--workload", default="square4096")
     ap.add_argument("--config", type=int, default=None, help="force a matrix-core tile config")
     ap.add_argument("--splits", type=int, default=0,
@@ -902,6 +946,10 @@ def main(argv=None) -> int:
     if args.workload in WINDOW_WORKLOADS:
         return bench_window(args)
     if args.workload in CONV_WORKLOADS:
+        if args.path not in ("mfma", "splitk"):
+            print("a convolution runs on --path mfma (conv2d_nhwc) or splitk "
+                  "(conv2d_nhwc_splitk)", file=sys.stderr)
+            return 2
         return bench_conv(args)
 
     if args.path == "window":

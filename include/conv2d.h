@@ -88,6 +88,58 @@ int conv2d_select_config(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, 
                          int64_t S, int64_t pad_h, int64_t pad_w, int64_t stride_h,
                          int64_t stride_w, int64_t dil_h, int64_t dil_w);
 
+/*
+ * y = conv2d(x, wt) as conv2d_nhwc, with the reduction over R*S*C split as in
+ * sgemm_splitk: on the implicit GEMM's output tiles, each of `splits` chunks
+ * of whole BK slices is reduced by its own workgroup, and the partial tiles
+ * join inside the same launch in chunk order (bit-reproducible, independent
+ * of timing; no workgroup waits for another).  With splits = 0 the time model
+ * chooses, and may split only the tiles of the last partial layer of one tile
+ * per CU, the others taking all of R*S*C ("Tiling Strategies" section 4 on
+ * tail effects: a 3x3 layer of 64 x 14 x 14 outputs and 256 channels makes
+ * 784 tiles of 64 x 64, three per CU and 16 more).  A chunk may start inside
+ * a filter tap.
+ *
+ * config: a configuration with a convolution split-K kernel
+ *   (conv2d_config_has_splitk), or -1 for the time model's choice (which may
+ *   be the plain convolution kernel).
+ * splits: 1 ... 64, or 0 for the time model's choice; the count used is at
+ *   most ceil(R*S*C / BK) (conv2d_nhwc_splitk_plan reports it).
+ * workspace, workspace_bytes: as for sgemm_splitk, with at least
+ *   conv2d_nhwc_splitk_plan(...) bytes (NULL and 0 when the plan does not
+ *   split).  The counter header must hold zeros before the first use; every
+ *   completed call leaves it zero, so one workspace serves sgemm_splitk and
+ *   conv2d_nhwc_splitk calls of any shape in turn.  Concurrent calls on one
+ *   workspace race.
+ * Errors as for conv2d_nhwc, plus SGEMM_STATUS_INVALID_CONFIG (no
+ * convolution split-K kernel), SGEMM_STATUS_INVALID_SIZE (splits outside
+ * 0 ... 64) and SGEMM_STATUS_INVALID_WORKSPACE; on an error nothing is
+ * enqueued.
+ */
+int conv2d_nhwc_splitk(int config, int64_t N, int64_t H, int64_t W, int64_t C, int64_t K,
+                       int64_t R, int64_t S, int64_t pad_h, int64_t pad_w, int64_t stride_h,
+                       int64_t stride_w, int64_t dil_h, int64_t dil_w, const float *x,
+                       const float *wt, float *y, int64_t splits, void *workspace,
+                       int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The plan conv2d_nhwc_splitk would run for these arguments: the tile
+ * configuration, the chunk count and the number of output tiles that take all
+ * of R*S*C without a join go to *plan_config, *plan_splits and
+ * *plan_full_tiles (each may be NULL); returns the workspace bytes it needs
+ * (0 when it does not split or there is nothing to compute), or a negative
+ * status.  Host only.
+ */
+int64_t conv2d_nhwc_splitk_plan(int config, int64_t N, int64_t H, int64_t W, int64_t C,
+                                int64_t K, int64_t R, int64_t S, int64_t pad_h, int64_t pad_w,
+                                int64_t stride_h, int64_t stride_w, int64_t dil_h,
+                                int64_t dil_w, int64_t splits, int *plan_config,
+                                int64_t *plan_splits, int64_t *plan_full_tiles);
+
+/* 1 if tile configuration `config` has a convolution split-K kernel, 0 if
+ * not; SGEMM_STATUS_INVALID_CONFIG for an unknown index.  Host only. */
+int conv2d_config_has_splitk(int config);
+
 #ifdef __cplusplus
 }
 #endif

@@ -58,6 +58,19 @@ def test_every_committed_gemm_summary_is_found_by_its_workload():
         assert "beyond_l2_bytes_per_launch:" in text and "kernel_source_sha256_16:" in text, f
 
 
+def test_conv_summaries_are_named_by_entry_point():
+    import os
+    assert bench.conv_traffic_file("mfma", "conv3x3_c256").endswith(
+        os.path.join("profiles", "conv2d_conv3x3_c256_counters.txt"))
+    assert bench.conv_traffic_file("splitk", "conv3x3_c256").endswith(
+        os.path.join("profiles", "conv2d_splitk_conv3x3_c256_counters.txt"))
+
+
+def test_conv_rejects_gemm_only_paths(capsys):
+    assert bench.main(["--workload", "conv3x3_c256", "--path", "valu"]) == 2
+    assert "conv2d_nhwc" in capsys.readouterr().err
+
+
 def test_source_hash_depends_on_every_listed_file(tmp_path, monkeypatch):
     for name in ("a.hpp", "b.hpp"):
         (tmp_path / name).write_text("int %s;\n" % name[0])

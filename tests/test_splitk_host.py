@@ -134,3 +134,58 @@ def test_hybrid_plan_splits_only_the_last_partial_layer():
     assert sg.splitk_plan_full_tiles(M, N, K, 4, cfg) == 0
     assert sg.splitk_plan_full_tiles(12288, 256, 2304) == 0
     assert sg.splitk_plan_full_tiles(512, 512, 8192) == 0
+
+
+CONV_SK = [c for c in range(sg.num_configs()) if sg.conv2d_config_has_splitk(c)]
+
+
+def test_conv_splitk_variants_are_convolution_tiles_with_split_k():
+    assert len(CONV_SK) >= 4
+    for c in CONV_SK:
+        assert sg.conv2d_config_available(c) and sg.config_has_splitk(c)
+    with pytest.raises(sg.SgemmError):
+        sg.conv2d_config_has_splitk(sg.num_configs())
+
+
+def test_conv_hybrid_plan_on_a_3x3_layer():
+    """64 images of 14 x 14 x 256, 256 filters of 3 x 3: the implicit GEMM is
+    12544 x 256 x 2304, 784 tiles of 64 x 64 = three layers of 256 and 16
+    more.  The automatic plan runs the 768 whole and splits the 16."""
+    cfg, splits, nbytes, full = sg.conv2d_splitk_plan(64, 14, 14, 256, 256, 3, 3, 1)
+    info = sg.config_info(cfg)
+    assert cfg in CONV_SK
+    tiles = -(-12544 // info["bm"]) * -(-256 // info["bn"])
+    assert full == tiles - tiles % 256 and 0 < full < tiles
+    assert splits > 1 and ((tiles - full) * splits) % 8 == 0
+    assert nbytes == sg.SPLITK_HEADER_BYTES + (tiles - full) * splits * info["bm"] * info["bn"] * 4
+    # An explicit chunk count splits every tile.
+    _, s4, nb4, full4 = sg.conv2d_splitk_plan(64, 14, 14, 256, 256, 3, 3, 1, 1, 1, 4, cfg)
+    assert (s4, full4) == (4, 0)
+    assert nb4 == sg.SPLITK_HEADER_BYTES + tiles * 4 * info["bm"] * info["bn"] * 4
+    # 16 x 16 images make 1024 tiles, four whole layers: nothing to even out.
+    assert sg.conv2d_splitk_plan(64, 16, 16, 256, 256, 3, 3, 1)[3] == 0
+    # Nothing to compute: no workspace.
+    assert sg.conv2d_splitk_plan(2, 4, 4, 0, 3, 3, 3, 1)[2] == 0
+    assert sg.conv2d_splitk_plan(1, 2, 2, 4, 3, 5, 5)[2] == 0
+
+
+def test_conv_splitk_call_errors_enqueue_nothing():
+    lib = _lib()
+    cfg = CONV_SK[0]
+    need = sg.conv2d_splitk_plan(1, 8, 8, 64, 64, 3, 3, 1, 1, 1, 4, cfg)[2]
+    assert need > 0
+    call = lambda **kw: lib.conv2d_nhwc_splitk(
+        kw.get("config", cfg), 1, 8, 8, 64, 64, 3, 3, 1, 1, kw.get("stride", 1), 1, 1, 1,
+        kw.get("x", FAKE), FAKE, FAKE, kw.get("splits", 4), kw.get("ws", FAKE),
+        kw.get("nbytes", need), None)
+    assert call(ws=None) == -9
+    assert call(nbytes=need - 1) == -9
+    assert call(splits=-1) == -1
+    assert call(splits=65) == -1
+    assert call(stride=0) == -1
+    assert call(x=None) == -3
+    assert call(config=sg.num_configs()) == -7
+    no_conv_split = [c for c in range(sg.num_configs()) if not sg.conv2d_config_has_splitk(c)]
+    assert call(config=no_conv_split[0]) == -7
+    with pytest.raises(sg.SgemmError):
+        sg.conv2d_splitk_plan(1, 8, 8, 64, 64, 3, 3, 1, 1, 1, 4, no_conv_split[0])

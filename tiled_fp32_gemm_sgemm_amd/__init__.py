@@ -9,7 +9,8 @@ leading dimensions and the current stream to it.
 """
 from .api import (SPLITK_HEADER_BYTES, SPLITK_MAX_TILES, attention, attention_raw, autotune, autotune_raw, config_has_general_form, config_info,
                   conv2d_config_available, conv2d_nhwc, conv2d_nhwc_raw, conv2d_output_size,
-                  conv2d_select_config,
+                  conv2d_select_config, conv2d_config_has_splitk, conv2d_nhwc_splitk,
+                  conv2d_nhwc_splitk_raw, conv2d_splitk_plan,
                   config_selectable, num_configs, predict_us, select_config,
                   select_general_config, sgemm, sgemm_ex, sgemm_ex_raw, sgemm_raw,
                   config_has_splitk, sgemm_splitk, sgemm_splitk_noalloc, splitk_plan,
@@ -23,7 +24,8 @@ __all__ = ["sgemm", "sgemm_strided_batched", "sgemm_raw", "sgemm_strided_batched
            "autotune", "autotune_raw", "sgemm_ex", "sgemm_ex_raw", "config_has_general_form",
            "select_general_config", "window_sum", "window_sum_raw", "conv2d_nhwc",
            "conv2d_nhwc_raw", "conv2d_output_size", "conv2d_config_available",
-           "conv2d_select_config", "workgroups_per_cu", "attention", "attention_raw",
+           "conv2d_select_config", "conv2d_config_has_splitk", "conv2d_nhwc_splitk",
+           "conv2d_nhwc_splitk_raw", "conv2d_splitk_plan", "workgroups_per_cu", "attention", "attention_raw",
            "sgemm_splitk", "sgemm_splitk_noalloc", "splitk_plan", "splitk_plan_full_tiles",
            "splitk_workspace", "config_has_splitk",
            "SPLITK_HEADER_BYTES", "SPLITK_MAX_TILES", "SgemmError",

@@ -92,6 +92,12 @@ _SIGS = {
                                 ctypes.c_int),
     "conv2d_config_available": ([ctypes.c_int], ctypes.c_int),
     "conv2d_select_config": ([_i64] * 13, ctypes.c_int),
+    "conv2d_nhwc_splitk": ([ctypes.c_int] + [_i64] * 13 + [_p, _p, _p, _i64, _p, _i64, _p],
+                           ctypes.c_int),
+    "conv2d_nhwc_splitk_plan": ([ctypes.c_int] + [_i64] * 14 +
+                                [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(_i64),
+                                 ctypes.POINTER(_i64)], _i64),
+    "conv2d_config_has_splitk": ([ctypes.c_int], ctypes.c_int),
     "attention_fwd": ([_i64, _i64, _i64, _i64, _p, _p, _p, _p, ctypes.c_float, ctypes.c_int, _p],
                       ctypes.c_int),
 }

@@ -479,6 +479,77 @@ def conv2d_nhwc(x, wt, pad=0, stride=1, dil=1, out=None, stream=None, config=Non
     return out
 
 
+def conv2d_splitk_plan(N, H, W, C, K, R, S, pad=0, stride=1, dil=1, splits: int = 0,
+                       config=None):
+    """(config, splits, workspace bytes, full tiles) of the plan
+    conv2d_nhwc_splitk would run (the library's conv2d_nhwc_splitk_plan)."""
+    ph, pw = _pair(pad, "pad")
+    sh, sw = _pair(stride, "stride")
+    dh, dw = _pair(dil, "dil")
+    cfg = ctypes.c_int()
+    sp = ctypes.c_int64()
+    full = ctypes.c_int64()
+    nbytes = _native.lib().conv2d_nhwc_splitk_plan(
+        -1 if config is None else int(config), N, H, W, C, K, R, S, ph, pw, sh, sw, dh, dw,
+        int(splits), ctypes.byref(cfg), ctypes.byref(sp), ctypes.byref(full))
+    if nbytes < 0:
+        raise _native.SgemmError(int(nbytes), "conv2d_nhwc_splitk_plan")
+    return cfg.value, sp.value, int(nbytes), full.value
+
+
+def conv2d_nhwc_splitk_raw(N, H, W, C, K, R, S, x_ptr, w_ptr, y_ptr, ws_ptr, ws_bytes, pad=0,
+                           stride=1, dil=1, splits=0, stream=0, config=None) -> int:
+    """conv2d_nhwc_splitk on device addresses (include/conv2d.h); returns the
+    status."""
+    ph, pw = _pair(pad, "pad")
+    sh, sw = _pair(stride, "stride")
+    dh, dw = _pair(dil, "dil")
+    return _native.lib().conv2d_nhwc_splitk(-1 if config is None else int(config), N, H, W, C, K,
+                                            R, S, ph, pw, sh, sw, dh, dw, x_ptr, w_ptr, y_ptr,
+                                            int(splits), ws_ptr, int(ws_bytes), stream)
+
+
+def conv2d_nhwc_splitk(x, wt, pad=0, stride=1, dil=1, out=None, *, splits: int = 0, config=None,
+                       workspace=None, stream=None):
+    """conv2d_nhwc with the reduction over R*S*C split across workgroups as in
+    sgemm_splitk (splits = 0: the time model's choice, possibly splitting only
+    the last partial layer of tiles).  workspace: a device tensor of at least
+    conv2d_splitk_plan(...)[2] bytes whose header starts at zero, or None for
+    the one kept for this device and stream (shared with sgemm_splitk)."""
+    import torch
+    for t, name in ((x, "x"), (wt, "wt")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or t.device.type != "cuda":
+            raise TypeError("%s must be a float32 CUDA tensor" % name)
+        if t.dim() != 4 or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous 4-D tensor" % name)
+    N, H, W, C = x.shape
+    K, R, S, C2 = wt.shape
+    if C2 != C:
+        raise ValueError("channel counts differ: x has %d, wt has %d" % (C, C2))
+    P, Q = conv2d_output_size(H, W, R, S, pad, stride, dil)
+    if out is None:
+        out = torch.empty((N, P, Q, K), dtype=torch.float32, device=x.device)
+    if tuple(out.shape) != (N, P, Q, K) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (%d, %d, %d, %d) tensor" % (N, P, Q, K))
+    _, _, nbytes, _ = conv2d_splitk_plan(N, H, W, C, K, R, S, pad, stride, dil, splits, config)
+    if workspace is None:
+        workspace = splitk_workspace(x.device, nbytes, stream)
+    with torch.cuda.device(x.device):
+        st = conv2d_nhwc_splitk_raw(N, H, W, C, K, R, S, x.data_ptr(), wt.data_ptr(),
+                                    out.data_ptr(), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), pad, stride,
+                                    dil, splits, _stream_handle(stream, x.device), config)
+    _check(st, "conv2d_nhwc_splitk")
+    return out
+
+
+def conv2d_config_has_splitk(config: int) -> bool:
+    st = _native.lib().conv2d_config_has_splitk(int(config))
+    if st < 0:
+        raise _native.SgemmError(st, "conv2d_config_has_splitk")
+    return bool(st)
+
+
 def conv2d_config_available(config: int) -> bool:
     st = _native.lib().conv2d_config_available(int(config))
     if st < 0:

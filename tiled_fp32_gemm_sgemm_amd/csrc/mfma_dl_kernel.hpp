@@ -184,7 +184,8 @@ struct DlTile {
     static_assert(SCHED >= 0 && SCHED <= 2, "slice schedule");
     static_assert(SCHED < 2 || LPS <= NKG * KG - HOLD, "one copy per k step fits in a slice");
     static_assert((KSPLIT - 1) * BM * BN <= STAGES * BUF_FLOATS, "k-group exchange fits in LDS");
-    static_assert(!SK || (A_KC && !B_KC && !EX && !CONV), "split-K: the plain product only");
+    static_assert(!SK || (A_KC && !EX && B_KC == CONV),
+                  "split-K: the plain product or the convolution only");
     static_assert(!SK || WTM * WTN <= 64 * 64, "split-K join holds one wave tile of sums");
 
     // Quad swizzle of k-contiguous row r.  Rows of at most 256 bytes: the 16
@@ -319,8 +320,11 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     const int rows_left = p.M - m0;
     const int cols_left = p.N - n0;
     const bool full_mn = rows_left >= T::BM && cols_left >= T::BN;
-    // The k range this workgroup reduces: all of K, or one split's part.
+    // The k range this workgroup reduces: all of K, or one split's part,
+    // which starts at kbeg (the operand pointers above are already moved
+    // there; only the convolution's gather works in absolute k).
     const int Kd = T::SK && !sk_full ? min(p.kchunk, p.K - tc.b * p.kchunk) : p.K;
+    const int kbeg = T::SK ? tc.b * p.kchunk : 0;
     const int nslices = (Kd + T::BK - 1) / T::BK;
 
     const int tid = threadIdx.x;
@@ -437,9 +441,13 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
         int a_range = (int)a_span;
         int64_t a_step = T::A_KC ? (int64_t)k0 : (int64_t)k0 * p.lda;
         if constexpr (T::CONV) {
-            const int tap = __builtin_amdgcn_readfirstlane(k0 / cg.C);
-            const int c0 = k0 - tap * cg.C;
-            if (c0 == 0) conv_offsets(tap);
+            // Slices are copied in k order, so the offsets are rebuilt at a
+            // new tap and at the first slice (a split-K chunk may start
+            // inside a tap).
+            const int kg = kbeg + k0;
+            const int tap = __builtin_amdgcn_readfirstlane(kg / cg.C);
+            const int c0 = kg - tap * cg.C;
+            if (c0 == 0 || k0 == 0) conv_offsets(tap);
             a_step = cv_org + c0;
             a_range = (int)((cv_span - c0) * 4);
         }
@@ -489,8 +497,8 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
                     for (int e = 0; e < 4; ++e) {
                         const int k = k0 + 4 * kq + e;
                         if (k < Kd) {
-                            const int tap = k / cg.C;
-                            const int c = k - tap * cg.C;
+                            const int tap = (kbeg + k) / cg.C;
+                            const int c = kbeg + k - tap * cg.C;
                             const int fr = tap / cg.S;
                             const int fs = tap - fr * cg.S;
                             const int ih = op * cg.stride_h - cg.pad_h + fr * cg.dil_h;

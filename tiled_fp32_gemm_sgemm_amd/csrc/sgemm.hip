@@ -160,6 +160,8 @@ struct ConfigEntry {
     const void* conv;
     // Split-K variant of the plain product; NULL where not built.
     const void* splitk;
+    // Split-K variant of the convolution; NULL where not built.
+    const void* conv_splitk;
 };
 
 // The same tile with stored-operand layouts and the alpha/beta epilogue.
@@ -191,6 +193,20 @@ const void* splitk_kernel() {
         return nullptr;
 }
 
+// The convolution's split-K variant, for the same tiles.
+template <class T>
+using DlConvSplitK = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::OCC,
+                            T::GROUP_M, T::STAGES, T::KSPLIT, T::SWIZZLE, false, true, false,
+                            T::BIL, true, T::SCHED, true>;
+
+template <class T>
+const void* conv_splitk_kernel() {
+    if constexpr (T::WTM * T::WTN <= 64 * 64 && T::BK >= 32)
+        return (const void*)&sgemm_mfma_dl_kernel<DlConvSplitK<T>>;
+    else
+        return nullptr;
+}
+
 #define SGEMM_CFG(T, name, per_cu, a1, b1, a2, b2) \
     { name, T::BM, T::BN, T::BK, T::NT, T::WG_PER_CU, (const void*)&sgemm_mfma_kernel<T>, per_cu, \
       a1, b1, a2, b2 }
@@ -204,7 +220,8 @@ const void* splitk_kernel() {
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, false>>,                        \
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, false, true>>,                        \
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, true>> },                        \
-      (const void*)&sgemm_mfma_dl_kernel<DlConv<T>>, splitk_kernel<T>() }
+      (const void*)&sgemm_mfma_dl_kernel<DlConv<T>>, splitk_kernel<T>(),                     \
+      conv_splitk_kernel<T>() }
 // General form, no convolution variant.
 #define SGEMM_DLG_CFG(T, name, per_cu, a1, b1, a2, b2)                                       \
     { name, T::BM, T::BN, T::BK, T::NT, T::WG_PER_CU, (const void*)&sgemm_mfma_dl_kernel<T>, \
@@ -213,13 +230,13 @@ const void* splitk_kernel() {
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, false>>,                        \
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, false, true>>,                        \
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, true>> },                        \
-      nullptr, splitk_kernel<T>() }
+      nullptr, splitk_kernel<T>(), nullptr }
 
 // Plain product and its split-K variant only.
 #define SGEMM_DLS_CFG(T, name, per_cu, a1, b1, a2, b2)                                       \
     { name, T::BM, T::BN, T::BK, T::NT, T::WG_PER_CU, (const void*)&sgemm_mfma_dl_kernel<T>, \
       per_cu, a1, b1, a2, b2, { nullptr, nullptr, nullptr, nullptr }, nullptr,               \
-      splitk_kernel<T>() }
+      splitk_kernel<T>(), nullptr }
 
 const ConfigEntry kConfigs[] = {
     SGEMM_CFG(Cfg256x128, "mfma32_256x128x16_w2x2", 1, 3.6505e-04, 4.2029e-06, 4.1134e-04, 8.0806e-06),
@@ -575,16 +592,22 @@ double predict_split_us(const ConfigEntry& c, const SplitPlan& sp, int64_t M, in
 // config < 0: every tile with a split-K variant (and the automatic plain
 // choice); splits == 0: every split count up to kMaxSplits.  Plans whose
 // workspace exceeds max_ws are left out.  The smallest predicted time wins.
+// conv_c > 0: the product is a convolution's implicit GEMM over conv_c input
+// channels; the tiles are those with a convolution split-K kernel, and a BK
+// that does not divide conv_c (slices gathered through registers) counts
+// four times slower, as in choose_conv_config.
 int plan_splitk(int config, int64_t M, int64_t N, int64_t K, int64_t splits, SplitPlan* out,
-                int64_t max_ws = INT64_MAX) {
+                int64_t max_ws = INT64_MAX, int64_t conv_c = 0) {
+    auto kernel_of = [&](const ConfigEntry& c) { return conv_c > 0 ? c.conv_splitk : c.splitk; };
     if (config >= kNumConfigs) return SGEMM_STATUS_INVALID_CONFIG;
-    if (config >= 0 && kConfigs[config].splitk == nullptr) return SGEMM_STATUS_INVALID_CONFIG;
+    if (config >= 0 && kernel_of(kConfigs[config]) == nullptr) return SGEMM_STATUS_INVALID_CONFIG;
     if (splits < 0 || splits > kMaxSplits) return SGEMM_STATUS_INVALID_SIZE;
     bool have = false;
     double best_us = 0.0;
     auto take = [&](const ConfigEntry& c, const SplitPlan& sp) {
         if (sp.ws_bytes > max_ws) return;
-        const double t = predict_split_us(c, sp, M, N, K);
+        const double t = predict_split_us(c, sp, M, N, K) *
+                         (conv_c > 0 && conv_c % c.bk != 0 ? 4.0 : 1.0);
         if (!have || t < best_us * (1.0 - 1e-9)) {
             have = true;
             best_us = t;
@@ -599,9 +622,10 @@ int plan_splitk(int config, int64_t M, int64_t N, int64_t K, int64_t splits, Spl
         SplitPlan hp;
         if (splits == 0 && make_hybrid_plan(c, idx, M, N, K, want, &hp)) take(c, hp);
     };
-    if (config < 0 && splits == 0 && M > 0 && N > 0 && K > 0) consider(choose_config(M, N, K, 1), 1);
+    if (config < 0 && splits == 0 && M > 0 && N > 0 && K > 0)
+        consider(conv_c > 0 ? choose_conv_config(M, N, K, conv_c) : choose_config(M, N, K, 1), 1);
     for (int idx = 0; idx < kNumConfigs; ++idx) {
-        if (config >= 0 ? idx != config : (kConfigs[idx].splitk == nullptr ||
+        if (config >= 0 ? idx != config : (kernel_of(kConfigs[idx]) == nullptr ||
                                            kConfigs[idx].per_cu == 0))
             continue;
         if (splits > 0) {
@@ -633,25 +657,30 @@ int prepare_splitk(int config, int64_t M, int64_t N, int64_t K, const float* A, 
 }
 
 // Enqueues a prepared plan; the workspace is used only when the plan splits.
+// conv: the product is that convolution's implicit GEMM (A the NHWC image,
+// B the filters stored N x K).
 int launch_splitk(const SplitPlan& sp, int64_t M, int64_t N, int64_t K, const float* A,
                   int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc,
-                  void* workspace, hipStream_t stream) {
+                  void* workspace, hipStream_t stream, const ConvGeom* conv = nullptr) {
     if (M == 0 || N == 0) return SGEMM_STATUS_SUCCESS;
     const ConfigEntry& c = kConfigs[sp.config];
     if (K == 0 || sp.splits == 1)
-        return launch_gemm(c.kernel, c.bm, c.bn, c.threads, M, N, K, A, lda, 0, B, ldb, 0, C,
-                           ldc, 0, 1, stream);
+        return launch_gemm(conv != nullptr ? c.conv : c.kernel, c.bm, c.bn, c.threads, M, N, K,
+                           A, lda, 0, B, ldb, 0, C, ldc, 0, 1, stream, 1.0f, 0.0f, conv);
     const int64_t tiles_m = ceil_div(M, c.bm), tiles_n = ceil_div(N, c.bn);
     const int64_t blocks = split_blocks(sp, tiles_m * tiles_n);
     GemmArgs p = {};
+    if (conv != nullptr) p.conv = *conv;
     p.A = A;
     p.B = B;
     p.C = C;
     p.lda = lda;
     p.ldb = ldb;
     p.ldc = ldc;
-    p.strideA = sp.kchunk;        // split b starts at column b * kchunk of A
-    p.strideB = sp.kchunk * ldb;  // and at row b * kchunk of B
+    // Split b starts at column b * kchunk of A (the convolution's gather
+    // adds it itself) and at row b * kchunk of B (column, for the filters).
+    p.strideA = conv != nullptr ? 0 : sp.kchunk;
+    p.strideB = conv != nullptr ? sp.kchunk : sp.kchunk * ldb;
     p.strideC = 0;
     p.M = (int)M;
     p.N = (int)N;
@@ -668,8 +697,8 @@ int launch_splitk(const SplitPlan& sp, int64_t M, int64_t N, int64_t K, const fl
     p.splits = (int)sp.splits;
     p.full_tiles = (int)sp.full_tiles;
     void* args[] = {&p};
-    hipError_t e = hipLaunchKernel(c.splitk, dim3((unsigned)blocks), dim3(c.threads), args, 0,
-                                   stream);
+    hipError_t e = hipLaunchKernel(conv != nullptr ? c.conv_splitk : c.splitk,
+                                   dim3((unsigned)blocks), dim3(c.threads), args, 0, stream);
     return e == hipSuccess ? SGEMM_STATUS_SUCCESS : SGEMM_STATUS_LAUNCH_FAILED;
 }
 
@@ -827,6 +856,25 @@ int conv_plan(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R, 
     return SGEMM_STATUS_SUCCESS;
 }
 
+ConvGeom conv_geom(int64_t H, int64_t W, int64_t C, int64_t S, int64_t pad_h, int64_t pad_w,
+                   int64_t stride_h, int64_t stride_w, int64_t dil_h, int64_t dil_w,
+                   const ConvPlan& pl) {
+    ConvGeom g;
+    g.H = (int)H;
+    g.W = (int)W;
+    g.C = (int)C;
+    g.P = (int)pl.P;
+    g.Q = (int)pl.Q;
+    g.S = (int)S;
+    g.pad_h = (int)pad_h;
+    g.pad_w = (int)pad_w;
+    g.stride_h = (int)stride_h;
+    g.stride_w = (int)stride_w;
+    g.dil_h = (int)dil_h;
+    g.dil_w = (int)dil_w;
+    return g;
+}
+
 int run_conv(int config, int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, int64_t R,
              int64_t S, int64_t pad_h, int64_t pad_w, int64_t stride_h, int64_t stride_w,
              int64_t dil_h, int64_t dil_w, const float* x, const float* w, float* y,
@@ -845,21 +893,58 @@ int run_conv(int config, int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, 
     if (x == nullptr || w == nullptr) return SGEMM_STATUS_NULL_POINTER;
     if (config < 0) config = choose_conv_config(pl.Mg, K, pl.Kg, C);
     const ConfigEntry& c = kConfigs[config];
-    ConvGeom g;
-    g.H = (int)H;
-    g.W = (int)W;
-    g.C = (int)C;
-    g.P = (int)pl.P;
-    g.Q = (int)pl.Q;
-    g.S = (int)S;
-    g.pad_h = (int)pad_h;
-    g.pad_w = (int)pad_w;
-    g.stride_h = (int)stride_h;
-    g.stride_w = (int)stride_w;
-    g.dil_h = (int)dil_h;
-    g.dil_w = (int)dil_w;
+    const ConvGeom g = conv_geom(H, W, C, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, pl);
     return launch_gemm(c.conv, c.bm, c.bn, c.threads, pl.Mg, K, pl.Kg, x, pl.Kg, 0, w, pl.Kg, 0, y,
                        K, 0, 1, stream, 1.0f, 0.0f, &g);
+}
+
+// The convolution's implicit GEMM with its reduction split as in
+// sgemm_splitk.  *sp gets the plan; nothing is enqueued.
+int plan_conv_splitk(int config, int64_t N, int64_t H, int64_t W, int64_t C, int64_t K,
+                     int64_t R, int64_t S, int64_t pad_h, int64_t pad_w, int64_t stride_h,
+                     int64_t stride_w, int64_t dil_h, int64_t dil_w, int64_t splits,
+                     ConvPlan* pl, SplitPlan* sp) {
+    const int st = conv_plan(N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w,
+                             pl);
+    if (st != SGEMM_STATUS_SUCCESS) return st;
+    if (config >= 0 && (config >= kNumConfigs || kConfigs[config].conv_splitk == nullptr))
+        return SGEMM_STATUS_INVALID_CONFIG;
+    if (splits < 0 || splits > kMaxSplits) return SGEMM_STATUS_INVALID_SIZE;
+    if (pl->Mg == 0 || K == 0 || pl->Kg == 0) {  // nothing to split
+        const int idx = config >= 0 ? config
+                                    : choose_conv_config(pl->Mg > 0 ? pl->Mg : 1, K > 0 ? K : 1,
+                                                         pl->Kg > 0 ? pl->Kg : 1, C);
+        *sp = SplitPlan{idx, 1, 0, 0, 0};
+        return SGEMM_STATUS_SUCCESS;
+    }
+    return plan_splitk(config, pl->Mg, K, pl->Kg, splits, sp, INT64_MAX, C);
+}
+
+int run_conv_splitk(int config, int64_t N, int64_t H, int64_t W, int64_t C, int64_t K,
+                    int64_t R, int64_t S, int64_t pad_h, int64_t pad_w, int64_t stride_h,
+                    int64_t stride_w, int64_t dil_h, int64_t dil_w, const float* x,
+                    const float* w, float* y, int64_t splits, void* workspace,
+                    int64_t workspace_bytes, hipStream_t stream) {
+    ConvPlan pl;
+    SplitPlan sp;
+    const int st = plan_conv_splitk(config, N, H, W, C, K, R, S, pad_h, pad_w, stride_h,
+                                    stride_w, dil_h, dil_w, splits, &pl, &sp);
+    if (st != SGEMM_STATUS_SUCCESS) return st;
+    if (pl.Mg == 0 || K == 0) return SGEMM_STATUS_SUCCESS;
+    if (y == nullptr) return SGEMM_STATUS_NULL_POINTER;
+    if (pl.Kg == 0)  // every output is the empty sum: +0
+        return launch_gemm(nullptr, 1, 1, 1, pl.Mg, K, 0, nullptr, 1, 0, nullptr, 1, 0, y, K, 0,
+                           1, stream);
+    if (x == nullptr || w == nullptr) return SGEMM_STATUS_NULL_POINTER;
+    if (sp.splits > 1) {
+        const ConfigEntry& c = kConfigs[sp.config];
+        const int64_t blocks = split_blocks(sp, ceil_div(pl.Mg, c.bm) * ceil_div(K, c.bn));
+        if (blocks > kMaxWorkItems / c.threads) return SGEMM_STATUS_SIZE_OVERFLOW;
+        if (workspace == nullptr || workspace_bytes < sp.ws_bytes)
+            return SGEMM_STATUS_INVALID_WORKSPACE;
+    }
+    const ConvGeom g = conv_geom(H, W, C, S, pad_h, pad_w, stride_h, stride_w, dil_h, dil_w, pl);
+    return launch_splitk(sp, pl.Mg, K, pl.Kg, x, pl.Kg, w, pl.Kg, y, K, workspace, stream, &g);
 }
 
 int run_valu(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, int64_t strideA,
@@ -1134,6 +1219,36 @@ int conv2d_select_config(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K, 
                              &pl);
     if (st != SGEMM_STATUS_SUCCESS) return st;
     return choose_conv_config(pl.Mg > 0 ? pl.Mg : 1, K > 0 ? K : 1, pl.Kg > 0 ? pl.Kg : 1, C);
+}
+
+int conv2d_nhwc_splitk(int config, int64_t N, int64_t H, int64_t W, int64_t C, int64_t K,
+                       int64_t R, int64_t S, int64_t pad_h, int64_t pad_w, int64_t stride_h,
+                       int64_t stride_w, int64_t dil_h, int64_t dil_w, const float* x,
+                       const float* wt, float* y, int64_t splits, void* workspace,
+                       int64_t workspace_bytes, hipStream_t stream) {
+    return run_conv_splitk(config, N, H, W, C, K, R, S, pad_h, pad_w, stride_h, stride_w, dil_h,
+                           dil_w, x, wt, y, splits, workspace, workspace_bytes, stream);
+}
+
+int64_t conv2d_nhwc_splitk_plan(int config, int64_t N, int64_t H, int64_t W, int64_t C,
+                                int64_t K, int64_t R, int64_t S, int64_t pad_h, int64_t pad_w,
+                                int64_t stride_h, int64_t stride_w, int64_t dil_h,
+                                int64_t dil_w, int64_t splits, int* plan_config,
+                                int64_t* plan_splits, int64_t* plan_full_tiles) {
+    ConvPlan pl;
+    SplitPlan sp;
+    const int st = plan_conv_splitk(config, N, H, W, C, K, R, S, pad_h, pad_w, stride_h,
+                                    stride_w, dil_h, dil_w, splits, &pl, &sp);
+    if (st != SGEMM_STATUS_SUCCESS) return st;
+    if (plan_config != nullptr) *plan_config = sp.config;
+    if (plan_splits != nullptr) *plan_splits = sp.splits;
+    if (plan_full_tiles != nullptr) *plan_full_tiles = sp.splits > 1 ? sp.full_tiles : 0;
+    return sp.splits > 1 ? sp.ws_bytes : 0;
+}
+
+int conv2d_config_has_splitk(int config) {
+    if (config < 0 || config >= kNumConfigs) return SGEMM_STATUS_INVALID_CONFIG;
+    return kConfigs[config].conv_splitk != nullptr ? 1 : 0;
 }
 
 const char* sgemm_status_string(int status) {
