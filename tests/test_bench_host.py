@@ -64,6 +64,12 @@ def test_conv_summaries_are_named_by_entry_point():
         os.path.join("profiles", "conv2d_conv3x3_c256_counters.txt"))
     assert bench.conv_traffic_file("splitk", "conv3x3_c256").endswith(
         os.path.join("profiles", "conv2d_splitk_conv3x3_c256_counters.txt"))
+    for path in ("mfma", "splitk"):
+        f = bench.conv_traffic_file(path, "conv3x3_c256")
+        assert os.path.exists(f), f
+        with open(f) as fh:
+            text = fh.read()
+        assert "beyond_l2_bytes_per_launch:" in text and "kernel_source_sha256_16:" in text, f
 
 
 def test_conv_rejects_gemm_only_paths(capsys):
