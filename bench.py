@@ -68,13 +68,16 @@ def gemm_metric(w) -> str:
     return "FP32 GEMM TFLOP/s at %s on 1 MI355X; %% of FP32 peak" % shape
 
 
-# Device sources each kernel family is compiled from.  A counter summary is
-# used only while these hash to the value recorded in it and it names the tile
-# the run uses (the tile's template arguments live in the host table).
-GEMM_SOURCES = ("tile_common.hpp", "mfma_dl_kernel.hpp", "mfma_kernel.hpp", "valu_kernel.hpp")
+# Sources each kernel family is compiled from, the host table that gives the
+# tiles their template arguments included.  A counter summary is used only
+# while these hash to the value recorded in it and it names the tile the run
+# uses.
+GEMM_SOURCES = ("tile_common.hpp", "mfma_dl_kernel.hpp", "mfma_kernel.hpp", "valu_kernel.hpp",
+                "sgemm.hip")
 WINDOW_SOURCES = ("window.hip", "window_kernel.hpp", "tile_common.hpp")
 WINDOW_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "window_sum_window5_counters.txt")
-ATTN_SOURCES = ("attention_kernel.hpp", "mfma_dl_kernel.hpp", "mfma_kernel.hpp", "tile_common.hpp")
+ATTN_SOURCES = ("attention.hip", "attention_kernel.hpp", "mfma_dl_kernel.hpp", "mfma_kernel.hpp",
+                "tile_common.hpp")
 ATTN_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_attn_s2048_d128_counters.txt")
 
 

@@ -137,6 +137,30 @@ def test_graph_splitk():
     assert torch.count_nonzero(ws[:sg.SPLITK_HEADER_BYTES]).item() == 0
 
 
+def test_graph_hybrid_splitk_and_conv():
+    """Hybrid plans (whole tiles plus the chunks of the last partial layer),
+    a product and a convolution, captured on one workspace."""
+    dev = _dev()
+    gen = torch.Generator(device=dev).manual_seed(17)
+    M, N, K = 3300, 300, 1000
+    assert sg.splitk_plan_full_tiles(M, N, K) > 0
+    A = torch.randn(M, K, device=dev, generator=gen)
+    B = torch.randn(K, N, device=dev, generator=gen)
+    C = torch.empty(M, N, device=dev)
+    xi = torch.randn(40, 15, 15, 96, device=dev, generator=gen)
+    wt = torch.randn(96, 3, 3, 96, device=dev, generator=gen)
+    yc = torch.empty(40, 15, 15, 96, device=dev)
+    plan = sg.conv2d_splitk_plan(40, 15, 15, 96, 96, 3, 3, 1)
+    assert plan[1] > 1 and plan[3] > 0
+    ws = torch.zeros(max(sg.splitk_plan(M, N, K)[2], plan[2]), dtype=torch.uint8, device=dev)
+
+    def capture():
+        sg.sgemm_splitk(A, B, C, workspace=ws)
+        sg.conv2d_nhwc_splitk(xi, wt, pad=1, out=yc, workspace=ws)
+    _replays_match(capture, [C, yc], _other_work(dev))
+    assert torch.count_nonzero(ws[:sg.SPLITK_HEADER_BYTES]).item() == 0
+
+
 def test_host_threads_on_their_own_streams():
     """The library keeps no mutable global state: four host threads, each on
     its own stream, calling different entry points at once, give the same

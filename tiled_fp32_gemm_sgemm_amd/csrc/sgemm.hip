@@ -134,8 +134,16 @@ using Dl128x128k64m32w4x2 =
     DlTile<128, 128, 64, 4, 2, 32, 2, 8, 2, 1, true, false, false, false, true, false, 2>;
 // Small LDS footprints, so that three or four workgroups share a CU and
 // their barriers fall at different times (4 waves of 64x64 or 32x32 each).
-using Dl128x128k16o4 = DlTile<128, 128, 16, 2, 2, 32, 4, 8, 2>;     // 32 KB LDS, 4 per CU
-using Dl128x128k16o3s3 = DlTile<128, 128, 16, 2, 2, 32, 3, 8, 3>;   // 48 KB LDS, 3 per CU
+// The 128 x 128 x 16 tiles spread their copies over the k steps (schedule
+// 2): batched 1024 x 128^3 41.9 -> 40.6 us, 8192^2 x 128 152.2 -> 145.7 us,
+// 16 x 3000 x 512 x 128 on the three-stage tile 63.1 -> 55.9 us, and level to
+// 1 % slower on the rest of the shapes that choose them.  The 64 x 64 x 32
+// tile keeps the burst: spread, it ran 1.4-3.4 % slower (its split-K variant
+// and hybrid plans included).
+using Dl128x128k16o4 =  // 32 KB LDS, 4 per CU
+    DlTile<128, 128, 16, 2, 2, 32, 4, 8, 2, 1, true, false, false, false, true, false, 2>;
+using Dl128x128k16o3s3 =  // 48 KB LDS, 3 per CU
+    DlTile<128, 128, 16, 2, 2, 32, 3, 8, 3, 1, true, false, false, false, true, false, 2>;
 using Dl64x64k32o4 = DlTile<64, 64, 32, 2, 2, 32, 4, 8, 2>;         // 32 KB LDS, 4 per CU
 // Control build: A stored unswizzled (bank conflicts on purpose); never chosen.
 using Dl256x256k32m32Plain = DlTile<256, 256, 32, 2, 4, 32, 2, 8, 2, 1, false>;
