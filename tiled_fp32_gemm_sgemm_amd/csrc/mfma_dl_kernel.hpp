@@ -167,6 +167,15 @@ struct DlTile {
     // and by the 160 KB of LDS.
     static constexpr int WG_PER_CU = (4 * OCC * 64 / NT) < (160 * 1024 / LDS_BYTES)
                                          ? (4 * OCC * 64 / NT) : (160 * 1024 / LDS_BYTES);
+    // Spread copies issued from a main loop specialised for whole direct
+    // slices: buffer descriptors built once per slice, no branch per copy.
+    // Taken by tiles that run one workgroup per CU (512 x 4096 x 4096: 123.0
+    // -> 120.5 us; 1024^3 19.5 -> 19.15; 2048^3 121.5 -> 119.7).  Tiles that
+    // share a CU between several workgroups keep the branch per copy: with
+    // the copies issued back to back after the k steps they ran 4-15 % slower
+    // (batched 1024 x 128^3 39.6 -> 41.0 us, 8192^2 x 128 134 -> 155), and
+    // no placement of them inside the slice recovered it on every shape.
+    static constexpr bool HOIST_SPREAD = SPREAD_COPIES && WG_PER_CU == 1;
 
     static_assert(MI == 16 || MI == 32, "MFMA tile edge");
     static_assert(BK == 16 || BK == 32 || BK == 64 || BK == 128, "BK must be 16, 32, 64 or 128");
@@ -703,13 +712,32 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     // `more` is a compile-time flag: the last slice is peeled off the loop so
     // that no control-flow join sits in front of the held MFMAs (at a join the
     // compiler's LDS wait would also cover the next slice's fresh reads).
-    auto slice = [&](auto more_tag, int buf, int s) {
+    // `hoisted_tag` (HOIST_SPREAD tiles only): the caller has checked that
+    // slice s + STAGES - 1 is a whole direct slice, so its copies go out one
+    // per k step through descriptors built once, at the top of the slice.
+    auto slice = [&](auto more_tag, auto hoisted_tag, int buf, int s) {
         constexpr bool more = decltype(more_tag)::value;
+        constexpr bool HOISTED = decltype(hoisted_tag)::value;
         const int ahead = s + T::STAGES - 1;
         // Copies of a direct slice spread over the k steps (SCHED = 2); a
         // register-staged slice is copied whole at the start.
-        const bool spread = T::SPREAD_COPIES && more && direct_ok && ahead < full_slices;
-        if (more && ahead < nslices && !spread) load_slice(ahead);
+        const bool spread = T::SPREAD_COPIES && !T::HOIST_SPREAD && more && direct_ok &&
+                            ahead < full_slices;
+        if (more && ahead < nslices && !HOISTED && !spread) load_slice(ahead);
+        __amdgpu_buffer_rsrc_t hs_ra, hs_rb;
+        float* hs_dst = smem;
+        if constexpr (HOISTED) {
+            const int64_t k0 = (int64_t)ahead * T::BK;
+            const float* const a_base =
+                p.A + uniform_i64(a_org + (T::A_KC ? k0 : k0 * p.lda));
+            const float* const b_base =
+                p.B + uniform_i64(b_org + (T::B_KC ? k0 : k0 * p.ldb));
+            hs_ra = __builtin_amdgcn_make_buffer_rsrc((void*)a_base, (short)0, (int)a_span,
+                                                      0x00020000);
+            hs_rb = __builtin_amdgcn_make_buffer_rsrc((void*)b_base, (short)0, (int)b_span,
+                                                      0x00020000);
+            hs_dst = smem + (ahead % T::STAGES) * T::BUF_FLOATS;
+        }
 #pragma unroll
         for (int g = 0; g < T::NKG; ++g) {
             const int s1 = g + 1 < T::NKG ? T::KG : T::KG - T::HOLD;
@@ -727,7 +755,22 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
                         else
                             read_part(buf, g + 1, st, opa[1], opb[1]);
                     }
-                    if constexpr (T::SPREAD_COPIES) {
+                    if constexpr (HOISTED) {
+                        // Copy j = this k step's index, as load_direct_part
+                        // issues it.
+                        const int j = g * T::KG + st;
+                        if (j < T::A_CHW)
+                            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                                hs_ra, (lds_void_t*)(hs_dst + 256 * (wave * T::A_CHW + j)), 16,
+                                a_off[j < T::A_CHW ? j : 0], 0, 0, 0);
+                        else if (j < T::LPS)
+                            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                                hs_rb,
+                                (lds_void_t*)(hs_dst + T::A_FLOATS +
+                                              256 * (wave * T::B_CHW + j - T::A_CHW)),
+                                16, b_off[j >= T::A_CHW && j < T::LPS ? j - T::A_CHW : 0], 0,
+                                0, 0);
+                    } else if constexpr (T::SPREAD_COPIES) {
                         const int step = g * T::KG + st;
                         if (spread && step < T::LPS)
                             load_direct_part(ahead * T::BK, ahead % T::STAGES, step, step + 1);
@@ -777,8 +820,15 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
     wait_slice(0, (T::STAGES - 1 < nslices ? T::STAGES - 1 : nslices) - 1);
     lds_barrier();
     read_group(0, 0, opa[0], opb[0]);
-    for (int s = 0; s + 1 < nslices; ++s) slice(std::true_type(), s % T::STAGES, s);
-    slice(std::false_type(), (nslices - 1) % T::STAGES, nslices - 1);
+    int s = 0;
+    if constexpr (T::HOIST_SPREAD) {
+        // Slices whose slice ahead is a whole direct slice: every slice but
+        // the last STAGES - 1 when BK divides K and the slices copy directly.
+        const int s_end = direct_ok ? min(nslices - 1, full_slices - (T::STAGES - 1)) : 0;
+        for (; s < s_end; ++s) slice(std::true_type(), std::true_type(), s % T::STAGES, s);
+    }
+    for (; s + 1 < nslices; ++s) slice(std::true_type(), std::false_type(), s % T::STAGES, s);
+    slice(std::false_type(), std::false_type(), (nslices - 1) % T::STAGES, nslices - 1);
 
     // k groups 1..KSPLIT-1 hand their partial sums to group 0 through LDS
     // (lane-contiguous 16-byte records, conflict-free); group 0 adds them in
