@@ -411,6 +411,17 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
             req = val["TCP_TCC_READ_REQ_sum"]
             L.append("l2_read_request_bytes_at_128B: %.0f (%.4f x the global-to-LDS model)"
                      % (req * 128, req * 128 / (4.0 * staged)))
+            nreq = model.l2_read_requests(w.M, w.N, w.K, info["bm"], info["bn"], info["bk"],
+                                          w.batch, w.lda, w.ldb)
+            what = "per tile and slice, the 128-byte lines each valid row piece of A and B touches"
+            if n_split > 1:
+                # the join reads every split tile's partials once, in whole lines
+                tiles = model.ceil_div(w.M, info["bm"]) * model.ceil_div(w.N, info["bn"])
+                full = sg.splitk_plan_full_tiles(w.M, w.N, w.K, splits)
+                nreq += (tiles - full) * n_split * info["bm"] * info["bn"] * 4 // 128
+                what += ", plus the join's reads of the partial tiles"
+            L.append("l2_read_requests_model: %d (%s)" % (nreq, what))
+            L.append("l2_read_requests_over_model: %.4f" % (req / nreq))
         resident = 32 * sg.workgroups_per_cu(cfg)
         # Split-K: chunk b of every tile runs as batch member b over K / chunks.
         panels = model.per_xcd_operand_bytes(w.M, w.N, model.ceil_div(w.K, n_split), info["bm"],

@@ -129,3 +129,33 @@ def test_convolution_useful_flops_by_brute_force():
     # 14 x 14, 3 x 3, pad 1: 40 of 42 taps per axis land inside, 1600 / 1764.
     w = ConvWorkload("t", 64, 14, 14, 256, 256, 3, 3, (1, 1), (1, 1), (1, 1), 0)
     assert w.useful_flops * 1764 == w.flops * 1600
+
+
+def test_l2_read_requests_by_enumeration():
+    # Whole-line, line-aligned row pieces: the count is the staged bytes / 128.
+    for (M, N, K, BM, BN, BK) in ((4096, 4096, 4096, 256, 256, 32), (512, 512, 1024, 64, 64, 128)):
+        staged = model.global_to_shared_loads(M, N, K, BM, BN, BK, padded=True)
+        assert model.l2_read_requests(M, N, K, BM, BN, BK) * 128 == 4 * staged
+
+    # Brute force: the set of 128-byte lines holding each valid element a
+    # tile reads, per tile and slice, A and B separately.
+    def enumerate_requests(M, N, K, BM, BN, BK, batch, lda, ldb):
+        total = 0
+        for tm in range(-(-M // BM)):
+            for tn in range(-(-N // BN)):
+                for k0 in range(0, K, BK):
+                    ks = range(k0, min(k0 + BK, K))
+                    for r in range(tm * BM, min(tm * BM + BM, M)):
+                        total += len({(4 * (r * lda + k)) // 128 for k in ks})
+                    for k in ks:
+                        total += len({(4 * (k * ldb + n)) // 128
+                                      for n in range(tn * BN, min(tn * BN + BN, N))})
+        return total * batch
+    for shape in ((128, 128, 128, 128, 128, 16, 3, 128, 128), (70, 90, 50, 32, 64, 16, 1, 53, 97),
+                  (65, 33, 40, 64, 32, 32, 2, 43, 35), (40, 64, 200, 32, 32, 64, 1, 203, 67)):
+        assert model.l2_read_requests(*shape) == enumerate_requests(*shape), shape
+    # The batched 1024 x 128^3 product on 128 x 128 x 16 tiles: 1.5 requests
+    # per 128 staged bytes (A rows of 64 bytes).
+    staged = model.global_to_shared_loads(128, 128, 128, 128, 128, 16, padded=True) * 1024
+    assert Fraction(model.l2_read_requests(128, 128, 128, 128, 128, 16, 1024) * 128,
+                    4 * staged) == Fraction(3, 2)

@@ -61,6 +61,36 @@ def global_to_shared_loads(M: int, N: int, K: int, BM: int, BN: int, BK: int | N
     return tiles * ceil_div(K, BK) * (BM + BN) * BK
 
 
+def l2_read_requests(M: int, N: int, K: int, BM: int, BN: int, BK: int, batch: int = 1,
+                     lda: int | None = None, ldb: int | None = None, line: int = 128,
+                     elem: int = 4) -> int:
+    """Read requests from the vector L1 to L2 for the staging of
+    `global_to_shared_loads`: each tile reads, per BK slice, the valid part
+    of each of its BM rows of A (k in [k0, min(k0 + BK, K))) and of each of
+    the slice's rows of B (its valid BN columns), one request per `line`
+    bytes each piece touches.  Rows start at multiples of lda (ldb) elements
+    from a line-aligned base, so a piece that straddles a line costs one
+    request more, and a piece shorter than a line (a BK = 16 slice reads 64
+    bytes of each A row) costs a whole one.  Every tile of a tile row reads
+    its A panel and every tile of a tile column its B panel."""
+    import numpy as np
+    lda = K if lda is None else lda
+    ldb = N if ldb is None else ldb
+    k0 = np.arange(0, K, BK, dtype=np.int64)
+    kend = np.minimum(k0 + BK, K)
+    r = np.arange(M, dtype=np.int64)[:, None]
+    first = (r * lda + k0[None, :]) * elem // line
+    last = ((r * lda + kend[None, :]) * elem - 1) // line
+    a = int(np.sum(last - first + 1)) * ceil_div(N, BN)
+    n0 = np.arange(0, N, BN, dtype=np.int64)
+    nend = np.minimum(n0 + BN, N)
+    k = np.arange(K, dtype=np.int64)[:, None]
+    first = (k * ldb + n0[None, :]) * elem // line
+    last = ((k * ldb + nend[None, :]) * elem - 1) // line
+    b = int(np.sum(last - first + 1)) * ceil_div(M, BM)
+    return (a + b) * batch
+
+
 def shared_to_register_loads(M: int, N: int, K: int, WM: int, WN: int) -> int:
     """Values read from shared staging into registers: each register tile of
     WM x WN outputs reads WM + WN values per k step ("CMU DLSys Lecture 12",
