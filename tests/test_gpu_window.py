@@ -49,8 +49,12 @@ def _vals(n, W, seed, dist):
     return draw(gen, n + W - 1, dist)
 
 
-@pytest.mark.parametrize("W", [1, 2, 3, 5, 17, 64, 255, 1023, 1024])
-@pytest.mark.parametrize("n", [1, 3, 4, 5, 4095, 4096, 4097, 12289, 100003])
+# Widths on both sides of 16 (the last one the narrow-window kernel takes,
+# 1024 outputs per workgroup; wider ones take 4096), and lengths around both
+# block sizes.
+@pytest.mark.parametrize("W", [1, 2, 3, 5, 16, 17, 64, 255, 1023, 1024])
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 1023, 1024, 1025, 2049, 4095, 4096, 4097, 12289,
+                               100003])
 def test_window_integer_bitwise(n, W):
     v = _vals(n, W, n + 7 * W, "int4")
     got = run_window(n, W, v)

@@ -8,19 +8,25 @@
 
 #include "window_kernel.hpp"
 
+template <int QUADS>
+int launch_window(int64_t n, int W, const float* x, float* y, hipStream_t stream) {
+    using WT = sgemm_dev::WindowTile<QUADS>;
+    const int64_t blocks = (n + WT::T - 1) / WT::T;
+    // A dispatch counts its work-items in 32 bits.
+    if (blocks > (int64_t)UINT32_MAX / WT::NT) return SGEMM_STATUS_SIZE_OVERFLOW;
+    void* args[] = {&x, &y, &n, &W};
+    const hipError_t e = hipLaunchKernel((const void*)&sgemm_dev::window_sum_kernel<QUADS>,
+                                         dim3((unsigned)blocks), dim3(WT::NT), args, 0, stream);
+    return e == hipSuccess ? SGEMM_STATUS_SUCCESS : SGEMM_STATUS_LAUNCH_FAILED;
+}
+
 extern "C" int window_sum(int64_t n, int64_t W, const float* x, float* y, hipStream_t stream) {
-    using sgemm_dev::WindowTile;
-    if (n < 0 || W < 1 || W > WindowTile::MAX_W) return SGEMM_STATUS_INVALID_SIZE;
+    if (n < 0 || W < 1 || W > sgemm_dev::WindowTile<1>::MAX_W) return SGEMM_STATUS_INVALID_SIZE;
     if (n == 0) return SGEMM_STATUS_SUCCESS;
     if (n > INT64_MAX - W) return SGEMM_STATUS_SIZE_OVERFLOW;
-    const int64_t blocks = (n + WindowTile::T - 1) / WindowTile::T;
-    // A dispatch counts its work-items in 32 bits.
-    if (blocks > (int64_t)UINT32_MAX / WindowTile::NT) return SGEMM_STATUS_SIZE_OVERFLOW;
     if (x == nullptr || y == nullptr) return SGEMM_STATUS_NULL_POINTER;
-    int w = (int)W;
-    void* args[] = {&x, &y, &n, &w};
-    const hipError_t e = hipLaunchKernel((const void*)&sgemm_dev::window_sum_kernel,
-                                         dim3((unsigned)blocks), dim3(WindowTile::NT), args, 0,
-                                         stream);
-    return e == hipSuccess ? SGEMM_STATUS_SUCCESS : SGEMM_STATUS_LAUNCH_FAILED;
+    // Narrow windows: 1024 outputs per workgroup; wider ones 4096, where the
+    // halo is a smaller share of each block's inputs.
+    return W <= sgemm_dev::kWindowNarrowMax ? launch_window<1>(n, (int)W, x, y, stream)
+                                            : launch_window<4>(n, (int)W, x, y, stream);
 }

@@ -7,14 +7,22 @@
 //
 // gfx950 shape of the same idea.  The work is a few additions per value, so
 // it is bound by HBM bandwidth (8 bytes per output), not by arithmetic:
-//  * A workgroup of 256 lanes owns T = 4096 consecutive outputs; lane t owns
-//    the quads of outputs 4t + 1024j (j = 0..3), so every 16-byte store of a
-//    wave covers 1 KB of y contiguously.
+//  * A workgroup of 256 lanes owns T = 1024 * QUADS consecutive outputs;
+//    lane t owns the quads of outputs 4t + 1024j (j < QUADS), so every
+//    16-byte store of a wave covers 1 KB of y contiguously.  Narrow windows
+//    (W <= 16) take QUADS = 1: more workgroups, so more of their copies are
+//    in flight at once (W = 5: 5.87 -> 6.5 TB/s against QUADS = 4); wider
+//    ones QUADS = 4, where the W - 1 halo is a smaller share of each block
+//    (W = 33: 4.56 with QUADS = 1, 4.83 with 4).
 //  * The block's T + W - 1 input values are copied straight into LDS with
 //    buffer_load_dwordx4 ... lds (1 KB per wave instruction, no VGPR staging).
 //    The buffer descriptor's range ends at the last valid input, so the
 //    buffer unit returns zeros past it: the lecture's guard against n + W - 1,
 //    done by the hardware.
+//  * Every input and output is touched once, so the copies carry the
+//    non-temporal hint (cache-policy bit 1, `nt`) and the 16-byte stores are
+//    non-temporal: the streams do not displace other lines on their way
+//    through the caches (W = 5 at QUADS = 4: 5.87 -> 6.2 TB/s).
 //  * Each lane sums its four outputs from 16-byte quads of the staged span:
 //    quad q holds x[o+4q .. o+4q+3], so the four values of step d come from
 //    quads d/4 and d/4 + 1, and (W + 3) / 4 + 1 ds_read_b128 serve all W
@@ -28,9 +36,10 @@
 
 namespace sgemm_dev {
 
+template <int QUADS_>
 struct WindowTile {
     static constexpr int NT = 256;                 // lanes per workgroup
-    static constexpr int QUADS = 4;                // output quads per lane
+    static constexpr int QUADS = QUADS_;           // output quads per lane
     static constexpr int T = NT * 4 * QUADS;       // outputs per workgroup
     static constexpr int MAX_W = 1024;             // widest window supported
     static constexpr int CHUNK = 256;              // floats per direct-copy wave instruction
@@ -41,8 +50,13 @@ struct WindowTile {
 
 typedef __attribute__((address_space(3))) void lds_void_w;
 
+// Widest window the narrow-window kernel takes.
+constexpr int kWindowNarrowMax = 16;
+// Cache-policy operand of the copies: bit 1 is the non-temporal hint.
+constexpr int kWindowLoadNt = 2;
+
+template <class WT>
 __device__ __forceinline__ void window_sum_body(const float* x, float* y, int64_t n, int W) {
-    using WT = WindowTile;
     __shared__ __attribute__((aligned(16))) float tile[WT::TILE];
 
     const int tid = threadIdx.x;
@@ -60,7 +74,8 @@ __device__ __forceinline__ void window_sum_body(const float* x, float* y, int64_
         __builtin_amdgcn_make_buffer_rsrc((void*)(x + base), (short)0, count * 4, 0x00020000);
     for (int c = wave; c < chunks; c += WT::NT / 64)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_void_w*)(tile + WT::CHUNK * c), 16,
-                                                 (WT::CHUNK * c + 4 * lane) * 4, 0, 0, 0);
+                                                 (WT::CHUNK * c + 4 * lane) * 4, 0, 0,
+                                                 kWindowLoadNt);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
@@ -84,15 +99,18 @@ __device__ __forceinline__ void window_sum_body(const float* x, float* y, int64_
             }
             cur = nxt;
         }
-        const f32x4 v = acc;
         const int64_t left = n - (base + o);
-        stg4_masked(y + base + o, v, left >= 4 ? 4 : (int)left);
+        if (left >= 4)
+            __builtin_nontemporal_store((f32x4_u)acc, (f32x4_u*)(y + base + o));
+        else
+            stg4_masked(y + base + o, acc, (int)left);
     }
 }
 
-__global__ __launch_bounds__(WindowTile::NT) void window_sum_kernel(const float* x, float* y,
-                                                                    int64_t n, int W) {
-    window_sum_body(x, y, n, W);
+template <int QUADS>
+__global__ __launch_bounds__(256) void window_sum_kernel(const float* x, float* y, int64_t n,
+                                                         int W) {
+    window_sum_body<WindowTile<QUADS>>(x, y, n, W);
 }
 
 }  // namespace sgemm_dev
