@@ -149,12 +149,13 @@ def test_batch_split_over_launches(path):
     assert bool((C[batch:] == SENTINEL).all().item())
 
 
-def test_window_sum_beyond_2_31_elements():
+@pytest.mark.parametrize("W", [5, 33])
+def test_window_sum_beyond_2_31_elements(W):
     """n = 2^31 + 4101 window sums of integers: exact.  Output ranges at the
     start, across element 2^31 and at the end, against the oracle on the same
-    stretch of x."""
+    stretch of x; a narrow and a wide window (the two block sizes)."""
     dev = _dev()
-    n, W = 2 ** 31 + 4101, 5
+    n = 2 ** 31 + 4101
     x = device_operand(1, 1, n + W - 1, n + W - 1, 0, seed=29, device=dev)
     y = torch.full((n + 64,), SENTINEL, device=dev)
     st = sg.window_sum_raw(n, W, x.data_ptr(), y.data_ptr(),

@@ -71,13 +71,14 @@ def test_window_uniform_tolerance(n, W):
     parity.assert_within_tolerance(got, ref, mag, "window uniform n=%d W=%d" % (n, W))
 
 
+@pytest.mark.parametrize("W", [5, 33])
 @pytest.mark.parametrize("x_off,y_off", [(1, 0), (2, 3), (3, 1)])
-def test_window_unaligned_pointers(x_off, y_off):
-    n, W = 9001, 5
+def test_window_unaligned_pointers(x_off, y_off, W):
+    n = 9001
     v = _vals(n, W, 17, "int4")
     got = run_window(n, W, v, x_off, y_off)
     ref, _ = oracle.window_sum_f64(n, W, v.numpy())
-    parity.assert_bitwise(got, ref, "window offsets %d %d" % (x_off, y_off))
+    parity.assert_bitwise(got, ref, "window offsets %d %d W=%d" % (x_off, y_off, W))
 
 
 def test_window_worked_example():
