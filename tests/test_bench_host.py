@@ -202,3 +202,12 @@ def test_counter_summary_derivations(tmp_path):
     v = summary([str(tmp_path / "s2.csv")])
     assert v["grbm_clock_ghz_counter_run"].startswith("omitted")
     assert v["fetch_scale_check"].startswith("1.0000")
+    # L1 -> L2 read requests against the line model of the chosen tile
+    import tiled_fp32_gemm_sgemm_amd as sg
+    from tiled_fp32_gemm_sgemm_amd import model
+    info = sg.config_info(sg.select_config(1024, 1024, 1024, 1))
+    nreq = model.l2_read_requests(1024, 1024, 1024, info["bm"], info["bn"], info["bk"])
+    _counter_csv(tmp_path / "s3.csv", [(2, k, "TCP_TCC_READ_REQ_sum", 1.5 * nreq, 0, 25000)])
+    v = summary([str(tmp_path / "s3.csv")])
+    assert v["l2_read_requests_model"].startswith("%d " % nreq)
+    assert v["l2_read_requests_over_model"].startswith("1.5000")
