@@ -25,7 +25,8 @@ extern "C" {
  * Returns 0; SGEMM_STATUS_INVALID_SIZE for n < 0, W < 1 or W > 1024;
  * SGEMM_STATUS_SIZE_OVERFLOW when n + W - 1 overflows or the launch would need
  * more than 2^32 - 1 work-items (blocks of 256 lanes hold 1024 outputs for
- * W <= 16 and 4096 for wider windows: n above about 1.7e10 or 6.9e10);
+ * W <= 8, 2048 for W <= 24 and 4096 for wider windows: n above about 1.7e10,
+ * 3.4e10 or 6.9e10);
  * SGEMM_STATUS_NULL_POINTER for a NULL x or y with n > 0;
  * SGEMM_STATUS_LAUNCH_FAILED if HIP rejects the launch.  n == 0 enqueues
  * nothing.

@@ -149,11 +149,11 @@ def test_batch_split_over_launches(path):
     assert bool((C[batch:] == SENTINEL).all().item())
 
 
-@pytest.mark.parametrize("W", [5, 33])
+@pytest.mark.parametrize("W", [5, 17, 33])
 def test_window_sum_beyond_2_31_elements(W):
     """n = 2^31 + 4101 window sums of integers: exact.  Output ranges at the
     start, across element 2^31 and at the end, against the oracle on the same
-    stretch of x; a narrow and a wide window (the two block sizes)."""
+    stretch of x; one window width per block size."""
     dev = _dev()
     n = 2 ** 31 + 4101
     x = device_operand(1, 1, n + W - 1, n + W - 1, 0, seed=29, device=dev)

@@ -49,11 +49,10 @@ def _vals(n, W, seed, dist):
     return draw(gen, n + W - 1, dist)
 
 
-# Widths on both sides of 16 (the last one the narrow-window kernel takes,
-# 1024 outputs per workgroup; wider ones take 4096), and lengths around both
-# block sizes.
-@pytest.mark.parametrize("W", [1, 2, 3, 5, 16, 17, 64, 255, 1023, 1024])
-@pytest.mark.parametrize("n", [1, 3, 4, 5, 1023, 1024, 1025, 2049, 4095, 4096, 4097, 12289,
+# Widths on both sides of 8 and 24 (the widest windows of the blocks of 1024
+# and 2048 outputs; wider ones take 4096), and lengths around the block sizes.
+@pytest.mark.parametrize("W", [1, 2, 3, 5, 8, 9, 16, 24, 25, 64, 255, 1023, 1024])
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 1023, 1024, 1025, 2047, 2049, 4095, 4096, 4097, 12289,
                                100003])
 def test_window_integer_bitwise(n, W):
     v = _vals(n, W, n + 7 * W, "int4")
@@ -71,7 +70,7 @@ def test_window_uniform_tolerance(n, W):
     parity.assert_within_tolerance(got, ref, mag, "window uniform n=%d W=%d" % (n, W))
 
 
-@pytest.mark.parametrize("W", [5, 33])
+@pytest.mark.parametrize("W", [5, 17, 33])
 @pytest.mark.parametrize("x_off,y_off", [(1, 0), (2, 3), (3, 1)])
 def test_window_unaligned_pointers(x_off, y_off, W):
     n = 9001

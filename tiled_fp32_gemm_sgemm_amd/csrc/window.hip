@@ -25,8 +25,9 @@ extern "C" int window_sum(int64_t n, int64_t W, const float* x, float* y, hipStr
     if (n == 0) return SGEMM_STATUS_SUCCESS;
     if (n > INT64_MAX - W) return SGEMM_STATUS_SIZE_OVERFLOW;
     if (x == nullptr || y == nullptr) return SGEMM_STATUS_NULL_POINTER;
-    // Narrow windows: 1024 outputs per workgroup; wider ones 4096, where the
-    // halo is a smaller share of each block's inputs.
-    return W <= sgemm_dev::kWindowNarrowMax ? launch_window<1>(n, (int)W, x, y, stream)
-                                            : launch_window<4>(n, (int)W, x, y, stream);
+    // Outputs per workgroup by window width: more, smaller blocks for narrow
+    // windows; larger ones where the halo is a bigger share of the inputs.
+    if (W <= sgemm_dev::kWindowQuads1Max) return launch_window<1>(n, (int)W, x, y, stream);
+    if (W <= sgemm_dev::kWindowQuads2Max) return launch_window<2>(n, (int)W, x, y, stream);
+    return launch_window<4>(n, (int)W, x, y, stream);
 }

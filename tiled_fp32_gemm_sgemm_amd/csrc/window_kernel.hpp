@@ -9,11 +9,13 @@
 // it is bound by HBM bandwidth (8 bytes per output), not by arithmetic:
 //  * A workgroup of 256 lanes owns T = 1024 * QUADS consecutive outputs;
 //    lane t owns the quads of outputs 4t + 1024j (j < QUADS), so every
-//    16-byte store of a wave covers 1 KB of y contiguously.  Narrow windows
-//    (W <= 16) take QUADS = 1: more workgroups, so more of their copies are
-//    in flight at once (W = 5: 5.87 -> 6.5 TB/s against QUADS = 4); wider
-//    ones QUADS = 4, where the W - 1 halo is a smaller share of each block
-//    (W = 33: 4.56 with QUADS = 1, 4.83 with 4).
+//    16-byte store of a wave covers 1 KB of y contiguously.  Small blocks
+//    put more workgroups, and so more copies, in flight at once; large ones
+//    make the W - 1 halo a smaller share of each block's inputs.  Measured
+//    on 2^28 outputs (TB/s for QUADS = 1 / 2 / 4): W = 5: 6.61 / 6.45 / 6.28;
+//    W = 9: 6.42 / 6.45 / 6.18; W = 17: 5.97 / 6.43 / 6.20; W = 24: 5.65 /
+//    5.90 / 5.89; W = 33: 4.67 / 4.87 / 4.89.  So QUADS = 1 up to W = 8, 2 up
+//    to W = 24, 4 beyond.
 //  * The block's T + W - 1 input values are copied straight into LDS with
 //    buffer_load_dwordx4 ... lds (1 KB per wave instruction, no VGPR staging).
 //    The buffer descriptor's range ends at the last valid input, so the
@@ -50,8 +52,9 @@ struct WindowTile {
 
 typedef __attribute__((address_space(3))) void lds_void_w;
 
-// Widest window the narrow-window kernel takes.
-constexpr int kWindowNarrowMax = 16;
+// Widest windows of the 1024- and 2048-output blocks.
+constexpr int kWindowQuads1Max = 8;
+constexpr int kWindowQuads2Max = 24;
 // Cache-policy operand of the copies: bit 1 is the non-temporal hint.
 constexpr int kWindowLoadNt = 2;
 
