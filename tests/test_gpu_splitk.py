@@ -240,6 +240,29 @@ def test_splitk_two_streams_default_workspaces():
     assert len(keys) == 2
 
 
+def test_splitk_default_workspaces_are_bounded():
+    """Calls on more streams than the binding keeps workspaces for: the
+    least recently used are dropped, and every result is still exact."""
+    from tiled_fp32_gemm_sgemm_amd import api
+    dev = _dev()
+    M, N, K = 512, 512, 8192
+    A, B = operands(M, N, K, K, N, seed=650, dist_a="int4")
+    A, B = A.view(M, K).to(dev), B.view(K, N).to(dev)
+    ref = sg.sgemm_splitk(A, B)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=dev) for _ in range(api.SPLITK_WORKSPACES_KEPT + 4)]
+    outs = []
+    for s in streams + streams[:2]:
+        with torch.cuda.stream(s):
+            outs.append(sg.sgemm_splitk(A, B))
+    torch.cuda.synchronize()
+    assert len(api._splitk_workspaces) <= api.SPLITK_WORKSPACES_KEPT
+    for s in streams[:2]:
+        assert (dev.index, int(s.cuda_stream)) in api._splitk_workspaces
+    for o in outs:
+        assert torch.equal(o, ref)
+
+
 @pytest.mark.parametrize("name", ["square1024", "square1024_int"])
 def test_square1024_splitk_full(name):
     """The 1024^3 workload through sgemm_splitk at the time model's plan and

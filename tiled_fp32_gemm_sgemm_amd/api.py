@@ -151,7 +151,11 @@ def config_has_splitk(config: int) -> bool:
 # It is allocated and zeroed on the stream whose launches use it, so the
 # zeros land before the first join reads them, and a buffer dropped when it
 # grows goes back to the allocator on that stream, behind every launch that
-# used it.  Calls on different streams never share one.
+# used it.  Calls on different streams never share one.  At most
+# SPLITK_WORKSPACES_KEPT are kept, the least recently used dropped first
+# (its memory, too, is reused only behind that stream's queued launches), so
+# workspaces of streams that are gone do not pile up.
+SPLITK_WORKSPACES_KEPT = 8
 _splitk_workspaces = {}
 
 
@@ -175,12 +179,14 @@ def splitk_workspace(device, nbytes: int, stream=None):
         device = torch.device("cuda", torch.cuda.current_device())
     s = _torch_stream(stream, device)
     key = (device.index, int(s.cuda_stream))
-    ws = _splitk_workspaces.get(key)
+    ws = _splitk_workspaces.pop(key, None)
     if ws is None or ws.numel() < nbytes:
         with torch.cuda.device(device), torch.cuda.stream(s):
-            _splitk_workspaces.pop(key, None)
+            ws = None
             ws = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
-        _splitk_workspaces[key] = ws
+    _splitk_workspaces[key] = ws  # most recently used last
+    while len(_splitk_workspaces) > SPLITK_WORKSPACES_KEPT:
+        _splitk_workspaces.pop(next(iter(_splitk_workspaces)))
     return ws
 
 
