@@ -240,12 +240,6 @@ const void* conv_splitk_kernel() {
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, true>> },                        \
       nullptr, splitk_kernel<T>(), nullptr }
 
-// Plain product and its split-K variant only.
-#define SGEMM_DLS_CFG(T, name, per_cu, a1, b1, a2, b2)                                       \
-    { name, T::BM, T::BN, T::BK, T::NT, T::WG_PER_CU, (const void*)&sgemm_mfma_dl_kernel<T>, \
-      per_cu, a1, b1, a2, b2, { nullptr, nullptr, nullptr, nullptr }, nullptr,               \
-      splitk_kernel<T>(), nullptr }
-
 const ConfigEntry kConfigs[] = {
     SGEMM_CFG(Cfg256x128, "mfma32_256x128x16_w2x2", 1, 3.6505e-04, 4.2029e-06, 4.1134e-04, 8.0806e-06),
     SGEMM_CFG(Cfg128x128, "mfma32_128x128x16_w2x2", 3, 4.3004e-04, 4.5225e-06, 6.6566e-04, 1.2010e-05),
@@ -279,14 +273,13 @@ const ConfigEntry kConfigs[] = {
     SGEMM_DLX_CFG(Dl64x128k64m32s2x2, "dl32_64x128x64_w2x2_s2_k2", 1, 5.6513e-04, 3.6309e-06, 9.9029e-04, 7.2336e-06),
     SGEMM_DL_CFG(Dl96x96k32m16, "dl16_96x96x32_w2x2", 3, 5.7956e-04, 4.1848e-06, 8.6320e-04, 1.0753e-05),
     SGEMM_DLG_CFG(Dl128x128k64m32s2x2, "dl32_128x128x64_w2x2_s2_k2", 1, 5.9521e-04, 3.4661e-06, 7.0309e-04, 6.9811e-06),
-    SGEMM_DLS_CFG(Dl64x64k128m32s2x4, "dl32_64x64x128_w2x1_s2_k4", 1, 1.1211e-03, 3.6461e-06, 1.8864e-03, 7.2474e-06),
-    SGEMM_DLS_CFG(Dl128x128k64m32w4x2, "dl32_128x128x64_w4x2_s2", 1, 3.3451e-04, 3.4895e-06, 6.3514e-04, 6.9657e-06),
+    SGEMM_DLG_CFG(Dl64x64k128m32s2x4, "dl32_64x64x128_w2x1_s2_k4", 1, 1.1211e-03, 3.6461e-06, 1.8864e-03, 7.2474e-06),
+    SGEMM_DLG_CFG(Dl128x128k64m32w4x2, "dl32_128x128x64_w4x2_s2", 1, 3.3451e-04, 3.4895e-06, 6.3514e-04, 6.9657e-06),
 };
 #undef SGEMM_CFG
 #undef SGEMM_DL_CFG
 #undef SGEMM_DLX_CFG
 #undef SGEMM_DLG_CFG
-#undef SGEMM_DLS_CFG
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 constexpr int kNumCu = 256;  // MI355X compute units
 
