@@ -133,8 +133,11 @@ def test_general_configs_exist():
 
 @pytest.mark.parametrize("layout", LAYOUTS, ids=LAYOUT_IDS)
 @pytest.mark.parametrize("config", GENERAL_CONFIGS, ids=lambda c: "cfg%d" % c)
+# 520 x 530 holds whole interior tiles of every size (up to 256 x 256) beside
+# ragged edge tiles: interior tiles read C ahead of their stores, edge tiles
+# element by element.
 @pytest.mark.parametrize("shape", [(33, 65, 17), (257, 129, 300), (200, 192, 1000),
-                                   (130, 260, 515), (3, 5, 299)],
+                                   (130, 260, 515), (3, 5, 299), (520, 530, 64)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_general_every_tile_bitwise(shape, config, layout):
     tA, tB = layout
