@@ -234,7 +234,7 @@ def test_tensor_api_matches_torch():
 
 
 # ---------------------------------------------------------------- full size, sampled
-@pytest.mark.parametrize("layout", LAYOUTS[1:], ids=LAYOUT_IDS[1:])
+@pytest.mark.parametrize("layout", LAYOUTS, ids=LAYOUT_IDS)
 def test_general_4096_sampled(layout):
     tA, tB = layout
     M = N = K = 4096
