@@ -225,14 +225,16 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
     from workloads import WINDOW_WORKLOADS, WORKLOADS
     from tiled_fp32_gemm_sgemm_amd import model
     import tiled_fp32_gemm_sgemm_amd as sg
-    from workloads import ATTN_WORKLOADS, CONV_WORKLOADS
+    from workloads import ATTN_WORKLOADS, CONV_WORKLOADS, GENERAL_WORKLOADS
     window = workload in WINDOW_WORKLOADS
     conv = workload in CONV_WORKLOADS
     attn = workload in ATTN_WORKLOADS
-    gemm = not (window or conv or attn)
+    general = workload in GENERAL_WORKLOADS
+    gemm = not (window or conv or attn or general)
     w = (WINDOW_WORKLOADS[workload] if window else
          CONV_WORKLOADS[workload] if conv else
-         ATTN_WORKLOADS[workload] if attn else WORKLOADS[workload])
+         ATTN_WORKLOADS[workload] if attn else
+         GENERAL_WORKLOADS[workload] if general else WORKLOADS[workload])
     L = ["# rocprofv3 hardware counters, %s path, workload %s" % (path, w.describe()),
          "# commands (one counter pass each, run from the repository root):"]
     L += ["#   " + c for c in commands]
@@ -317,6 +319,8 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
     # ----------------------------------------------------------- memory side
     compulsory = (w.bytes if window else conv_compulsory_bytes(w) if conv else
                   4 * w.BH * w.D * (2 * w.Sq + 2 * w.Skv) if attn else
+                  4 * (w.M * w.K + w.K * w.N + 2 * w.M * w.N) if general and w.beta != 0 else
+                  model.compulsory_bytes(w.M, w.N, w.K) if general else
                   model.compulsory_bytes(w.M, w.N, w.K, w.batch))
     copy_part = "MulFunctor"
     fetch = _per_dispatch(_read_csv(fetch_csv), kernel_part) if fetch_csv else {}
@@ -390,6 +394,25 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
                     for b in range(qb))
         L.append("mfma_instructions_closed_form: %d (attention, 256 x 64 blocks)"
                  % (w.BH * pairs * 8 * 2 * w.D))
+    if general:
+        # The general form's tile; its A and B panels are the plain product's
+        # (only their stored orientation differs), and with beta != 0 each
+        # XCD also reads its tiles' part of C once.
+        cfg = sg.select_general_config(w.M, w.N, w.K)
+        info = sg.config_info(cfg)
+        mi = 16 if info["name"].startswith("dl16") else 32
+        L.append("mfma_instructions_closed_form: %d (tile %s)" % (
+            model.mfma_instructions(w.M, w.N, w.K, info["bm"], info["bn"], info["bk"], mi, 1),
+            info["name"]))
+        resident = 32 * sg.workgroups_per_cu(cfg)
+        panels = model.per_xcd_operand_bytes(w.M, w.N, w.K, info["bm"], info["bn"], 1,
+                                             resident=resident)
+        c_read = 4 * w.M * w.N if w.beta != 0 else 0
+        L.append("per_xcd_panel_read_bytes_model: %d (each XCD's L2 fetches the A and B panels "
+                 "of each round of %d resident tiles once)" % (panels, resident))
+        L.append("c_read_bytes: %d (beta != 0: C read once)" % c_read)
+        if fetch:
+            L.append("beyond_l2_read_over_panel_model_plus_c: %.4f" % (rd / (panels + c_read)))
     if path in ("mfma", "splitk") and gemm:
         n_split = 1
         if path == "splitk":
@@ -860,6 +883,182 @@ def bench_attention(args) -> int:
     return 0
 
 
+def general_cpu_baseline(w, A, B, C0, target_s: float = 12.0, keep=None):
+    """The oracle's general form, untouched, on the leading rows of C (for A
+    stored K x M the first rows of C use the first columns of A)."""
+    import oracle
+    a, b, c = A.numpy(), B.numpy(), C0.numpy()
+
+    def rows_of_c(rows):
+        return oracle.sgemm_ex_f64(bool(w.transA), bool(w.transB), rows, w.N, w.K, w.alpha, a,
+                                   w.lda, b, w.ldb, w.beta, c, w.ldc)
+
+    rows0 = 16
+    t0 = time.perf_counter()
+    rows_of_c(rows0)
+    dt0 = time.perf_counter() - t0
+    rows = int(min(w.M, max(rows0, rows0 * target_s / max(dt0, 1e-6))))
+    t0 = time.perf_counter()
+    ref, mag, used = rows_of_c(rows)
+    dt = time.perf_counter() - t0
+    if keep is not None:
+        keep.update(rows=rows, ref=ref, mag=mag)
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(used), "kind": "oracle",
+            "sample": "rows 0..%d of C for %s (%dx%dx%d, %.3g GFLOP) in %.2f s, FP64 "
+                      "accumulation, OpenMP over rows" % (rows - 1, w.name, rows, w.N, w.K,
+                                                          flops / 1e9, dt),
+            "seconds": dt}
+
+
+def bench_general(args) -> int:
+    """The general form C = alpha op(A) op(B) + beta C (sgemm_ex): TFLOP/s
+    of the 2MNK product against the FP32 matrix peak; C is read and written."""
+    import torch
+    from workloads import GENERAL_WORKLOADS, general_operands
+    import tiled_fp32_gemm_sgemm_amd as sg
+
+    if args.path != "mfma" or args.graph or args.cold or args.config is not None:
+        print("the general-form workloads time sgemm_ex on --path mfma with its own tile choice, "
+              "launched on a stream", file=sys.stderr)
+        return 2
+    w = GENERAL_WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    A_cpu, B_cpu, C0_cpu = general_operands(w, pad=0.0)
+    A, B, C0 = A_cpu.to(dev), B_cpu.to(dev), C0_cpu.to(dev)
+    C = C0.clone()
+    stream = torch.cuda.current_stream(dev)
+    handle = stream.cuda_stream
+
+    def step():
+        st = sg.sgemm_ex_raw(w.transA, w.transB, w.M, w.N, w.K, w.alpha, A.data_ptr(), w.lda,
+                             B.data_ptr(), w.ldb, w.beta, C.data_ptr(), w.ldc, handle)
+        if st != 0:
+            raise sg.SgemmError(st, "sgemm_ex")
+
+    # op(A), op(B) and C as torch views for hipBLASLt's addmm beside it.
+    ra, ca = (w.K, w.M) if w.transA else (w.M, w.K)
+    rb, cb = (w.N, w.K) if w.transB else (w.K, w.N)
+    opA = A.as_strided((ra, ca), (w.lda, 1))
+    opA = opA.t() if w.transA else opA
+    opB = B.as_strided((rb, cb), (w.ldb, 1))
+    opB = opB.t() if w.transB else opB
+    C2 = C0.clone().as_strided((w.M, w.N), (w.ldc, 1))
+
+    def torch_step():
+        C2.addmm_(opA, opB, beta=w.beta, alpha=w.alpha)
+
+    def timed(fn, n_steps, n_warm):
+        for _ in range(n_warm):
+            fn()
+        torch.cuda.synchronize()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(n_steps):
+            fn()
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) / n_steps
+
+    if args.calibrate_copy:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # Clock settle, then warm-up and timed counts from the time of one step,
+    # as for the plain product.
+    t0 = time.perf_counter()
+    n_settle = 0
+    while time.perf_counter() - t0 < SETTLE_S:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+        n_settle += 4
+    settle = {"launches": n_settle, "seconds": round(time.perf_counter() - t0, 4)}
+    t0 = time.perf_counter()
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    n = max(1, int(GEMM_WORK_S / max((time.perf_counter() - t0) / 5, 1e-6)))
+    args.warmup = args.warmup if args.warmup is not None else max(30, n)
+    args.steps = args.steps if args.steps is not None else max(50, n)
+    ms = timed(step, args.steps, args.warmup)
+    pairs = []
+    for _ in range(min(args.steps, 50)):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+        pairs.append((e0, e1))
+    torch.cuda.synchronize()
+    single = sorted(e0.elapsed_time(e1) for e0, e1 in pairs)
+    flops = float(w.flops)
+    tflops = flops / (ms * 1e-3) / 1e12
+    tile = sg.config_info(sg.select_general_config(w.M, w.N, w.K))["name"]
+
+    comparators = {}
+    if not args.no_comparator:
+        tms = timed(torch_step, max(5, args.steps // 2), 3)
+        comparators["torch_addmm"] = {"tflops": flops / (tms * 1e-3) / 1e12, "ms_per_step": tms,
+                                      "note": "torch addmm_ (hipBLASLt) with the same layouts "
+                                              "and scalars, same timing"}
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        keep = {}
+        cpu = general_cpu_baseline(w, A_cpu, B_cpu, C0_cpu, keep=keep)
+        # One launch from the initial C (the timed launches kept updating it).
+        C.copy_(C0)
+        step()
+        torch.cuda.synchronize()
+        rows = keep["rows"]
+        C_rows = C[:rows * w.ldc].view(rows, w.ldc)[:, :w.N].cpu().numpy()
+        parity = gemm_parity(C_rows, keep)
+    out = {
+        "metric": "FP32 GEMM, general form C = alpha op(A) op(B) + beta C, TFLOP/s at M=%d N=%d "
+                  "K=%d on 1 MI355X; %% of FP32 peak" % (w.M, w.N, w.K),
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_fp32_peak": 100.0 * tflops / PEAK_FP32_TFLOPS,
+        "cache": "warm",
+        "clock_settle": settle,
+        "launch": "stream",
+        "single_launch": {"n": len(single), "median_ms": single[len(single) // 2],
+                          "min_ms": single[0],
+                          "median_tflops": flops / (single[len(single) // 2] * 1e-3) / 1e12,
+                          "max_tflops": flops / (single[0] * 1e-3) / 1e12},
+        "config": {"workload": w.describe(), "M": w.M, "N": w.N, "K": w.K,
+                   "transA": w.transA, "transB": w.transB, "alpha": w.alpha, "beta": w.beta,
+                   "path": "mfma", "tile": tile},
+        "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_FP32_TFLOPS,
+                     "unit": "TFLOP/s", "frac": tflops / PEAK_FP32_TFLOPS,
+                     "traffic": read_traffic(gemm_traffic_file("ex", w.name), GEMM_SOURCES, tile),
+                     "kernel": tile, "event_ms_per_launch": ms},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "comparators": comparators,
+        "device": torch.cuda.get_device_name(dev),
+        "host": host_info(),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -942,7 +1141,7 @@ def main(argv=None) -> int:
               "has no multi-GPU path (asked for --gpus %d)" % args.gpus, file=sys.stderr)
         return 2
 
-    from workloads import ATTN_WORKLOADS, CONV_WORKLOADS, WINDOW_WORKLOADS
+    from workloads import ATTN_WORKLOADS, CONV_WORKLOADS, GENERAL_WORKLOADS, WINDOW_WORKLOADS
     short = args.workload in WINDOW_WORKLOADS or args.workload in CONV_WORKLOADS
     gemm = not (short or args.workload in ATTN_WORKLOADS)
     # GEMM defaults are set from the measured time of one step (at least
@@ -957,6 +1156,8 @@ def main(argv=None) -> int:
         return 2
     if args.workload in ATTN_WORKLOADS:
         return bench_attention(args)
+    if args.workload in GENERAL_WORKLOADS:
+        return bench_general(args)
     if args.workload in WINDOW_WORKLOADS:
         return bench_window(args)
     if args.workload in CONV_WORKLOADS:

@@ -211,3 +211,42 @@ def test_counter_summary_derivations(tmp_path):
     v = summary([str(tmp_path / "s3.csv")])
     assert v["l2_read_requests_model"].startswith("%d " % nreq)
     assert v["l2_read_requests_over_model"].startswith("1.5000")
+
+
+def test_general_form_counter_summary(tmp_path):
+    """The general-form workload's summary: compulsory bytes with C read and
+    written, the general tile's closed form, and reads against the per-XCD
+    panel model plus one read of C."""
+    import tiled_fp32_gemm_sgemm_amd as sg
+    from tiled_fp32_gemm_sgemm_amd import model
+    from workloads import GENERAL_WORKLOADS
+    w = GENERAL_WORKLOADS["atb4096"]
+    k = "sgemm_dev::sgemm_mfma_dl_kernel<x>"
+    cp = "MulFunctor<float>"
+    copy_kib = bench.COPY_BYTES / 1024.0
+    cfg = sg.select_general_config(w.M, w.N, w.K)
+    info = sg.config_info(cfg)
+    panels = model.per_xcd_operand_bytes(w.M, w.N, w.K, info["bm"], info["bn"], 1,
+                                         resident=32 * sg.workgroups_per_cu(cfg))
+    c_read = 4 * w.M * w.N
+    # FETCH_SIZE scaled by 2 (the copy's 512 MiB read as 256 MiB): reads equal the model.
+    _counter_csv(tmp_path / "f.csv", [(1, cp, "FETCH_SIZE", copy_kib / 2, 0, 1000),
+                                      (2, k, "FETCH_SIZE", (panels + c_read) / 2048.0, 0, 900000)])
+    _counter_csv(tmp_path / "w.csv", [(1, cp, "WRITE_SIZE", copy_kib, 0, 1000),
+                                      (2, k, "WRITE_SIZE", c_read / 1024.0, 0, 900000)])
+    out = tmp_path / "c.txt"
+    bench.summarize_counters(str(out), "atb4096", "mfma", "sgemm_", str(tmp_path / "f.csv"),
+                             str(tmp_path / "w.csv"), [], ["cmd"])
+    v = dict(l.split(": ", 1) for l in out.read_text().splitlines()
+             if ": " in l and not l.startswith("#"))
+    assert v["compulsory_bytes"] == str(4 * (2 * w.M * w.K + 2 * w.M * w.N))
+    assert v["mfma_instructions_closed_form"].endswith("(tile %s)" % info["name"])
+    assert v["c_read_bytes"].startswith("%d " % c_read)
+    assert v["beyond_l2_read_over_panel_model_plus_c"].startswith("1.0000")
+    assert bench.gemm_traffic_file("ex", "atb4096").endswith("sgemm_ex_atb4096_counters.txt")
+
+
+def test_general_form_bench_takes_its_own_tile(capsys):
+    assert bench.main(["--workload", "atb4096", "--path", "valu"]) == 2
+    assert bench.main(["--workload", "atb4096", "--config", "3"]) == 2
+    assert "sgemm_ex" in capsys.readouterr().err

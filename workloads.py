@@ -320,7 +320,7 @@ def workload_operands(w: Workload, pad: float = float("nan")):
 
 def stored_operands(transA: bool, transB: bool, M: int, N: int, K: int, lda: int, ldb: int,
                     seed: int, dist_a: str = "uniform", dist_b: str | None = None,
-                    pad: float = float("nan")):
+                    pad: float = float("nan"), scale_a: float = 1.0, scale_b: float = 1.0):
     """Flat float32 CPU buffers (A, B) as stored for the general form: A is
     M x K, or K x M when transA; B is K x N, or N x K when transB.  A is drawn
     before B."""
@@ -328,9 +328,60 @@ def stored_operands(transA: bool, transB: bool, M: int, N: int, K: int, lda: int
     gen = torch.Generator("cpu").manual_seed(seed)
     ra, ca = (K, M) if transA else (M, K)
     rb, cb = (N, K) if transB else (K, N)
-    A = place(draw(gen, ra * ca, dist_a), ra, ca, lda, pad)
-    B = place(draw(gen, rb * cb, dist_b), rb, cb, ldb, pad)
+    A = place(draw(gen, ra * ca, dist_a, scale_a), ra, ca, lda, pad)
+    B = place(draw(gen, rb * cb, dist_b, scale_b), rb, cb, ldb, pad)
     return A, B
+
+
+@dataclass(frozen=True)
+class GeneralWorkload:
+    """C = alpha op(A) op(B) + beta C with stored layouts: A is M x K, or
+    K x M when transA; B is K x N, or N x K when transB."""
+    name: str
+    M: int
+    N: int
+    K: int
+    transA: int
+    transB: int
+    lda: int
+    ldb: int
+    ldc: int
+    alpha: float
+    beta: float
+    dist: str            # A and B (scaled) and C (unscaled)
+    scale: float
+    seed: int
+    about: str = field(default="", compare=False)
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+    def describe(self) -> str:
+        return ("sgemm_ex transA=%d transB=%d M=%d N=%d K=%d lda=%d ldb=%d ldc=%d alpha=%g "
+                "beta=%g A,B~%s C~%s seed=%d"
+                % (self.transA, self.transB, self.M, self.N, self.K, self.lda, self.ldb, self.ldc,
+                   self.alpha, self.beta, _dist_text(self.dist, self.scale, self.K),
+                   _dist_text(self.dist, 1.0, self.K), self.seed))
+
+
+# The general form at the headline size in the lecture's C = A^T B layout (A
+# stored K x M), with beta != 0 so that C is read as well as written.
+GENERAL_WORKLOADS = {
+    "atb4096": GeneralWorkload("atb4096", 4096, 4096, 4096, 1, 0, 4096, 4096, 4096, 1.0, 0.5,
+                               "normal", 1.0 / math.sqrt(4096), 14,
+                               about="C = A^T B + 0.5 C at 4096^3, A stored K x M, "
+                                     "normal(0,1)/sqrt(K) operands, normal(0,1) C, seed 14"),
+}
+
+
+def general_operands(w: GeneralWorkload, pad: float = float("nan")):
+    """Flat float32 CPU buffers (A, B, C) for a general-form workload: A and B
+    as stored_operands draws them, then C from seed + 1."""
+    A, B = stored_operands(bool(w.transA), bool(w.transB), w.M, w.N, w.K, w.lda, w.ldb, w.seed,
+                           w.dist, w.dist, pad, w.scale, w.scale)
+    C = matrix(w.M, w.N, w.ldc, w.seed + 1, w.dist, pad)
+    return A, B, C
 
 
 def matrix(rows: int, cols: int, ld: int, seed: int, dist: str = "uniform",
