@@ -50,7 +50,7 @@ def test_every_committed_gemm_summary_is_found_by_its_workload():
     import os
     for path, workload in [("mfma", "square4096"), ("mfma", "square1024"), ("mfma", "tall"),
                            ("mfma", "ragged"), ("mfma", "shard512"), ("mfma", "batched128"),
-                           ("splitk", "longk512"), ("valu", "square4096")]:
+                           ("splitk", "longk512"), ("valu", "square4096"), ("ex", "atb4096")]:
         f = bench.gemm_traffic_file(path, workload)
         assert os.path.exists(f), f
         with open(f) as fh:
