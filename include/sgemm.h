@@ -323,6 +323,48 @@ int64_t sgemm_splitk_plan_full_tiles(int config, int64_t M, int64_t N, int64_t K
    SGEMM_STATUS_INVALID_CONFIG if unknown.  Host only. */
 int sgemm_config_has_splitk(int config);
 
+/*
+ * The general form C = alpha op(A) op(B) + beta C (as sgemm_ex, one product)
+ * with its reduction split as in sgemm_splitk: chunk b of every output tile
+ * reduces k in [b kchunk, (b+1) kchunk) over the stored layouts, the chunks
+ * join in chunk order through the caller's workspace, and the joining
+ * workgroup stores alpha times the sum, plus beta C when beta != 0 (C is
+ * read once, by that store).  For thin products with a long K, where one
+ * tile per CU leaves most of the machine idle ("Tiling Strategies" section 4
+ * on tile size and tail effects; "CMU DLSys Lecture 12: GPU Acceleration" section 4 writes the
+ * product as C = A^T B with A stored K x M, the transA = 1 layout here).
+ *
+ * transA, transB, sizes, scalars, A, lda, B, ldb, C, ldc: as for sgemm_ex.
+ * config: a configuration with general-form split-K variants
+ *   (sgemm_config_has_general_splitk), or -1 for the time model's choice,
+ *   which may be the unsplit general form.
+ * splits, workspace, workspace_bytes: as for sgemm_splitk, with the size
+ *   sgemm_ex_splitk_plan reports; the same workspace layout, header and
+ *   zero-once rule, so one workspace serves sgemm_splitk and this call in
+ *   turn.  alpha = 0 or K = 0 scale C by beta and use no workspace.
+ * Results are bit for bit those of the same plan's chunks summed in chunk
+ * order, independent of timing.  Errors as for sgemm_ex and sgemm_splitk; on
+ * an error nothing is enqueued.
+ */
+int sgemm_ex_splitk(int config, int transA, int transB, int64_t M, int64_t N, int64_t K,
+                    float alpha, const float *A, int64_t lda, const float *B, int64_t ldb,
+                    float beta, float *C, int64_t ldc, int64_t splits, void *workspace,
+                    int64_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The plan sgemm_ex_splitk would run with these arguments: its tile in
+ * *plan_config and chunk count in *plan_splits (either pointer may be NULL),
+ * and the workspace bytes it needs as the return value (0 when it runs one
+ * chunk or the product is empty), or a negative status.  Host only.
+ */
+int64_t sgemm_ex_splitk_plan(int config, int transA, int transB, int64_t M, int64_t N,
+                             int64_t K, int64_t splits, int *plan_config, int64_t *plan_splits);
+
+/* 1 if configuration `config` has split-K variants of the general form (all
+   four layouts), 0 if not, SGEMM_STATUS_INVALID_CONFIG if unknown.  Host
+   only. */
+int sgemm_config_has_general_splitk(int config);
+
 /* Static text for a status code (never NULL). */
 const char *sgemm_status_string(int status);
 

@@ -384,6 +384,73 @@ def sgemm_ex(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, transA: bool =
     return C
 
 
+def ex_splitk_plan(M: int, N: int, K: int, transA: bool = False, transB: bool = False,
+                   splits: int = 0, config=None):
+    """(config, splits, workspace bytes) that sgemm_ex_splitk runs for this
+    shape and layout."""
+    cfg = ctypes.c_int(-1)
+    sp = ctypes.c_int64(0)
+    st = _native.lib().sgemm_ex_splitk_plan(-1 if config is None else int(config), int(transA),
+                                            int(transB), M, N, K, int(splits), ctypes.byref(cfg),
+                                            ctypes.byref(sp))
+    if st < 0:
+        raise _native.SgemmError(int(st), "sgemm_ex_splitk_plan")
+    return cfg.value, sp.value, int(st)
+
+
+def sgemm_ex_splitk_raw(transA, transB, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr,
+                        ldc, ws_ptr, ws_bytes, stream=0, splits: int = 0, config=None) -> int:
+    """The general form with its reduction split, on device addresses;
+    returns the status."""
+    return _native.lib().sgemm_ex_splitk(-1 if config is None else int(config), int(transA),
+                                         int(transB), M, N, K, float(alpha), A_ptr, lda, B_ptr,
+                                         ldb, float(beta), C_ptr, ldc, int(splits), ws_ptr,
+                                         int(ws_bytes), stream)
+
+
+def sgemm_ex_splitk(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, transA: bool = False,
+                    transB: bool = False, *, splits: int = 0, config=None, workspace=None,
+                    stream=None):
+    """sgemm_ex (2-D operands) with the k range split as in sgemm_splitk.
+    workspace: a device tensor of at least ex_splitk_plan(...)[2] bytes whose
+    header starts at zero, or None for the one kept for this device and
+    stream (shared with sgemm_splitk)."""
+    import torch
+    _operand(A, "A", 2)
+    _operand(B, "B", 2)
+    ra, ca = A.shape
+    rb, cb = B.shape
+    M, K = (ca, ra) if transA else (ra, ca)
+    K2, N = (cb, rb) if transB else (rb, cb)
+    if K != K2:
+        raise ValueError("shapes differ: %s vs %s" % (tuple(A.shape), tuple(B.shape)))
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("C is required when beta != 0")
+        C = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    _operand(C, "C", 2)
+    if tuple(C.shape) != (M, N):
+        raise ValueError("C must have shape (%d, %d)" % (M, N))
+    _, _, nbytes = ex_splitk_plan(M, N, K, transA, transB, splits, config)
+    if workspace is None:
+        workspace = splitk_workspace(A.device, nbytes, stream)
+    with torch.cuda.device(A.device):
+        st = sgemm_ex_splitk_raw(transA, transB, M, N, K, alpha, A.data_ptr(), _ld(A),
+                                 B.data_ptr(), _ld(B), beta, C.data_ptr(), _ld(C),
+                                 workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(),
+                                 _stream_handle(stream, A.device), splits, config)
+    _check(st, "sgemm_ex_splitk")
+    return C
+
+
+def config_has_general_splitk(config: int) -> bool:
+    st = _native.lib().sgemm_config_has_general_splitk(int(config))
+    if st < 0:
+        raise _native.SgemmError(st, "sgemm_config_has_general_splitk")
+    return bool(st)
+
+
 def config_has_general_form(config: int) -> bool:
     st = _native.lib().sgemm_config_has_general_form(int(config))
     if st < 0:

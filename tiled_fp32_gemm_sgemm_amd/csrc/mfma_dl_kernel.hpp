@@ -193,8 +193,8 @@ struct DlTile {
     static_assert(SCHED >= 0 && SCHED <= 2, "slice schedule");
     static_assert(SCHED < 2 || LPS <= NKG * KG - HOLD, "one copy per k step fits in a slice");
     static_assert((KSPLIT - 1) * BM * BN <= STAGES * BUF_FLOATS, "k-group exchange fits in LDS");
-    static_assert(!SK || (A_KC && !EX && B_KC == CONV),
-                  "split-K: the plain product or the convolution only");
+    static_assert(!SK || !CONV || (A_KC && B_KC && !EX),
+                  "split-K convolution: k-contiguous operands, beta = 0");
     static_assert(!SK || WTM * WTN <= 64 * 64, "split-K join holds one wave tile of sums");
 
     // Quad swizzle of k-contiguous row r.  Rows of at most 256 bytes: the 16
@@ -1023,6 +1023,21 @@ __device__ __forceinline__ void sgemm_mfma_dl_body(const GemmArgs& p) {
 #pragma unroll
                     for (int u = 0; u < T::BV; ++u)
                         v[u] = part[(mi * T::TN + h * T::BV + u) * RQ + r];
+                    if constexpr (T::EX) {
+                        // alpha * sum, plus beta * C when beta != 0.
+                        if (p.beta != 0.0f) {
+#pragma unroll
+                            for (int u = 0; u < T::BV; ++u) {
+                                const bool in = full_mn ||
+                                                (row < rows_left && col + u < cols_left);
+                                const float old = in ? c[u] : 0.0f;
+                                v[u] = __builtin_fmaf(p.beta, old, p.alpha * v[u]);
+                            }
+                        } else {
+#pragma unroll
+                            for (int u = 0; u < T::BV; ++u) v[u] = p.alpha * v[u];
+                        }
+                    }
                     if (full_mn) {
                         __builtin_nontemporal_store(v, (svec_t*)c);
                     } else {

@@ -170,6 +170,9 @@ struct ConfigEntry {
     const void* splitk;
     // Split-K variant of the convolution; NULL where not built.
     const void* conv_splitk;
+    // Split-K variants of the general form, by operand layout; NULL where
+    // not built.
+    const void* general_splitk[4];
 };
 
 // The same tile with stored-operand layouts and the alpha/beta epilogue.
@@ -215,6 +218,24 @@ const void* conv_splitk_kernel() {
         return nullptr;
 }
 
+// The general form's split-K variants, for the tiles that have a plain one.
+template <class T, bool TA, bool TB>
+using DlGeneralSplitK = DlTile<T::BM, T::BN, T::BK, T::WAVES_M, T::WAVES_N, T::MI, T::OCC,
+                               T::GROUP_M, T::STAGES, T::KSPLIT, T::SWIZZLE, TA, TB, true,
+                               T::BIL, false, T::SCHED, true>;
+
+template <class T, bool TA, bool TB>
+const void* general_splitk_kernel() {
+    if constexpr (T::WTM * T::WTN <= 64 * 64 && T::BK >= 32)
+        return (const void*)&sgemm_mfma_dl_kernel<DlGeneralSplitK<T, TA, TB>>;
+    else
+        return nullptr;
+}
+
+#define SGEMM_GENERAL_SPLITK(T)                                                         \
+    { general_splitk_kernel<T, false, false>(), general_splitk_kernel<T, true, false>(), \
+      general_splitk_kernel<T, false, true>(), general_splitk_kernel<T, true, true>() }
+
 #define SGEMM_CFG(T, name, per_cu, a1, b1, a2, b2) \
     { name, T::BM, T::BN, T::BK, T::NT, T::WG_PER_CU, (const void*)&sgemm_mfma_kernel<T>, per_cu, \
       a1, b1, a2, b2 }
@@ -229,7 +250,7 @@ const void* conv_splitk_kernel() {
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, false, true>>,                        \
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, true>> },                        \
       (const void*)&sgemm_mfma_dl_kernel<DlConv<T>>, splitk_kernel<T>(),                     \
-      conv_splitk_kernel<T>() }
+      conv_splitk_kernel<T>(), SGEMM_GENERAL_SPLITK(T) }
 // General form, no convolution variant.
 #define SGEMM_DLG_CFG(T, name, per_cu, a1, b1, a2, b2)                                       \
     { name, T::BM, T::BN, T::BK, T::NT, T::WG_PER_CU, (const void*)&sgemm_mfma_dl_kernel<T>, \
@@ -238,7 +259,7 @@ const void* conv_splitk_kernel() {
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, false>>,                        \
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, false, true>>,                        \
         (const void*)&sgemm_mfma_dl_kernel<DlGeneral<T, true, true>> },                        \
-      nullptr, splitk_kernel<T>(), nullptr }
+      nullptr, splitk_kernel<T>(), nullptr, SGEMM_GENERAL_SPLITK(T) }
 
 const ConfigEntry kConfigs[] = {
     SGEMM_CFG(Cfg256x128, "mfma32_256x128x16_w2x2", 1, 3.6505e-04, 4.2029e-06, 4.1134e-04, 8.0806e-06),
@@ -280,6 +301,7 @@ const ConfigEntry kConfigs[] = {
 #undef SGEMM_DL_CFG
 #undef SGEMM_DLX_CFG
 #undef SGEMM_DLG_CFG
+#undef SGEMM_GENERAL_SPLITK
 constexpr int kNumConfigs = (int)(sizeof(kConfigs) / sizeof(kConfigs[0]));
 constexpr int kNumCu = 256;  // MI355X compute units
 
@@ -597,9 +619,14 @@ double predict_split_us(const ConfigEntry& c, const SplitPlan& sp, int64_t M, in
 // channels; the tiles are those with a convolution split-K kernel, and a BK
 // that does not divide conv_c (slices gathered through registers) counts
 // four times slower, as in choose_conv_config.
+// layout >= 0: the general form in that operand layout (transA + 2 transB);
+// the tiles are those with its split-K kernel, and the unsplit choice is
+// the general form's.
 int plan_splitk(int config, int64_t M, int64_t N, int64_t K, int64_t splits, SplitPlan* out,
-                int64_t max_ws = INT64_MAX, int64_t conv_c = 0) {
-    auto kernel_of = [&](const ConfigEntry& c) { return conv_c > 0 ? c.conv_splitk : c.splitk; };
+                int64_t max_ws = INT64_MAX, int64_t conv_c = 0, int layout = -1) {
+    auto kernel_of = [&](const ConfigEntry& c) {
+        return conv_c > 0 ? c.conv_splitk : layout >= 0 ? c.general_splitk[layout] : c.splitk;
+    };
     if (config >= kNumConfigs) return SGEMM_STATUS_INVALID_CONFIG;
     if (config >= 0 && kernel_of(kConfigs[config]) == nullptr) return SGEMM_STATUS_INVALID_CONFIG;
     if (splits < 0 || splits > kMaxSplits) return SGEMM_STATUS_INVALID_SIZE;
@@ -624,7 +651,8 @@ int plan_splitk(int config, int64_t M, int64_t N, int64_t K, int64_t splits, Spl
         if (splits == 0 && make_hybrid_plan(c, idx, M, N, K, want, &hp)) take(c, hp);
     };
     if (config < 0 && splits == 0 && M > 0 && N > 0 && K > 0)
-        consider(conv_c > 0 ? choose_conv_config(M, N, K, conv_c) : choose_config(M, N, K, 1), 1);
+        consider(conv_c > 0 ? choose_conv_config(M, N, K, conv_c)
+                            : choose_config(M, N, K, 1, layout >= 0), 1);
     for (int idx = 0; idx < kNumConfigs; ++idx) {
         if (config >= 0 ? idx != config : (kernel_of(kConfigs[idx]) == nullptr ||
                                            kConfigs[idx].per_cu == 0))
@@ -814,6 +842,66 @@ int run_general(int config, int transA, int transB, int64_t M, int64_t N, int64_
     const ConfigEntry& c = kConfigs[config];
     return launch_gemm(c.general[layout], c.bm, c.bn, c.threads, M, N, K, A, lda, strideA, B,
                        ldb, strideB, C, ldc, strideC, batch, stream, alpha, beta);
+}
+
+// The general form with its reduction split as in run_splitk: the chunks'
+// operands start kchunk further along k (a row of A stored K x M, a column
+// of B stored N x K), and the join's stores apply alpha and beta.
+int run_ex_splitk(int config, int transA, int transB, int64_t M, int64_t N, int64_t K,
+                  float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                  float beta, float* C, int64_t ldc, int64_t splits, void* workspace,
+                  int64_t workspace_bytes, hipStream_t stream) {
+    int st = validate_general(transA, transB, M, N, K, alpha, A, lda, 0, B, ldb, 0, C, ldc, 0, 1);
+    if (st != SGEMM_STATUS_SUCCESS) return st;
+    const int layout = transA + 2 * transB;
+    if (config >= kNumConfigs || (config >= 0 && kConfigs[config].general_splitk[layout] == nullptr))
+        return SGEMM_STATUS_INVALID_CONFIG;
+    if (splits < 0 || splits > kMaxSplits) return SGEMM_STATUS_INVALID_SIZE;
+    if (M == 0 || N == 0) return SGEMM_STATUS_SUCCESS;
+    if (K == 0 || alpha == 0.0f) {
+        if (beta == 1.0f) return SGEMM_STATUS_SUCCESS;
+        return launch_scale(M, N, C, ldc, 0, 1, beta, stream);
+    }
+    SplitPlan sp;
+    st = plan_splitk(config, M, N, K, splits, &sp, INT64_MAX, 0, layout);
+    if (st != SGEMM_STATUS_SUCCESS) return st;
+    const ConfigEntry& c = kConfigs[sp.config];
+    if (sp.splits == 1)
+        return launch_gemm(c.general[layout], c.bm, c.bn, c.threads, M, N, K, A, lda, 0, B, ldb,
+                           0, C, ldc, 0, 1, stream, alpha, beta);
+    const int64_t tiles_m = ceil_div(M, c.bm), tiles_n = ceil_div(N, c.bn);
+    const int64_t blocks = split_blocks(sp, tiles_m * tiles_n);
+    if (blocks > kMaxWorkItems / c.threads) return SGEMM_STATUS_SIZE_OVERFLOW;
+    if (workspace == nullptr || workspace_bytes < sp.ws_bytes)
+        return SGEMM_STATUS_INVALID_WORKSPACE;
+    GemmArgs p = {};
+    p.A = A;
+    p.B = B;
+    p.C = C;
+    p.lda = lda;
+    p.ldb = ldb;
+    p.ldc = ldc;
+    p.strideA = transA ? sp.kchunk * lda : sp.kchunk;
+    p.strideB = transB ? sp.kchunk : sp.kchunk * ldb;
+    p.strideC = 0;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.tiles_m = (int)tiles_m;
+    p.tiles_n = (int)tiles_n;
+    p.batch_base = 0;
+    p.batch_count = (int)sp.splits;
+    p.alpha = alpha;
+    p.beta = beta;
+    p.counters = (uint32_t*)workspace;
+    p.ws = (float*)((char*)workspace + kSplitHeaderBytes);
+    p.kchunk = (int)sp.kchunk;
+    p.splits = (int)sp.splits;
+    p.full_tiles = (int)sp.full_tiles;
+    void* args[] = {&p};
+    hipError_t e = hipLaunchKernel(c.general_splitk[layout], dim3((unsigned)blocks),
+                                   dim3(c.threads), args, 0, stream);
+    return e == hipSuccess ? SGEMM_STATUS_SUCCESS : SGEMM_STATUS_LAUNCH_FAILED;
 }
 
 // Output extent of a convolution along one axis; -1 for invalid arguments.
@@ -1030,6 +1118,36 @@ int64_t sgemm_splitk_plan_full_tiles(int config, int64_t M, int64_t N, int64_t K
     const int st = plan_splitk(config, M, N, K, splits, &sp);
     if (st != SGEMM_STATUS_SUCCESS) return st;
     return sp.splits > 1 ? sp.full_tiles : 0;
+}
+
+int sgemm_ex_splitk(int config, int transA, int transB, int64_t M, int64_t N, int64_t K,
+                    float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                    float beta, float* C, int64_t ldc, int64_t splits, void* workspace,
+                    int64_t workspace_bytes, hipStream_t stream) {
+    return run_ex_splitk(config, transA, transB, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                         splits, workspace, workspace_bytes, stream);
+}
+
+int64_t sgemm_ex_splitk_plan(int config, int transA, int transB, int64_t M, int64_t N,
+                             int64_t K, int64_t splits, int* plan_config, int64_t* plan_splits) {
+    if ((transA != 0 && transA != 1) || (transB != 0 && transB != 1))
+        return SGEMM_STATUS_INVALID_OP;
+    if (M < 0 || N < 0 || K < 0) return SGEMM_STATUS_INVALID_SIZE;
+    if (M > kMaxDim || N > kMaxDim || K > kMaxDim) return SGEMM_STATUS_SIZE_OVERFLOW;
+    const int layout = transA + 2 * transB;
+    if (config >= kNumConfigs || (config >= 0 && kConfigs[config].general_splitk[layout] == nullptr))
+        return SGEMM_STATUS_INVALID_CONFIG;
+    SplitPlan sp;
+    const int st = plan_splitk(config, M, N, K, splits, &sp, INT64_MAX, 0, layout);
+    if (st != SGEMM_STATUS_SUCCESS) return st;
+    if (plan_config != nullptr) *plan_config = sp.config;
+    if (plan_splits != nullptr) *plan_splits = sp.splits;
+    return (M == 0 || N == 0 || K == 0) ? 0 : sp.ws_bytes;
+}
+
+int sgemm_config_has_general_splitk(int config) {
+    if (config < 0 || config >= kNumConfigs) return SGEMM_STATUS_INVALID_CONFIG;
+    return kConfigs[config].general_splitk[0] != nullptr ? 1 : 0;
 }
 
 int sgemm_config_has_splitk(int config) {
