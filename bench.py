@@ -397,22 +397,45 @@ def summarize_counters(out: str, workload: str, path: str, kernel_part: str, fet
     if general:
         # The general form's tile; its A and B panels are the plain product's
         # (only their stored orientation differs), and with beta != 0 each
-        # XCD also reads its tiles' part of C once.
-        cfg = sg.select_general_config(w.M, w.N, w.K)
+        # XCD also reads its tiles' part of C once.  Split (path splitk):
+        # chunk b of every tile runs as batch member b over K / chunks, and
+        # the join writes and reads the partial tiles once.
+        n_split = 1
+        if path == "splitk":
+            cfg, n_split, _ = sg.ex_splitk_plan(w.M, w.N, w.K, bool(w.transA), bool(w.transB),
+                                                splits)
+        else:
+            cfg = sg.select_general_config(w.M, w.N, w.K)
         info = sg.config_info(cfg)
         mi = 16 if info["name"].startswith("dl16") else 32
         L.append("mfma_instructions_closed_form: %d (tile %s)" % (
             model.mfma_instructions(w.M, w.N, w.K, info["bm"], info["bn"], info["bk"], mi, 1),
             info["name"]))
         resident = 32 * sg.workgroups_per_cu(cfg)
-        panels = model.per_xcd_operand_bytes(w.M, w.N, w.K, info["bm"], info["bn"], 1,
-                                             resident=resident)
+        panels = model.per_xcd_operand_bytes(w.M, w.N, model.ceil_div(w.K, n_split), info["bm"],
+                                             info["bn"], n_split, resident=resident)
         c_read = 4 * w.M * w.N if w.beta != 0 else 0
         L.append("per_xcd_panel_read_bytes_model: %d (each XCD's L2 fetches the A and B panels "
                  "of each round of %d resident tiles once)" % (panels, resident))
         L.append("c_read_bytes: %d (beta != 0: C read once)" % c_read)
+        part = 0
+        if n_split > 1:
+            tiles = model.ceil_div(w.M, info["bm"]) * model.ceil_div(w.N, info["bn"])
+            full = sg.ex_splitk_plan_full_tiles(w.M, w.N, w.K, bool(w.transA), bool(w.transB),
+                                                splits)
+            part = (tiles - full) * n_split * info["bm"] * info["bn"] * 4
+            L.append("splitk_chunks: %d" % n_split)
+            L.append("splitk_full_tiles: %d of %d (all of K, no join)" % (full, tiles))
+            L.append("splitk_partial_bytes_model: %d (split tiles x chunks x BM x BN x 4, "
+                     "written once and read once by the join)" % part)
         if fetch:
             L.append("beyond_l2_read_over_panel_model_plus_c: %.4f" % (rd / (panels + c_read)))
+            if part:
+                L.append("beyond_l2_read_minus_panels_and_c_over_partials: %.4f ((read bytes - "
+                         "panel model - C) / partial bytes)" % ((rd - panels - c_read) / part))
+        if fetch and write and part:
+            L.append("beyond_l2_write_minus_output_over_partials: %.4f ((write bytes - 4MN) "
+                     "/ partial bytes)" % ((wr - 4.0 * w.M * w.N) / part))
     if path in ("mfma", "splitk") and gemm:
         n_split = 1
         if path == "splitk":
@@ -918,10 +941,11 @@ def bench_general(args) -> int:
     from workloads import GENERAL_WORKLOADS, general_operands
     import tiled_fp32_gemm_sgemm_amd as sg
 
-    if args.path != "mfma" or args.graph or args.cold or args.config is not None:
-        print("the general-form workloads time sgemm_ex on --path mfma with its own tile choice, "
-              "launched on a stream", file=sys.stderr)
+    if args.path not in ("mfma", "splitk") or args.graph or args.cold or args.config is not None:
+        print("the general-form workloads time sgemm_ex (--path mfma) or sgemm_ex_splitk (--path "
+              "splitk) with their own tile choice, launched on a stream", file=sys.stderr)
         return 2
+    splitk = args.path == "splitk"
     w = GENERAL_WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -931,11 +955,21 @@ def bench_general(args) -> int:
     stream = torch.cuda.current_stream(dev)
     handle = stream.cuda_stream
 
+    if splitk:
+        sk_config, sk_splits, sk_bytes = sg.ex_splitk_plan(w.M, w.N, w.K, bool(w.transA),
+                                                           bool(w.transB), args.splits)
+        ws = torch.zeros(max(sk_bytes, 256), dtype=torch.uint8, device=dev)
+
     def step():
-        st = sg.sgemm_ex_raw(w.transA, w.transB, w.M, w.N, w.K, w.alpha, A.data_ptr(), w.lda,
-                             B.data_ptr(), w.ldb, w.beta, C.data_ptr(), w.ldc, handle)
+        if splitk:
+            st = sg.sgemm_ex_splitk_raw(w.transA, w.transB, w.M, w.N, w.K, w.alpha, A.data_ptr(),
+                                        w.lda, B.data_ptr(), w.ldb, w.beta, C.data_ptr(), w.ldc,
+                                        ws.data_ptr(), ws.numel(), handle, args.splits)
+        else:
+            st = sg.sgemm_ex_raw(w.transA, w.transB, w.M, w.N, w.K, w.alpha, A.data_ptr(),
+                                 w.lda, B.data_ptr(), w.ldb, w.beta, C.data_ptr(), w.ldc, handle)
         if st != 0:
-            raise sg.SgemmError(st, "sgemm_ex")
+            raise sg.SgemmError(st, "sgemm_ex_splitk" if splitk else "sgemm_ex")
 
     # op(A), op(B) and C as torch views for hipBLASLt's addmm beside it.
     ra, ca = (w.K, w.M) if w.transA else (w.M, w.K)
@@ -1000,9 +1034,24 @@ def bench_general(args) -> int:
     single = sorted(e0.elapsed_time(e1) for e0, e1 in pairs)
     flops = float(w.flops)
     tflops = flops / (ms * 1e-3) / 1e12
-    tile = sg.config_info(sg.select_general_config(w.M, w.N, w.K))["name"]
+    if splitk:
+        tile = "%s_splits%d" % (sg.config_info(sk_config)["name"], sk_splits)
+        traffic = read_traffic(gemm_traffic_file("ex_splitk", w.name), GEMM_SOURCES,
+                               sg.config_info(sk_config)["name"], sk_splits)
+    else:
+        tile = sg.config_info(sg.select_general_config(w.M, w.N, w.K))["name"]
+        traffic = read_traffic(gemm_traffic_file("ex", w.name), GEMM_SOURCES, tile)
 
     comparators = {}
+    if not args.no_comparator and splitk:
+        def plain_step():
+            st = sg.sgemm_ex_raw(w.transA, w.transB, w.M, w.N, w.K, w.alpha, A.data_ptr(), w.lda,
+                                 B.data_ptr(), w.ldb, w.beta, C.data_ptr(), w.ldc, handle)
+            if st != 0:
+                raise sg.SgemmError(st, "sgemm_ex")
+        pms = timed(plain_step, max(5, args.steps // 2), 3)
+        comparators["sgemm_ex"] = {"tflops": flops / (pms * 1e-3) / 1e12, "ms_per_step": pms,
+                                   "note": "the unsplit general form, same timing"}
     if not args.no_comparator:
         tms = timed(torch_step, max(5, args.steps // 2), 3)
         comparators["torch_addmm"] = {"tflops": flops / (tms * 1e-3) / 1e12, "ms_per_step": tms,
@@ -1044,11 +1093,10 @@ def bench_general(args) -> int:
                           "max_tflops": flops / (single[0] * 1e-3) / 1e12},
         "config": {"workload": w.describe(), "M": w.M, "N": w.N, "K": w.K,
                    "transA": w.transA, "transB": w.transB, "alpha": w.alpha, "beta": w.beta,
-                   "path": "mfma", "tile": tile},
+                   "path": args.path, "tile": tile},
         "roofline": {"bound": "mfma", "achieved": tflops, "peak": PEAK_FP32_TFLOPS,
                      "unit": "TFLOP/s", "frac": tflops / PEAK_FP32_TFLOPS,
-                     "traffic": read_traffic(gemm_traffic_file("ex", w.name), GEMM_SOURCES, tile),
-                     "kernel": tile, "event_ms_per_launch": ms},
+                     "traffic": traffic, "kernel": tile, "event_ms_per_launch": ms},
         "cpu_baseline": cpu,
         "parity": parity,
         "comparators": comparators,

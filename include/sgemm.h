@@ -360,6 +360,14 @@ int sgemm_ex_splitk(int config, int transA, int transB, int64_t M, int64_t N, in
 int64_t sgemm_ex_splitk_plan(int config, int transA, int transB, int64_t M, int64_t N,
                              int64_t K, int64_t splits, int *plan_config, int64_t *plan_splits);
 
+/*
+ * For the plan sgemm_ex_splitk would run with these arguments: the number of
+ * output tiles that take all of K without a join (0 when every tile is split
+ * or the plan is unsplit), or a negative status.  Host only.
+ */
+int64_t sgemm_ex_splitk_plan_full_tiles(int config, int transA, int transB, int64_t M,
+                                        int64_t N, int64_t K, int64_t splits);
+
 /* 1 if configuration `config` has split-K variants of the general form (all
    four layouts), 0 if not, SGEMM_STATUS_INVALID_CONFIG if unknown.  Host
    only. */

@@ -15,7 +15,7 @@ from .api import (SPLITK_HEADER_BYTES, SPLITK_MAX_TILES, attention, attention_ra
                   select_general_config, sgemm, sgemm_ex, sgemm_ex_raw, sgemm_raw,
                   config_has_splitk, sgemm_splitk, sgemm_splitk_noalloc, splitk_plan,
                   splitk_plan_full_tiles, splitk_workspace, config_has_general_splitk,
-                  ex_splitk_plan, sgemm_ex_splitk, sgemm_ex_splitk_raw,
+                  ex_splitk_plan, ex_splitk_plan_full_tiles, sgemm_ex_splitk, sgemm_ex_splitk_raw,
                   sgemm_strided_batched, sgemm_strided_batched_raw, window_sum,
                   window_sum_raw, workgroups_per_cu)
 from ._native import SgemmError, status_string
@@ -29,6 +29,7 @@ __all__ = ["sgemm", "sgemm_strided_batched", "sgemm_raw", "sgemm_strided_batched
            "conv2d_nhwc_splitk_raw", "conv2d_splitk_plan", "workgroups_per_cu", "attention", "attention_raw",
            "sgemm_splitk", "sgemm_splitk_noalloc", "splitk_plan", "splitk_plan_full_tiles",
            "splitk_workspace", "config_has_splitk", "config_has_general_splitk",
-           "ex_splitk_plan", "sgemm_ex_splitk", "sgemm_ex_splitk_raw",
+           "ex_splitk_plan", "ex_splitk_plan_full_tiles", "sgemm_ex_splitk",
+           "sgemm_ex_splitk_raw",
            "SPLITK_HEADER_BYTES", "SPLITK_MAX_TILES", "SgemmError",
            "status_string"]

@@ -89,6 +89,8 @@ _SIGS = {
                          _i64, _p], ctypes.c_int),
     "sgemm_ex_splitk_plan": ([ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _i64, _i64, _i64,
                               ctypes.POINTER(ctypes.c_int), ctypes.POINTER(_i64)], _i64),
+    "sgemm_ex_splitk_plan_full_tiles": ([ctypes.c_int, ctypes.c_int, ctypes.c_int, _i64, _i64,
+                                         _i64, _i64], _i64),
     "sgemm_config_has_general_splitk": ([ctypes.c_int], ctypes.c_int),
     "sgemm_status_string": ([ctypes.c_int], ctypes.c_char_p),
     "window_sum": ([_i64, _i64, _p, _p, _p], ctypes.c_int),

@@ -398,6 +398,17 @@ def ex_splitk_plan(M: int, N: int, K: int, transA: bool = False, transB: bool = 
     return cfg.value, sp.value, int(st)
 
 
+def ex_splitk_plan_full_tiles(M: int, N: int, K: int, transA: bool = False,
+                              transB: bool = False, splits: int = 0, config=None) -> int:
+    """Output tiles of sgemm_ex_splitk's plan that take all of K with no join."""
+    st = _native.lib().sgemm_ex_splitk_plan_full_tiles(-1 if config is None else int(config),
+                                                       int(transA), int(transB), M, N, K,
+                                                       int(splits))
+    if st < 0:
+        raise _native.SgemmError(int(st), "sgemm_ex_splitk_plan_full_tiles")
+    return int(st)
+
+
 def sgemm_ex_splitk_raw(transA, transB, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr,
                         ldc, ws_ptr, ws_bytes, stream=0, splits: int = 0, config=None) -> int:
     """The general form with its reduction split, on device addresses;

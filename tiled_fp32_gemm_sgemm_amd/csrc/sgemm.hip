@@ -1145,6 +1145,19 @@ int64_t sgemm_ex_splitk_plan(int config, int transA, int transB, int64_t M, int6
     return (M == 0 || N == 0 || K == 0) ? 0 : sp.ws_bytes;
 }
 
+int64_t sgemm_ex_splitk_plan_full_tiles(int config, int transA, int transB, int64_t M,
+                                        int64_t N, int64_t K, int64_t splits) {
+    int plan_config = -1;
+    int64_t plan_splits = 0;
+    const int64_t st = sgemm_ex_splitk_plan(config, transA, transB, M, N, K, splits,
+                                            &plan_config, &plan_splits);
+    if (st < 0) return st;
+    SplitPlan sp;
+    const int r = plan_splitk(config, M, N, K, splits, &sp, INT64_MAX, 0, transA + 2 * transB);
+    if (r != SGEMM_STATUS_SUCCESS) return r;
+    return sp.splits > 1 ? sp.full_tiles : 0;
+}
+
 int sgemm_config_has_general_splitk(int config) {
     if (config < 0 || config >= kNumConfigs) return SGEMM_STATUS_INVALID_CONFIG;
     return kConfigs[config].general_splitk[0] != nullptr ? 1 : 0;

@@ -372,6 +372,11 @@ GENERAL_WORKLOADS = {
                                "normal", 1.0 / math.sqrt(4096), 14,
                                about="C = A^T B + 0.5 C at 4096^3, A stored K x M, "
                                      "normal(0,1)/sqrt(K) operands, normal(0,1) C, seed 14"),
+    "atb_longk512": GeneralWorkload("atb_longk512", 512, 512, 8192, 1, 0, 512, 512, 512, 1.0,
+                                    0.5, "normal", 1.0 / math.sqrt(8192), 16,
+                                    about="C = A^T B + 0.5 C at 512x512x8192 (the thin long-K "
+                                          "case, for sgemm_ex_splitk), normal(0,1)/sqrt(K) "
+                                          "operands, normal(0,1) C, seed 16"),
 }
 
 
