@@ -161,6 +161,34 @@ def test_graph_hybrid_splitk_and_conv():
     assert torch.count_nonzero(ws[:sg.SPLITK_HEADER_BYTES]).item() == 0
 
 
+def test_graph_general_splitk():
+    """The general form split over k, two layouts with beta != 0, captured on
+    one workspace (C reset inside the graph by a kernel)."""
+    dev = _dev()
+    gen = torch.Generator(device=dev).manual_seed(19)
+    At = torch.randn(4096, 300, device=dev, generator=gen)   # stored K x M
+    B = torch.randn(4096, 200, device=dev, generator=gen)
+    C0 = torch.randn(300, 200, device=dev, generator=gen)
+    C = torch.empty_like(C0)
+    A2 = torch.randn(128, 3000, device=dev, generator=gen)
+    Bt2 = torch.randn(256, 3000, device=dev, generator=gen)  # stored N x K
+    C20 = torch.randn(128, 256, device=dev, generator=gen)
+    C2 = torch.empty_like(C20)
+    n1 = sg.ex_splitk_plan(300, 200, 4096, True, False, 5)[2]
+    n2 = sg.ex_splitk_plan(128, 256, 3000, False, True, 3)[2]
+    assert n1 > 0 and n2 > 0
+    ws = torch.zeros(max(n1, n2), dtype=torch.uint8, device=dev)
+
+    def capture():
+        torch.mul(C0, 1.0, out=C)
+        sg.sgemm_ex_splitk(At, B, C, alpha=1.5, beta=-0.5, transA=True, splits=5, workspace=ws)
+        torch.mul(C20, 1.0, out=C2)
+        sg.sgemm_ex_splitk(A2, Bt2, C2, alpha=0.5, beta=2.0, transB=True, splits=3,
+                           workspace=ws)
+    _replays_match(capture, [C, C2], _other_work(dev))
+    assert torch.count_nonzero(ws[:sg.SPLITK_HEADER_BYTES]).item() == 0
+
+
 def test_host_threads_on_their_own_streams():
     """The library keeps no mutable global state: four host threads, each on
     its own stream, calling different entry points at once, give the same
