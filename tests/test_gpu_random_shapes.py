@@ -2,8 +2,9 @@
 
 The named workloads and the hand-picked ragged shapes each land on a few tiles;
 these shapes, drawn log-uniformly, let the time model pick whatever it picks
-(the plain product's tile, the split-K plan, hybrid or not, and the general
-form's tile), with leading dimensions past the row length.  Inputs are small
+(the plain product's tile, the split-K plan, hybrid or not, the general
+form's tile and the general form's split plan), with leading dimensions past
+the row length.  Inputs are small
 integers and the scalars dyadic, so every result is exact and unique, and the
 comparison is bit for bit.  Padding in A and B is NaN; C's padding and a guard
 past it hold a sentinel that must come back unchanged.
@@ -121,3 +122,32 @@ def test_random_shape_general(case):
     torch.cuda.synchronize()
     parity.assert_bitwise(_window(C, M, N, ldc), ref,
                           "ex %dx%dx%d t%d%d a%g b%g" % (M, N, K, tA, tB, alpha, beta))
+
+
+@pytest.mark.parametrize("case", CASES, ids=IDS)
+def test_random_shape_general_splitk(case):
+    """The general form split over k with the automatic plan (which may keep
+    the unsplit general form), on the same shapes, layouts and scalars."""
+    i, M, N, K, pa, pb, pc, (tA, tB), alpha, beta = case
+    dev = _dev()
+    lda = (M if tA else K) + pa
+    ldb = (K if tB else N) + pb
+    ldc = N + pc
+    A_cpu, B_cpu = stored_operands(bool(tA), bool(tB), M, N, K, lda, ldb, 4000 + i, "int4")
+    C_cpu = matrix(M, N, ldc, 5000 + i, "int4")
+    ref, _, _ = oracle.sgemm_ex_f64(bool(tA), bool(tB), M, N, K, alpha, A_cpu.numpy(), lda,
+                                    B_cpu.numpy(), ldb, beta, C_cpu.numpy(), ldc)
+    A, B = A_cpu.to(dev), B_cpu.to(dev)
+    C = _c_buffer(M, ldc, dev, C_cpu)
+    cfg, splits, nbytes = sg.ex_splitk_plan(M, N, K, bool(tA), bool(tB))
+    ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    st = sg.sgemm_ex_splitk_raw(tA, tB, M, N, K, alpha, A.data_ptr(), lda, B.data_ptr(), ldb,
+                                beta, C.data_ptr(), ldc, ws.data_ptr(), ws.numel(), stream)
+    assert st == 0, sg.status_string(st)
+    torch.cuda.synchronize()
+    parity.assert_bitwise(_window(C, M, N, ldc), ref,
+                          "ex_splitk %dx%dx%d t%d%d a%g b%g plan %s"
+                          % (M, N, K, tA, tB, alpha, beta, (cfg, splits)))
+    if splits > 1:
+        assert torch.count_nonzero(ws[:sg.SPLITK_HEADER_BYTES]).item() == 0, "counters not reset"
